@@ -1,0 +1,6 @@
+"""CPU oracle for CSA2 decode (test infrastructure only).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  The product path (the HIP library and its binding) never does.
+"""
+from .oracle import *  # noqa: F401,F403
