@@ -1,0 +1,206 @@
+"""Thin ctypes binding over libcsa2.so (the C ABI in include/csa2.h).
+
+Argument marshalling only: every step of the decode path runs in the HIP
+kernels of libcsa2.  torch supplies device memory and the stream.  If the
+library is missing or fails to load, every call raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcsa2.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH = range(5)
+OP_INDEX_FULL, OP_INDEX_REINDEX, OP_DECODE_ATTN = 1, 2, 3
+
+D, HEADS, IDX_HEADS, IDX_DIM, WINDOW, RECORD, BLOCK = 128, 16, 4, 64, 128, 144, 8
+
+
+class Csa2Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+class csa2_cache(C.Structure):
+    _fields_ = [("kv", C.c_void_p), ("idxk", C.c_void_p), ("idxk_scale", C.c_float),
+                ("n_seq", C.c_int32), ("cap", C.c_int64)]
+
+
+class csa2_window(C.Structure):
+    _fields_ = [("k", C.c_void_p), ("v", C.c_void_p), ("k_scale", C.c_float),
+                ("v_scale", C.c_float), ("n_layers", C.c_int32), ("n_seq", C.c_int32),
+                ("w_cap", C.c_int32)]
+
+
+_lib = None
+_P = C.c_void_p
+
+
+def lib():
+    """Load libcsa2.so (raises OSError when it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise OSError(f"libcsa2.so not built at {LIB_PATH}; run "
+                          "`python -m fp4_kv_cache_decode_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        L.csa2_quantize_kv.argtypes = [C.POINTER(csa2_cache), C.POINTER(csa2_window), _P, _P, _P,
+                                       _P, _P, _P, _P, C.c_int64, _P]
+        L.csa2_index_full.argtypes = [C.POINTER(csa2_cache), _P, _P, _P, _P, C.c_int32, C.c_int64,
+                                      C.c_int32, C.c_int32, C.c_int32, _P, _P, _P, C.c_size_t, _P]
+        L.csa2_index_reindex.argtypes = [C.POINTER(csa2_cache), _P, _P, _P, _P, C.c_int32, _P,
+                                         C.c_int32, C.c_int32, C.c_int32, _P, _P, C.c_size_t, _P]
+        L.csa2_decode_attn.argtypes = [C.POINTER(csa2_cache), C.POINTER(csa2_window), C.c_int32,
+                                       _P, _P, _P, _P, C.c_int32, C.c_int32, C.c_float, _P, _P,
+                                       C.c_size_t, _P]
+        L.csa2_workspace_bytes.argtypes = [C.c_int32, C.c_int32, C.c_int64, C.c_int32, C.c_int32,
+                                           C.c_int32]
+        L.csa2_workspace_bytes.restype = C.c_size_t
+        L.csa2_status_string.argtypes = [C.c_int]
+        L.csa2_status_string.restype = C.c_char_p
+        for f in ("csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex",
+                  "csa2_decode_attn"):
+            getattr(L, f).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return lib().csa2_status_string(s).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != OK:
+        raise Csa2Error(status, where)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("expected a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError("expected a device tensor")
+    if not t.is_contiguous():
+        raise ValueError("expected a contiguous tensor")
+    return t.data_ptr()
+
+
+def _need(t, dtype, shape, name):
+    if t is None:
+        raise ValueError(f"{name} is required")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def workspace_bytes(op: int, B: int, max_ctx: int = 0, n_blocks: int = 2048, block: int = 8,
+                    topk: int = 512) -> int:
+    return int(lib().csa2_workspace_bytes(op, B, max_ctx, n_blocks, block, topk))
+
+
+class Cache:
+    """Device storage for the compressed cache and the per-layer window stores.
+
+    Allocation goes through torch; the library only receives the pointers.
+    """
+
+    def __init__(self, n_seq: int, cap: int, n_layers: int = 1, w_cap: int = WINDOW,
+                 idxk_scale: float = 1.0, wk_scale: float = 1.0, wv_scale: float = 1.0,
+                 device="cuda"):
+        self.n_seq, self.cap, self.n_layers, self.w_cap = n_seq, cap, n_layers, w_cap
+        self.kv = torch.zeros((n_seq, cap, RECORD), dtype=torch.uint8, device=device)
+        self.idxk = torch.zeros((n_seq, cap, IDX_DIM), dtype=torch.uint8, device=device)
+        self.wk = torch.zeros((n_layers, n_seq, w_cap, D), dtype=torch.uint8, device=device)
+        self.wv = torch.zeros_like(self.wk)
+        self.c = csa2_cache(self.kv.data_ptr(), self.idxk.data_ptr(), idxk_scale, n_seq, cap)
+        self.w = csa2_window(self.wk.data_ptr(), self.wv.data_ptr(), wk_scale, wv_scale,
+                             n_layers, n_seq, w_cap)
+
+
+def quantize_kv(cache: Cache, k, v, seq, pos, idx_k=None, win_k=None, win_v=None,
+                stream=None) -> None:
+    n = k.shape[0]
+    _need(k, torch.float32, (n, D), "k")
+    _need(v, torch.float32, (n, D), "v")
+    _need(seq, torch.int32, (n,), "seq")
+    _need(pos, torch.int64, (n,), "pos")
+    if idx_k is not None:
+        _need(idx_k, torch.float32, (n, IDX_DIM), "idx_k")
+    if win_k is not None:
+        _need(win_k, torch.float32, (cache.n_layers, n, D), "win_k")
+        _need(win_v, torch.float32, (cache.n_layers, n, D), "win_v")
+    st = lib().csa2_quantize_kv(C.byref(cache.c), C.byref(cache.w), _ptr(k), _ptr(v),
+                                _ptr(idx_k), _ptr(win_k), _ptr(win_v), _ptr(seq), _ptr(pos), n,
+                                _stream(stream))
+    _check(st, "csa2_quantize_kv")
+
+
+def index_full(cache: Cache, q_idx, w, seq, ctx, max_ctx: int, pool, idx, ws,
+               n_blocks: int = 2048, block: int = 8, topk: int = 512, stream=None) -> None:
+    B = q_idx.shape[0]
+    _need(q_idx, torch.float32, (B, IDX_HEADS, IDX_DIM), "q_idx")
+    _need(w, torch.float32, (B, IDX_HEADS), "w")
+    _need(seq, torch.int32, (B,), "seq")
+    _need(ctx, torch.int64, (B,), "ctx")
+    _need(idx, torch.int32, (B, topk), "idx")
+    if pool is not None:
+        _need(pool, torch.int32, (B, n_blocks), "pool")
+    _need(ws, torch.uint8, None, "ws")
+    st = lib().csa2_index_full(C.byref(cache.c), _ptr(q_idx), _ptr(w), _ptr(seq), _ptr(ctx), B,
+                               max_ctx, n_blocks, block, topk, _ptr(pool), _ptr(idx), _ptr(ws),
+                               ws.numel(), _stream(stream))
+    _check(st, "csa2_index_full")
+
+
+def index_reindex(cache: Cache, q_idx, w, seq, ctx, pool, idx, ws, block: int = 8,
+                  topk: int = 512, stream=None) -> None:
+    B = q_idx.shape[0]
+    n_blocks = pool.shape[1]
+    _need(q_idx, torch.float32, (B, IDX_HEADS, IDX_DIM), "q_idx")
+    _need(w, torch.float32, (B, IDX_HEADS), "w")
+    _need(seq, torch.int32, (B,), "seq")
+    _need(ctx, torch.int64, (B,), "ctx")
+    _need(pool, torch.int32, (B, n_blocks), "pool")
+    _need(idx, torch.int32, (B, topk), "idx")
+    _need(ws, torch.uint8, None, "ws")
+    st = lib().csa2_index_reindex(C.byref(cache.c), _ptr(q_idx), _ptr(w), _ptr(seq), _ptr(ctx),
+                                  B, _ptr(pool), n_blocks, block, topk, _ptr(idx), _ptr(ws),
+                                  ws.numel(), _stream(stream))
+    _check(st, "csa2_index_reindex")
+
+
+def decode_attn(cache: Cache, layer: int, q, idx, seq, ctx, out, ws, sm_scale=None,
+                stream=None) -> None:
+    B, topk = idx.shape
+    _need(q, torch.float32, (B, HEADS, D), "q")
+    _need(idx, torch.int32, (B, topk), "idx")
+    _need(seq, torch.int32, (B,), "seq")
+    _need(ctx, torch.int64, (B,), "ctx")
+    _need(out, torch.float32, (B, HEADS, D), "out")
+    _need(ws, torch.uint8, None, "ws")
+    if sm_scale is None:
+        sm_scale = float(torch.tensor(D ** -0.5, dtype=torch.float32))
+    st = lib().csa2_decode_attn(C.byref(cache.c), C.byref(cache.w), layer, _ptr(q), _ptr(idx),
+                                _ptr(seq), _ptr(ctx), B, topk, sm_scale, _ptr(out), _ptr(ws),
+                                ws.numel(), _stream(stream))
+    _check(st, "csa2_decode_attn")
+
+
+def alloc_workspace(op: int, B: int, max_ctx: int = 0, n_blocks: int = 2048, topk: int = 512,
+                    device="cuda") -> torch.Tensor:
+    n = workspace_bytes(op, B, max_ctx, n_blocks, BLOCK, topk)
+    if n == 0 and B > 0:
+        raise Csa2Error(ERR_INVALID_ARG, "csa2_workspace_bytes")
+    return torch.empty(max(n, 1), dtype=torch.uint8, device=device)

@@ -1,0 +1,201 @@
+// C ABI of libcsa2: argument validation, workspace layout, launch order.
+// The operations and their sources are documented in include/csa2.h.
+#include <math.h>
+
+#include "csa2_device.h"
+#include "csa2_internal.h"
+
+namespace {
+
+using csa2::BLOCK;
+
+constexpr size_t ALIGN = 256;
+
+size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+bool good_scale(float s) { return isfinite(s) && s > 0.0f; }
+
+// Block-maxima row stride (floats) for contexts up to max_ctx.
+int64_t m_stride(int64_t max_ctx) {
+    int64_t nb = (max_ctx + BLOCK - 1) / BLOCK;
+    return (nb + 63) / 64 * 64;
+}
+
+struct FullLayout {
+    size_t m_off, pool_off, s_off, total;
+};
+
+FullLayout full_layout(int32_t B, int64_t max_ctx, int32_t n_blocks) {
+    FullLayout L;
+    L.m_off = 0;
+    L.pool_off = align_up(L.m_off + (size_t)B * (size_t)m_stride(max_ctx) * sizeof(float));
+    L.s_off = align_up(L.pool_off + (size_t)B * (size_t)n_blocks * sizeof(int32_t));
+    L.total = align_up(L.s_off + (size_t)B * (size_t)n_blocks * BLOCK * sizeof(float));
+    return L;
+}
+
+size_t reindex_bytes(int32_t B, int32_t n_blocks) {
+    return align_up((size_t)B * (size_t)n_blocks * BLOCK * sizeof(float));
+}
+
+size_t attn_bytes(int32_t B, int32_t topk) {
+    return align_up((size_t)B * (size_t)csa2::attn_tiles(topk) * csa2::ATTN_PART_FLOATS *
+                    sizeof(float));
+}
+
+csa2_status check_cache(const csa2_cache* c, bool need_kv, bool need_idxk) {
+    if (!c) return CSA2_ERR_INVALID_ARG;
+    if ((need_kv && !c->kv) || (need_idxk && !c->idxk)) return CSA2_ERR_INVALID_ARG;
+    if (c->n_seq <= 0 || c->cap <= 0) return CSA2_ERR_INVALID_ARG;
+    if (need_idxk && !good_scale(c->idxk_scale)) return CSA2_ERR_INVALID_ARG;
+    return CSA2_OK;
+}
+
+csa2_status check_window(const csa2_window* w, const csa2_cache* c) {
+    if (!w || !w->k || !w->v) return CSA2_ERR_INVALID_ARG;
+    if (w->n_layers <= 0 || w->n_seq != c->n_seq) return CSA2_ERR_INVALID_ARG;
+    if (w->w_cap < CSA2_WINDOW) return CSA2_ERR_UNSUPPORTED;
+    if (!good_scale(w->k_scale) || !good_scale(w->v_scale)) return CSA2_ERR_INVALID_ARG;
+    return CSA2_OK;
+}
+
+csa2_status check_select(int32_t B, int32_t n_blocks, int32_t block, int32_t topk) {
+    if (B < 0) return CSA2_ERR_INVALID_ARG;
+    if (B > 65535) return CSA2_ERR_UNSUPPORTED;
+    if (block != CSA2_BLOCK) return CSA2_ERR_UNSUPPORTED;
+    if (n_blocks < 1 || n_blocks > CSA2_MAX_POOL) return CSA2_ERR_UNSUPPORTED;
+    if (topk < 1 || topk > CSA2_MAX_TOPK) return CSA2_ERR_UNSUPPORTED;
+    if ((int64_t)topk > (int64_t)n_blocks * block) return CSA2_ERR_INVALID_ARG;
+    return CSA2_OK;
+}
+
+csa2_status launched(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* csa2_status_string(csa2_status s) {
+    switch (s) {
+        case CSA2_OK: return "ok";
+        case CSA2_ERR_INVALID_ARG: return "invalid argument";
+        case CSA2_ERR_UNSUPPORTED: return "unsupported size";
+        case CSA2_ERR_WORKSPACE: return "workspace missing or too small";
+        case CSA2_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+size_t csa2_workspace_bytes(int32_t op, int32_t B, int64_t max_ctx, int32_t n_blocks,
+                            int32_t block, int32_t topk) {
+    if (B < 0) return 0;
+    switch (op) {
+        case CSA2_OP_INDEX_FULL:
+            if (max_ctx < 0 || check_select(B, n_blocks, block, topk) != CSA2_OK) return 0;
+            return full_layout(B, max_ctx, n_blocks).total;
+        case CSA2_OP_INDEX_REINDEX:
+            if (check_select(B, n_blocks, block, topk) != CSA2_OK) return 0;
+            return reindex_bytes(B, n_blocks);
+        case CSA2_OP_DECODE_ATTN:
+            if (topk < 1 || topk > CSA2_MAX_TOPK) return 0;
+            return attn_bytes(B, topk);
+    }
+    return 0;
+}
+
+csa2_status csa2_quantize_kv(const csa2_cache* cache, const csa2_window* win, const float* k,
+                             const float* v, const float* idx_k, const float* win_k,
+                             const float* win_v, const int32_t* seq, const int64_t* pos,
+                             int64_t n, hipStream_t stream) {
+    csa2_status st = check_cache(cache, true, idx_k != nullptr);
+    if (st != CSA2_OK) return st;
+    if (!k || !v || !seq || !pos || n < 0) return CSA2_ERR_INVALID_ARG;
+    if ((win_k == nullptr) != (win_v == nullptr)) return CSA2_ERR_INVALID_ARG;
+    if (win_k) {
+        st = check_window(win, cache);
+        if (st != CSA2_OK) return st;
+        if (win->n_layers > 65533) return CSA2_ERR_UNSUPPORTED;
+    }
+    if (n > ((int64_t)1 << 34)) return CSA2_ERR_UNSUPPORTED;
+    if (n == 0) return CSA2_OK;
+    return launched(csa2::launch_quantize(*cache, win, k, v, idx_k, win_k, win_v, seq, pos, n,
+                                          stream));
+}
+
+csa2_status csa2_index_full(const csa2_cache* cache, const float* q_idx, const float* w,
+                            const int32_t* seq, const int64_t* ctx, int32_t B,
+                            int64_t max_ctx, int32_t n_blocks, int32_t block, int32_t topk,
+                            int32_t* pool, int32_t* idx, void* ws, size_t ws_bytes,
+                            hipStream_t stream) {
+    csa2_status st = check_cache(cache, false, true);
+    if (st != CSA2_OK) return st;
+    if (!q_idx || !w || !seq || !ctx || !idx) return CSA2_ERR_INVALID_ARG;
+    st = check_select(B, n_blocks, block, topk);
+    if (st != CSA2_OK) return st;
+    if (max_ctx < 0 || max_ctx > cache->cap) return CSA2_ERR_INVALID_ARG;
+    if (B == 0) return CSA2_OK;
+    const FullLayout L = full_layout(B, max_ctx, n_blocks);
+    if (!ws || ws_bytes < L.total) return CSA2_ERR_WORKSPACE;
+    char* base = static_cast<char*>(ws);
+    float* M = reinterpret_cast<float*>(base + L.m_off);
+    int32_t* pool_out = pool ? pool : reinterpret_cast<int32_t*>(base + L.pool_off);
+    float* S = reinterpret_cast<float*>(base + L.s_off);
+
+    // enough workgroups to fill 256 CUs several times over
+    const int64_t total = (int64_t)B * max_ctx;
+    int64_t kpw = (total + 2047) / 2048;
+    kpw = (kpw + 255) / 256 * 256;
+    kpw = kpw < 256 ? 256 : (kpw > 4096 ? 4096 : kpw);
+
+    hipError_t e = csa2::launch_score_blocks(*cache, q_idx, w, seq, ctx, B, max_ctx,
+                                             m_stride(max_ctx), M, (int32_t)kpw, stream);
+    if (e != hipSuccess) return CSA2_ERR_LAUNCH;
+    e = csa2::launch_topk(M, m_stride(max_ctx), ctx, max_ctx, 0, nullptr, 0, B, n_blocks,
+                          pool_out, stream);
+    if (e != hipSuccess) return CSA2_ERR_LAUNCH;
+    e = csa2::launch_score_pool(*cache, q_idx, w, seq, ctx, B, pool_out, n_blocks, S, stream);
+    if (e != hipSuccess) return CSA2_ERR_LAUNCH;
+    return launched(csa2::launch_topk(S, (int64_t)n_blocks * BLOCK, nullptr, 0,
+                                      n_blocks * BLOCK, pool_out, n_blocks, B, topk, idx,
+                                      stream));
+}
+
+csa2_status csa2_index_reindex(const csa2_cache* cache, const float* q_idx, const float* w,
+                               const int32_t* seq, const int64_t* ctx, int32_t B,
+                               const int32_t* pool, int32_t n_blocks, int32_t block,
+                               int32_t topk, int32_t* idx, void* ws, size_t ws_bytes,
+                               hipStream_t stream) {
+    csa2_status st = check_cache(cache, false, true);
+    if (st != CSA2_OK) return st;
+    if (!q_idx || !w || !seq || !ctx || !pool || !idx) return CSA2_ERR_INVALID_ARG;
+    st = check_select(B, n_blocks, block, topk);
+    if (st != CSA2_OK) return st;
+    if (B == 0) return CSA2_OK;
+    if (!ws || ws_bytes < reindex_bytes(B, n_blocks)) return CSA2_ERR_WORKSPACE;
+    float* S = static_cast<float*>(ws);
+    hipError_t e = csa2::launch_score_pool(*cache, q_idx, w, seq, ctx, B, pool, n_blocks, S,
+                                           stream);
+    if (e != hipSuccess) return CSA2_ERR_LAUNCH;
+    return launched(csa2::launch_topk(S, (int64_t)n_blocks * BLOCK, nullptr, 0,
+                                      n_blocks * BLOCK, pool, n_blocks, B, topk, idx, stream));
+}
+
+csa2_status csa2_decode_attn(const csa2_cache* cache, const csa2_window* win, int32_t layer,
+                             const float* q, const int32_t* idx, const int32_t* seq,
+                             const int64_t* ctx, int32_t B, int32_t topk, float sm_scale,
+                             float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    csa2_status st = check_cache(cache, true, false);
+    if (st != CSA2_OK) return st;
+    st = check_window(win, cache);
+    if (st != CSA2_OK) return st;
+    if (!q || !idx || !seq || !ctx || !out) return CSA2_ERR_INVALID_ARG;
+    if (layer < 0 || layer >= win->n_layers || B < 0 || !isfinite(sm_scale))
+        return CSA2_ERR_INVALID_ARG;
+    if (topk < 1 || topk > CSA2_MAX_TOPK || B > 65535) return CSA2_ERR_UNSUPPORTED;
+    if (B == 0) return CSA2_OK;
+    if (!ws || ws_bytes < attn_bytes(B, topk)) return CSA2_ERR_WORKSPACE;
+    return launched(csa2::launch_attn(*cache, *win, layer, q, idx, seq, ctx, B, topk, sm_scale,
+                                      out, static_cast<float*>(ws), stream));
+}
+
+}  // extern "C"

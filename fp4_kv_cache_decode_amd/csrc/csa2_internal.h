@@ -1,0 +1,51 @@
+// Host-side launchers behind the C ABI (internal to libcsa2).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/csa2.h"
+
+namespace csa2 {
+
+// Quantise-on-write of n rows into the cache (and window stores).
+hipError_t launch_quantize(const csa2_cache& c, const csa2_window* w, const float* k,
+                           const float* v, const float* idx_k, const float* win_k,
+                           const float* win_v, const int32_t* seq, const int64_t* pos,
+                           int64_t n, hipStream_t stream);
+
+// Full-context scoring: block maxima M[b][j] for blocks j < ceil(ctx[b]/8).
+// keys_per_wg is a multiple of 256.
+hipError_t launch_score_blocks(const csa2_cache& c, const float* q_idx, const float* w,
+                               const int32_t* seq, const int64_t* ctx, int32_t B,
+                               int64_t max_ctx, int64_t m_stride, float* M,
+                               int32_t keys_per_wg, hipStream_t stream);
+
+// Pool scoring: S[b][i] = score of position pool[b][i/8]*8 + i%8, or -inf when
+// the pool slot is -1 or the position is >= ctx[b].
+hipError_t launch_score_pool(const csa2_cache& c, const float* q_idx, const float* w,
+                             const int32_t* seq, const int64_t* ctx, int32_t B,
+                             const int32_t* pool, int32_t n_blocks, float* S,
+                             hipStream_t stream);
+
+// Top-k select per row, ties to the lower index, output ascending, -1 padded.
+// Row b has n = ceil(ctx[b]/8) entries (ctx != null, block mode) or n_fixed
+// entries (pool mode, -inf entries are absent).  With pool != null an entry i
+// is reported as pool[b][i/8]*8 + i%8, else as i.
+hipError_t launch_topk(const float* vals, int64_t stride, const int64_t* ctx,
+                       int64_t max_ctx, int32_t n_fixed, const int32_t* pool,
+                       int32_t n_blocks, int32_t B, int32_t k, int32_t* out,
+                       hipStream_t stream);
+
+// Split-K gather/dequant attention for one layer plus the cross-split merge.
+hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
+                       const float* q, const int32_t* idx, const int32_t* seq,
+                       const int64_t* ctx, int32_t B, int32_t topk, float sm_scale,
+                       float* out, float* partials, hipStream_t stream);
+
+// Number of 64-entry tiles of an attention call (main tiles + 2 window tiles).
+inline int32_t attn_tiles(int32_t topk) { return (topk + 63) / 64 + 2; }
+constexpr size_t ATTN_PART_FLOATS = 16 + 16 + 16 * 128;
+
+}  // namespace csa2

@@ -1,0 +1,202 @@
+/*
+ * csa2.h - C ABI of libcsa2, CSA2 decode attention over a compressed global
+ * KV cache on AMD MI355X (gfx950).
+ *
+ * What the calls compute comes from these pages (news summaries of the
+ * DeepSeek-V4.1-Flash technical report):
+ *  [P1] trawling.dev, "DeepSeek-V4.1-Flash released - a 552B multimodal MoE that
+ *       cuts the KV cache to 890 bytes per token", section "CSA2 and FP4 KV caching".
+ *  [P3] cursorai.co.kr, "DeepSeek-V4.1-Flash: how an 890-byte KV cache changes
+ *       agent infrastructure", section 3, step 3 "FP4 KV cache quantisation".
+ *  [P4] origotech.dev, "Inside DeepSeek V4.1-Flash: KV cache, the 1017 update and
+ *       the Harness stack", section "How the architecture shrinks the KV cache"
+ *       and its sub-section "FP4 and SWA Bounded Replay".
+ *  [P5] ttj.kr, "DeepSeek-V4.1-Flash compresses the KV cache to 890 bytes per
+ *       token", section "CSA2 and the attention redesign".
+ *
+ * Conventions shared by every call
+ *  - Every array argument is a DEVICE pointer allocated by the caller; the
+ *    descriptor structs themselves are host memory read during the call.
+ *  - The library allocates nothing, frees nothing, never synchronises and keeps
+ *    no global state: each call validates its arguments on the host, enqueues
+ *    kernels on `stream` and returns.  Calls are reentrant; calls on different
+ *    streams must not share a workspace.
+ *  - Argument errors are reported synchronously through the return value and
+ *    enqueue nothing.  Launch errors return CSA2_ERR_LAUNCH.  Device-side
+ *    faults surface at the caller's next synchronisation.
+ *  - Per-query arrays seq[] and ctx[] live on the device.  seq[b] names the
+ *    cache sequence query b reads; ctx[b] = N is the number of visible
+ *    positions 0..N-1 (the current token included).  Kernels clamp values
+ *    outside [0, n_seq) / [0, max_ctx] so that no access leaves the buffers;
+ *    results for such queries are unspecified.
+ *  - Inputs must be finite.  Index outputs are ascending and padded with -1.
+ *
+ * Data layout in HBM (the cache descriptor)
+ *  - kv   [n_seq][cap][144] bytes, one record per token:
+ *         [0,64)   K codes, FP4 E2M1, channel 2j in the low nibble of byte j,
+ *                  channel 2j+1 in the high nibble;
+ *         [64,128) V codes, same packing;
+ *         [128,136) 8 K scales, E4M3FN, scale g covers channels 16g..16g+15;
+ *         [136,144) 8 V scales.
+ *    (FP4 E2M1 main KV with one E4M3 scale per 16 channels, quantised after
+ *    RoPE: [P1] "CSA2 and FP4 KV caching", [P4] "FP4 and SWA Bounded Replay";
+ *    0.5 byte per element: [P3] section 3 step 3.)
+ *  - idxk [n_seq][cap][64] bytes, E4M3FN indexer keys; key value = code value
+ *    times idxk_scale.  Main KV and indexer keys are shared by every layer of
+ *    the decoder ([P1] "CSA2 and FP4 KV caching"; [P4] mode list).
+ *  - window k/v [n_layers][n_seq][w_cap][128] bytes, E4M3FN, one store per
+ *    layer; position u lives in slot u % w_cap; value = code times k_scale /
+ *    v_scale.  (FP8 sliding-window KV: [P4] "FP4 and SWA Bounded Replay";
+ *    size 128: [P4], [P5] "CSA2 and the attention redesign".)
+ */
+#ifndef CSA2_H
+#define CSA2_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Fixed shapes. */
+#define CSA2_D 128          /* K / V channels of the single shared KV head */
+#define CSA2_HEADS 16       /* attention query heads */
+#define CSA2_IDX_HEADS 4    /* indexer heads */
+#define CSA2_IDX_DIM 64     /* indexer dims */
+#define CSA2_WINDOW 128     /* sliding-window tokens ([P4], [P5]) */
+#define CSA2_RECORD 144     /* bytes per FP4 K+V record */
+#define CSA2_BLOCK 8        /* positions per indexer block ([P4]) */
+#define CSA2_MAX_TOPK 2048  /* largest supported topk */
+#define CSA2_MAX_POOL 4096  /* largest supported n_blocks */
+
+typedef enum csa2_status {
+    CSA2_OK = 0,
+    CSA2_ERR_INVALID_ARG = 1,  /* null pointer, negative size, out-of-range value */
+    CSA2_ERR_UNSUPPORTED = 2,  /* a size this build does not implement */
+    CSA2_ERR_WORKSPACE = 3,    /* ws null or ws_bytes below csa2_workspace_bytes */
+    CSA2_ERR_LAUNCH = 4        /* a kernel launch failed (hipGetLastError) */
+} csa2_status;
+
+/* The shared compressed store: main-KV records and indexer keys. */
+typedef struct csa2_cache {
+    uint8_t* kv;        /* device [n_seq][cap][144] */
+    uint8_t* idxk;      /* device [n_seq][cap][64]  */
+    float idxk_scale;   /* per-tensor scale of the indexer keys (> 0) */
+    int32_t n_seq;
+    int64_t cap;        /* positions per sequence */
+} csa2_cache;
+
+/* Per-layer FP8 sliding-window stores, all layers in one allocation. */
+typedef struct csa2_window {
+    uint8_t* k;         /* device [n_layers][n_seq][w_cap][128] */
+    uint8_t* v;         /* device, same shape */
+    float k_scale;      /* per-tensor scales (> 0) */
+    float v_scale;
+    int32_t n_layers;
+    int32_t n_seq;      /* must equal the cache's n_seq */
+    int32_t w_cap;      /* slots per sequence, >= 128 */
+} csa2_window;
+
+/* Operation ids for csa2_workspace_bytes. */
+enum { CSA2_OP_INDEX_FULL = 1, CSA2_OP_INDEX_REINDEX = 2, CSA2_OP_DECODE_ATTN = 3 };
+
+/*
+ * csa2_quantize_kv - quantise-on-write of n new tokens.
+ * Passage: main KV stored as FP4 E2M1 with one E4M3 scale per 16 channels,
+ * quantised after RoPE; sliding-window KV kept in FP8 ([P4] "FP4 and SWA
+ * Bounded Replay"; [P1] "CSA2 and FP4 KV caching").
+ *   k, v      [n][128] fp32, post-RoPE main K and V rows -> record at
+ *             kv[seq[i]][pos[i]].  Per 16-channel group: scale code =
+ *             E4M3(fp32(amax)/6) rounded to nearest even and saturated at 448;
+ *             each nibble = nearest E2M1 value of x/scale (ties to even,
+ *             saturating at 6, sign of x kept); a zero scale gives zero codes.
+ *   idx_k     [n][64] fp32 or NULL -> idxk[seq[i]][pos[i]] = E4M3(x/idxk_scale).
+ *   win_k/v   [win->n_layers][n][128] fp32 or NULL (both or neither) -> slot
+ *             pos[i] % w_cap of every layer's window store, E4M3(x/scale).
+ *   win       may be NULL when win_k/win_v are NULL.
+ *   seq, pos  [n] device; pos must lie in [0, cap).  Rows with seq or pos out of
+ *             range are skipped.  Rows are written in parallel: duplicate
+ *             (seq, pos) pairs, or window rows of one call that share a slot
+ *             (same seq, equal pos % w_cap), race.
+ */
+csa2_status csa2_quantize_kv(const csa2_cache* cache, const csa2_window* win,
+                             const float* k, const float* v, const float* idx_k,
+                             const float* win_k, const float* win_v, const int32_t* seq,
+                             const int64_t* pos, int64_t n, hipStream_t stream);
+
+/*
+ * csa2_index_full - Full-mode indexer: score, block pool, top-k.
+ * Passage: a Full layer computes its own indexer query and a fresh top-k; the
+ * first Full layer selects 2,048 blocks of 8 positions (a 16,384-position pool)
+ * and top-k is 512 ([P4] "How the architecture shrinks the KV cache"; [P1]
+ * "CSA2 and FP4 KV caching").  Score function and block score are this
+ * library's reading: score_t = sum_h w_h * max(0, q_h . khat_t), khat = key
+ * code value * idxk_scale; block score = max over the block's positions < N.
+ *   q_idx     [B][4][64] fp32, w [B][4] fp32.
+ *   max_ctx   host bound with ctx[b] <= max_ctx <= cap for all b (sizes grids).
+ *   n_blocks  pool size in blocks, 1..4096 (2048 in the pages); block must be 8.
+ *   topk      1..2048 and <= n_blocks*8 (512 in the pages).
+ *   pool      [B][n_blocks] int32 out, or NULL: the n_blocks largest block
+ *             scores (ties to the lower block), ascending, -1 padded.
+ *   idx       [B][topk] int32 out: the topk largest scores among the pool's
+ *             positions < N (ties to the lower position), ascending, -1 padded.
+ *   ws        device workspace of at least
+ *             csa2_workspace_bytes(CSA2_OP_INDEX_FULL, B, max_ctx, n_blocks, 8, topk).
+ */
+csa2_status csa2_index_full(const csa2_cache* cache, const float* q_idx, const float* w,
+                            const int32_t* seq, const int64_t* ctx, int32_t B,
+                            int64_t max_ctx, int32_t n_blocks, int32_t block, int32_t topk,
+                            int32_t* pool, int32_t* idx, void* ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/*
+ * csa2_index_reindex - Reindex-mode indexer over a given pool.
+ * Passage: a Reindex layer reuses the previous layer's main KV and indexer keys,
+ * has its own indexer query and recomputes top-k; only Reindex layers score the
+ * first Full layer's pool ([P4] "How the architecture shrinks the KV cache";
+ * [P1] "CSA2 and FP4 KV caching").
+ *   pool      [B][n_blocks] int32 (as written by csa2_index_full), ascending,
+ *             -1 entries ignored.  Positions >= ctx[b] are ignored.
+ *   idx       [B][topk] int32 out, same ranking and padding rules as above.
+ *   ws        at least csa2_workspace_bytes(CSA2_OP_INDEX_REINDEX, B, 0, n_blocks, 8, topk).
+ */
+csa2_status csa2_index_reindex(const csa2_cache* cache, const float* q_idx, const float* w,
+                               const int32_t* seq, const int64_t* ctx, int32_t B,
+                               const int32_t* pool, int32_t n_blocks, int32_t block,
+                               int32_t topk, int32_t* idx, void* ws, size_t ws_bytes,
+                               hipStream_t stream);
+
+/*
+ * csa2_decode_attn - gather, dequantise and attend for one layer.
+ * Passage: attention reads the top-k selected global positions plus a local
+ * 128-token sliding window ([P4] "How the architecture shrinks the KV cache";
+ * [P5] "CSA2 and the attention redesign"); Reuse layers reuse main KV and top-k
+ * indices (pass the same idx again).  Reading: one softmax per head over the
+ * valid main rows idx[b][j] >= 0 and the window rows of positions
+ * [max(0, N-128), N); logits (q_h . k) * sm_scale; no sink, no bias.
+ *   layer     window layer in [0, win->n_layers).
+ *   q         [B][16][128] fp32, |q| < 65504.
+ *   idx       [B][topk] int32 positions (< ctx[b]) or -1.
+ *   out       [B][16][128] fp32.  A query with no valid entry gets zeros.
+ *   ws        at least csa2_workspace_bytes(CSA2_OP_DECODE_ATTN, B, 0, 0, 0, topk).
+ */
+csa2_status csa2_decode_attn(const csa2_cache* cache, const csa2_window* win, int32_t layer,
+                             const float* q, const int32_t* idx, const int32_t* seq,
+                             const int64_t* ctx, int32_t B, int32_t topk, float sm_scale,
+                             float* out, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Workspace bytes an operation needs (0 for unknown op or invalid sizes). */
+size_t csa2_workspace_bytes(int32_t op, int32_t B, int64_t max_ctx, int32_t n_blocks,
+                            int32_t block, int32_t topk);
+
+/* Static description of a status code. */
+const char* csa2_status_string(csa2_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CSA2_H */

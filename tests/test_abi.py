@@ -1,0 +1,139 @@
+"""The C-ABI library loads, exports what include/csa2.h declares, sizes its
+workspaces consistently and rejects bad arguments on the host (CPU only: none
+of these calls reaches a kernel launch)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from conftest import ROOT
+
+HEADER = os.path.join(ROOT, "include", "csa2.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from fp4_kv_cache_decode_amd import csa2
+    if not os.path.exists(csa2.LIB_PATH):
+        from fp4_kv_cache_decode_amd import build
+        build.build()
+    return csa2.lib()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(csa2_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_four_calls():
+    names = _declared()
+    for n in ("csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex", "csa2_decode_attn",
+              "csa2_workspace_bytes", "csa2_status_string"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    for name in _declared():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    from fp4_kv_cache_decode_amd import csa2
+    assert csa2.status_string(0) == "ok"
+    assert "workspace" in csa2.status_string(3)
+
+
+def test_workspace_sizes(L):
+    from fp4_kv_cache_decode_amd import csa2 as K
+    full = K.workspace_bytes(K.OP_INDEX_FULL, 4, 1 << 20, 2048, 8, 512)
+    # block maxima (4 x 131072 fp32) + pool (4 x 2048 int32) + pool scores (4 x 16384 fp32)
+    assert full >= 4 * 131072 * 4 + 4 * 2048 * 4 + 4 * 16384 * 4
+    assert full % 256 == 0
+    assert K.workspace_bytes(K.OP_INDEX_REINDEX, 4, 0, 2048, 8, 512) == 4 * 16384 * 4
+    assert K.workspace_bytes(K.OP_DECODE_ATTN, 4, 0, 0, 0, 512) >= 4 * 10 * (32 + 2048) * 4
+    assert K.workspace_bytes(K.OP_INDEX_FULL, 4, 1 << 20, 2048, 4, 512) == 0      # block != 8
+    assert K.workspace_bytes(K.OP_INDEX_FULL, 4, 1 << 20, 8192, 8, 512) == 0      # pool too big
+    assert K.workspace_bytes(K.OP_DECODE_ATTN, 4, 0, 0, 0, 4096) == 0             # topk too big
+    assert K.workspace_bytes(99, 4, 0, 0, 0, 512) == 0
+
+
+FAKE = C.c_void_p(0x10000)   # never dereferenced: validation fails first
+
+
+def _cache(K, kv=FAKE, idxk=FAKE, n_seq=1, cap=1024, scale=1.0):
+    return K.csa2_cache(kv.value if kv else None, idxk.value if idxk else None, scale, n_seq, cap)
+
+
+def _win(K, n_layers=1, n_seq=1, w_cap=128):
+    return K.csa2_window(FAKE.value, FAKE.value, 1.0, 1.0, n_layers, n_seq, w_cap)
+
+
+def test_quantize_error_paths(L):
+    from fp4_kv_cache_decode_amd import csa2 as K
+    c, w = _cache(K), _win(K)
+    f = L.csa2_quantize_kv
+    assert f(None, C.byref(w), FAKE, FAKE, None, None, None, FAKE, FAKE, 4, None) == 1
+    assert f(C.byref(_cache(K, kv=None)), None, FAKE, FAKE, None, None, None, FAKE, FAKE, 4,
+             None) == 1
+    assert f(C.byref(c), None, None, FAKE, None, None, None, FAKE, FAKE, 4, None) == 1
+    assert f(C.byref(c), None, FAKE, FAKE, None, None, None, FAKE, FAKE, -1, None) == 1
+    assert f(C.byref(c), C.byref(w), FAKE, FAKE, None, FAKE, None, FAKE, FAKE, 4, None) == 1
+    assert f(C.byref(c), None, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, None) == 1
+    assert f(C.byref(c), C.byref(_win(K, w_cap=64)), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+             4, None) == 2
+    assert f(C.byref(c), C.byref(_win(K, n_seq=2)), FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE,
+             4, None) == 1
+    assert f(C.byref(_cache(K, scale=0.0)), None, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, 4,
+             None) == 1
+    assert f(C.byref(c), None, FAKE, FAKE, None, None, None, FAKE, FAKE, 0, None) == 0
+
+
+def test_index_error_paths(L):
+    from fp4_kv_cache_decode_amd import csa2 as K
+    c = _cache(K)
+    f = L.csa2_index_full
+    ws_ok = K.workspace_bytes(K.OP_INDEX_FULL, 2, 1024, 64, 8, 32)
+    args = lambda **kw: dict(dict(cache=C.byref(c), q=FAKE, w=FAKE, seq=FAKE, ctx=FAKE, B=2,
+                                  max_ctx=1024, nb=64, block=8, topk=32, pool=None, idx=FAKE,
+                                  ws=FAKE, wsb=ws_ok), **kw)
+    call = lambda a: f(a["cache"], a["q"], a["w"], a["seq"], a["ctx"], a["B"], a["max_ctx"],
+                       a["nb"], a["block"], a["topk"], a["pool"], a["idx"], a["ws"], a["wsb"],
+                       None)
+    assert call(args(cache=None)) == 1
+    assert call(args(q=None)) == 1
+    assert call(args(idx=None)) == 1
+    assert call(args(block=16)) == 2
+    assert call(args(nb=5000)) == 2
+    assert call(args(topk=4096)) == 2
+    assert call(args(nb=2, topk=32)) == 1            # topk > n_blocks * 8
+    assert call(args(max_ctx=2048)) == 1             # beyond cap
+    assert call(args(B=-1)) == 1
+    assert call(args(ws=None)) == 3
+    assert call(args(wsb=ws_ok - 1)) == 3
+    assert call(args(B=0)) == 0
+    r = L.csa2_index_reindex
+    assert r(C.byref(c), FAKE, FAKE, FAKE, FAKE, 2, None, 64, 8, 32, FAKE, FAKE, 1 << 20,
+             None) == 1
+    assert r(C.byref(c), FAKE, FAKE, FAKE, FAKE, 2, FAKE, 64, 8, 32, FAKE, FAKE, 16, None) == 3
+
+
+def test_attn_error_paths(L):
+    from fp4_kv_cache_decode_amd import csa2 as K
+    c, w = _cache(K), _win(K, n_layers=2)
+    f = L.csa2_decode_attn
+    ws = K.workspace_bytes(K.OP_DECODE_ATTN, 2, 0, 0, 0, 512)
+    call = lambda **kw: f(kw.get("c", C.byref(c)), kw.get("w", C.byref(w)), kw.get("layer", 1),
+                          FAKE, kw.get("idx", FAKE), FAKE, FAKE, kw.get("B", 2),
+                          kw.get("topk", 512), kw.get("sm", 0.088), FAKE, kw.get("ws", FAKE),
+                          kw.get("wsb", ws), None)
+    assert call(w=None) == 1
+    assert call(layer=2) == 1
+    assert call(layer=-1) == 1
+    assert call(idx=None) == 1
+    assert call(topk=0) == 2
+    assert call(topk=4096) == 2
+    assert call(sm=float("nan")) == 1
+    assert call(wsb=ws - 4) == 3
+    assert call(B=0) == 0

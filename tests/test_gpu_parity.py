@@ -1,0 +1,334 @@
+"""GPU parity: every step of the decode path through the C ABI against the oracle.
+
+Bars: FP4/FP8 codes and scales bit-exact; index sets equal up to positions whose
+oracle score lies within 1e-5 relative of the oracle's k-th score (exact when the
+scores are exactly representable); attention max-abs <= 2e-3 of the fp64 oracle.
+Stages are isolated: reindex gets the oracle's pool, attention the oracle's
+indices, so one near tie cannot cascade.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+import oracle as O
+from fp4_kv_cache_decode_amd import datagen as G
+from parity import ATTN_TOL, block_scores, check_index_set, fill_both
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def K():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from fp4_kv_cache_decode_amd import csa2
+    csa2.lib()
+    return csa2
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+# ----------------------------------------------------------------- quantise
+
+def _adversarial_rows(n, rng):
+    k = (rng.standard_normal((n, 128)) * rng.uniform(0.01, 30, (n, 1))).astype(np.float32)
+    if n < 7:
+        return k
+    k[0] = 0.0
+    k[1] = -0.0
+    k[2, :16] = [6.0, .25, .75, 1.25, 1.75, 2.5, 3.5, 5.0, -.25, -.75, -1.25, -1.75, -2.5, -3.5,
+                 -5.0, 0.0]
+    k[3] = rng.standard_normal(128) * 1e-9
+    k[3, 5] = 3000.0                     # scale saturates at 448
+    k[4] = 6e-4                          # scale rounds to 0
+    k[5, :16] = np.r_[6.4, rng.uniform(-6.4, 6.4, 15)]
+    k[6] = rng.standard_normal(128) * 1e5
+    return k
+
+
+@pytest.mark.parametrize("n,n_layers,scales", [(1, 1, (1.0, 1.0, 1.0)), (1000, 3, (1.0, 1.0, 1.0)),
+                                                (777, 2, (0.37, 1.7, 0.5))])
+def test_quantize_bit_exact(K, n, n_layers, scales):
+    _say(f"quantize n={n} layers={n_layers} scales={scales}")
+    rng = np.random.default_rng(n)
+    cap, n_seq, w_cap = 4096, 3, 160
+    k = _adversarial_rows(n, rng)
+    v = _adversarial_rows(n, rng)[::-1].copy()
+    ik = (rng.standard_normal((n, 64)) * 40).astype(np.float32)
+    ik[0, :4] = [1e6, -1e6, 2.0 ** -10, -(2.0 ** -10)]
+    wk = (rng.standard_normal((n_layers, n, 128)) * 20).astype(np.float32)
+    wv = (rng.standard_normal((n_layers, n, 128)) * 3).astype(np.float32)
+    seq = rng.integers(0, n_seq, n).astype(np.int32)
+    pos = rng.choice(cap, n, replace=False).astype(np.int64)
+    oc = O.Cache(n_seq, cap, n_layers, w_cap, *scales)
+    oc.quantize(k, v, ik, wk, wv, seq, pos)
+    gc = K.Cache(n_seq, cap, n_layers, w_cap, *scales)
+    K.quantize_kv(gc, dev(k), dev(v), dev(seq), dev(pos), idx_k=dev(ik), win_k=dev(wk),
+                  win_v=dev(wv))
+    torch.cuda.synchronize()
+    assert np.array_equal(gc.kv.cpu().numpy(), oc.kv)
+    assert np.array_equal(gc.idxk.cpu().numpy(), oc.idxk)
+    # window slots may collide (pos % w_cap): compare only slots written once
+    slots = pos % w_cap
+    uniq = {(s, p) for s, p in zip(seq, slots)}
+    counts = {}
+    for s, p in zip(seq, slots):
+        counts[(s, p)] = counts.get((s, p), 0) + 1
+    gwk, gwv = gc.wk.cpu().numpy(), gc.wv.cpu().numpy()
+    for (s, p) in uniq:
+        if counts[(s, p)] == 1:
+            assert np.array_equal(gwk[:, s, p], oc.wk[:, s, p])
+            assert np.array_equal(gwv[:, s, p], oc.wv[:, s, p])
+
+
+def test_quantize_all_e4m3_inputs(K):
+    """Every E4M3 value, every midpoint and its neighbours through the FP8 path."""
+    _say("quantize fp8 exhaustive")
+    vals = torch.arange(127, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    mids = (vals[:-1] + vals[1:]) / 2
+    x = np.concatenate([vals, mids, np.nextafter(mids, 0), np.nextafter(mids, 1e9), [448, 464, 1e4]])
+    x = np.concatenate([x, -x]).astype(np.float32)
+    n = -(-x.size // 64)
+    ik = np.zeros((n, 64), np.float32)
+    ik.ravel()[:x.size] = x
+    zeros = np.zeros((n, 128), np.float32)
+    oc = O.Cache(1, n)
+    oc.quantize(zeros, zeros, ik, None, None, np.zeros(n, np.int32), np.arange(n))
+    gc = K.Cache(1, n)
+    K.quantize_kv(gc, dev(zeros), dev(zeros), dev(np.zeros(n, np.int32)),
+                  dev(np.arange(n, dtype=np.int64)), idx_k=dev(ik))
+    torch.cuda.synchronize()
+    assert np.array_equal(gc.idxk.cpu().numpy(), oc.idxk)
+
+
+# ----------------------------------------------------------------- indexer
+
+def _setup(K, seed, n_seq, N, n_layers=1, cap=None):
+    cap = cap or N
+    oc = O.Cache(n_seq, cap, n_layers)
+    gc = K.Cache(n_seq, cap, n_layers)
+    fill_both(seed, n_seq, N, n_layers, oc, gc)
+    torch.cuda.synchronize()
+    return oc, gc
+
+
+def _run_full(K, gc, q, w, seq, ctx, max_ctx, n_blocks=2048, topk=512):
+    B = q.shape[0]
+    pool = torch.empty((B, n_blocks), dtype=torch.int32, device="cuda")
+    idx = torch.empty((B, topk), dtype=torch.int32, device="cuda")
+    ws = K.alloc_workspace(K.OP_INDEX_FULL, B, max_ctx, n_blocks, topk)
+    K.index_full(gc, dev(q), dev(w), dev(seq), dev(ctx), max_ctx, pool, idx, ws,
+                 n_blocks=n_blocks, topk=topk)
+    torch.cuda.synchronize()
+    return pool.cpu().numpy(), idx.cpu().numpy()
+
+
+def _check_full(oc, q, w, seq, ctx, gpool, gidx, n_blocks, topk, exact=False):
+    opool, oidx, kb, kp = oc.index_full(q, w, seq, ctx, n_blocks=n_blocks, topk=topk)
+    n_diff = 0
+    for b in range(len(seq)):
+        sc = oc.scores(int(seq[b]), q[b], w[b], int(ctx[b]))
+        M = block_scores(sc, int(ctx[b]))
+        n_diff += check_index_set(gpool[b], opool[b], lambda j: M[j], kb[b], exact=exact)
+        n_diff += check_index_set(gidx[b], oidx[b], lambda t: sc[t], kp[b], exact=exact)
+    return n_diff
+
+
+@pytest.mark.parametrize("N", [1, 7, 100, 513, 4096, 16385, 40001])
+def test_index_full_ragged(K, N):
+    _say(f"index_full N={N}")
+    B = 3
+    oc, gc = _setup(K, N, B, N)
+    q, w = G.index_queries(N, 0, B)
+    seq = np.arange(B, dtype=np.int32)
+    ctx = np.array([N, max(1, N - 5), max(1, N // 2)], np.int64)
+    gpool, gidx = _run_full(K, gc, q, w, seq, ctx, N)
+    nd = _check_full(oc, q, w, seq, ctx, gpool, gidx, 2048, 512)
+    _say(f"  exempt differences: {nd}")
+
+
+def test_index_full_small_pool_params(K):
+    """n_blocks / topk other than 2048 / 512 with a strict-subset pool."""
+    _say("index_full small pool")
+    N, B = 3000, 2
+    oc, gc = _setup(K, 77, B, N)
+    q, w = G.index_queries(77, 0, B)
+    seq = np.arange(B, dtype=np.int32)
+    ctx = np.array([N, 2999], np.int64)
+    for nb, tk in [(16, 8), (64, 100), (100, 800), (1, 8)]:
+        gpool, gidx = _run_full(K, gc, q, w, seq, ctx, N, nb, tk)
+        _check_full(oc, q, w, seq, ctx, gpool, gidx, nb, tk)
+
+
+def test_index_full_integer_scores_exact(K):
+    """Integer keys and queries: fp32 scores are exact, so the sets must match
+    exactly, ties included (many equal scores)."""
+    _say("index_full integer exact")
+    N, B = 50000, 2
+    rng = np.random.default_rng(3)
+    oc = O.Cache(B, N)
+    gc = K.Cache(B, N)
+    zeros = np.zeros((N, 128), np.float32)
+    for s in range(B):
+        ik = rng.integers(-3, 4, (N, 64)).astype(np.float32)
+        seq = np.full(N, s, np.int32)
+        pos = np.arange(N, dtype=np.int64)
+        oc.quantize(zeros, zeros, ik, None, None, seq, pos)
+        K.quantize_kv(gc, dev(zeros), dev(zeros), dev(seq), dev(pos), idx_k=dev(ik))
+    q = rng.integers(-2, 3, (B, 4, 64)).astype(np.float32)
+    w = np.array([[1, 0.5, 0.25, 2], [1, 1, 1, 1]], np.float32)
+    seq = np.arange(B, dtype=np.int32)
+    ctx = np.array([N, N - 3], np.int64)
+    gpool, gidx = _run_full(K, gc, q, w, seq, ctx, N)
+    _check_full(oc, q, w, seq, ctx, gpool, gidx, 2048, 512, exact=True)
+
+
+def test_index_all_zero_scores_take_lowest(K):
+    """All scores 0 (queries orthogonal to keys): lowest blocks / positions win."""
+    _say("index_full all-zero scores")
+    N = 70000
+    oc, gc = _setup(K, 5, 1, N)
+    q = np.zeros((1, 4, 64), np.float32)
+    w = np.ones((1, 4), np.float32)
+    gpool, gidx = _run_full(K, gc, q, w, np.zeros(1, np.int32), np.array([N]), N)
+    assert list(gpool[0]) == list(range(2048))
+    assert list(gidx[0]) == list(range(512))
+
+
+def test_index_reindex(K):
+    _say("index_reindex")
+    N, B = 60000, 3
+    oc, gc = _setup(K, 21, B, N)
+    q0, w0 = G.index_queries(21, 0, B)
+    q1, w1 = G.index_queries(21, 1, B)
+    seq = np.arange(B, dtype=np.int32)
+    ctx = np.array([N, N - 1, 20000], np.int64)
+    opool, _, _, _ = oc.index_full(q0, w0, seq, ctx)
+    oidx, kp = oc.index_reindex(q1, w1, seq, ctx, opool)
+    idx = torch.empty((B, 512), dtype=torch.int32, device="cuda")
+    ws = K.alloc_workspace(K.OP_INDEX_REINDEX, B)
+    K.index_reindex(gc, dev(q1), dev(w1), dev(seq), dev(ctx), dev(opool), idx, ws)
+    torch.cuda.synchronize()
+    gidx = idx.cpu().numpy()
+    for b in range(B):
+        sc = oc.scores(b, q1[b], w1[b], int(ctx[b]))
+        check_index_set(gidx[b], oidx[b], lambda t: sc[t], kp[b])
+    # Reindex with the Full query reproduces the Full selection
+    _, fidx = _run_full(K, gc, q0, w0, seq, ctx, N)
+    K.index_reindex(gc, dev(q0), dev(w0), dev(seq), dev(ctx), dev(opool), idx, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(idx.cpu().numpy(), fidx)
+
+
+# ----------------------------------------------------------------- attention
+
+def _attn_case(K, N, B, n_layers, layer, seed, topk=512, w_cap=128, idx=None):
+    oc = O.Cache(B, N, n_layers, w_cap)
+    gc = K.Cache(B, N, n_layers, w_cap)
+    fill_both(seed, B, N, n_layers, oc, gc)
+    q = G.attn_queries(seed, layer, B)
+    seq = np.arange(B, dtype=np.int32)
+    ctx = np.full(B, N, np.int64)
+    if idx is None:
+        qi, wi = G.index_queries(seed, 0, B)
+        _, idx, _, _ = oc.index_full(qi, wi, seq, ctx, topk=topk)
+    want = oc.decode_attn(layer, q, idx, seq, ctx)
+    out = torch.empty((B, 16, 128), dtype=torch.float32, device="cuda")
+    ws = K.alloc_workspace(K.OP_DECODE_ATTN, B, topk=idx.shape[1])
+    K.decode_attn(gc, layer, dev(q), dev(idx), dev(seq), dev(ctx), out, ws)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    err = float(np.max(np.abs(got - want)))
+    _say(f"  attn N={N} B={B} layer={layer} max-abs err {err:.3g}")
+    return got, want, err
+
+
+@pytest.mark.parametrize("N", [1, 50, 128, 129, 700, 5000])
+def test_decode_attn(K, N):
+    _say(f"decode_attn N={N}")
+    got, want, err = _attn_case(K, N, 3, 2, 1, seed=N)
+    assert err <= ATTN_TOL
+    assert err <= 1e-4, "fp32-accurate design bound"
+
+
+def test_decode_attn_ragged_topk_and_padding(K):
+    _say("decode_attn topk=200 with padding")
+    N, B = 3000, 2
+    rng = np.random.default_rng(1)
+    idx = np.full((B, 200), -1, np.int32)
+    idx[0, :150] = np.sort(rng.choice(N, 150, replace=False))
+    idx[1, :3] = [0, 1, N - 1]
+    got, want, err = _attn_case(K, N, B, 1, 0, seed=9, idx=idx)
+    assert err <= 1e-4
+
+
+def test_decode_attn_zero_query_is_mean(K):
+    _say("decode_attn q=0")
+    N, B = 1000, 1
+    oc = O.Cache(B, N)
+    gc = K.Cache(B, N)
+    fill_both(4, B, N, 1, oc, gc)
+    idx = np.arange(0, 1000, 2, dtype=np.int32)[None, :500]
+    idx = np.pad(idx, ((0, 0), (0, 12)), constant_values=-1)
+    q = np.zeros((1, 16, 128), np.float32)
+    out = torch.empty((1, 16, 128), dtype=torch.float32, device="cuda")
+    ws = K.alloc_workspace(K.OP_DECODE_ATTN, 1, topk=512)
+    K.decode_attn(gc, 0, dev(q), dev(idx), dev(np.zeros(1, np.int32)), dev(np.array([N])), out, ws)
+    torch.cuda.synchronize()
+    want = oc.decode_attn(0, q, idx, [0], [N])
+    assert np.max(np.abs(out.cpu().numpy() - want)) <= 1e-5
+
+
+def test_reuse_layers_share_indices(K):
+    """Reuse: the group's idx buffer is passed unchanged to every layer."""
+    _say("reuse layers")
+    N, B, L = 20000, 2, 4
+    oc = O.Cache(B, N, L)
+    gc = K.Cache(B, N, L)
+    fill_both(31, B, N, L, oc, gc)
+    qi, wi = G.index_queries(31, 0, B)
+    seq = np.arange(B, dtype=np.int32)
+    ctx = np.full(B, N, np.int64)
+    _, oidx, _, _ = oc.index_full(qi, wi, seq, ctx)
+    idx = dev(oidx)
+    before = idx.clone()
+    ws = K.alloc_workspace(K.OP_DECODE_ATTN, B)
+    out = torch.empty((B, 16, 128), dtype=torch.float32, device="cuda")
+    for layer in range(L):
+        q = G.attn_queries(31, layer, B)
+        K.decode_attn(gc, layer, dev(q), idx, dev(seq), dev(ctx), out, ws)
+        torch.cuda.synchronize()
+        want = oc.decode_attn(layer, q, oidx, seq, ctx)
+        assert np.max(np.abs(out.cpu().numpy() - want)) <= ATTN_TOL
+    assert torch.equal(idx, before)
+
+
+def test_determinism(K):
+    _say("determinism")
+    N, B = 30000, 2
+    oc, gc = _setup(K, 2, B, N, n_layers=1)
+    q, w = G.index_queries(2, 0, B)
+    seq, ctx = np.arange(B, dtype=np.int32), np.full(B, N, np.int64)
+    a = _run_full(K, gc, q, w, seq, ctx, N)
+    b = _run_full(K, gc, q, w, seq, ctx, N)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    qa = G.attn_queries(2, 0, B)
+    outs = []
+    for _ in range(2):
+        out = torch.empty((B, 16, 128), dtype=torch.float32, device="cuda")
+        ws = K.alloc_workspace(K.OP_DECODE_ATTN, B)
+        K.decode_attn(gc, 0, dev(qa), dev(a[1]), dev(seq), dev(ctx), out, ws)
+        torch.cuda.synchronize()
+        outs.append(out.cpu().numpy())
+    assert np.array_equal(outs[0], outs[1])
