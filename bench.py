@@ -1,0 +1,302 @@
+#!/usr/bin/env python3
+"""CSA2 decode benchmark on one MI355X.
+
+A step is one decode token for every sequence of the workload through the
+whole hot path: quantise-on-write of the new token (main KV, indexer key and
+the window rows of every layer), the Full layer's indexer (block scores, the
+2,048-block pool, top-512), the Reindex layers, and the gather/dequant
+attention of every layer (Reuse layers pass the group's index list unchanged).
+
+Default workload: the 20-layer decoder pattern [Full + 3 Reuse] + 4 x
+[Reindex + 3 Reuse] at 1,048,576 cached tokens, batch 4, seeded synthetic
+data.  Inputs are resident in HBM before the timed region; steps rotate over
+cache replicas so the 268 MB indexer-key set is re-read from HBM every step
+rather than from the 256 MB Infinity Cache.
+
+Prints one JSON line (rank 0) with queries/s, the roofline of the dominant
+kernel (the Full layer's indexer scan) measured with HIP events on the launch
+stream, and the CPU oracle timed on a bounded sample on the host.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+PEAK_HBM_GBS = 8000.0
+METRIC = "CSA2 decode queries/s at 1M ctx + achieved HBM GB/s as % of MI355X peak"
+SCORE_SRC = os.path.join(ROOT, "fp4_kv_cache_decode_amd", "csrc", "index_score.hip")
+COUNTER_FILE = os.path.join(ROOT, "profiles", "score_blocks_decoder20_1m_b4_counters.txt")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash(path=SCORE_SRC) -> str:
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def counter_traffic(workload: str):
+    """HBM bytes per scoring launch from committed rocprofv3 counters, scaled by
+    the copy-kernel calibration; None if absent or the kernel source changed."""
+    if not os.path.exists(COUNTER_FILE):
+        return None
+    txt = open(COUNTER_FILE).read()
+    kv = dict(re.findall(r"^(\w+)\s*=\s*(\S+)\s*$", txt, flags=re.M))
+    if kv.get("workload") != workload or kv.get("source_sha256") != source_hash():
+        return None
+    try:
+        fetch = float(kv["score_fetch_kib"]) * 1024 * float(kv["copy_fetch_factor"])
+        write = float(kv["score_write_kib"]) * 1024 * float(kv["copy_write_factor"])
+    except (KeyError, ValueError):
+        return None
+    return fetch + write
+
+
+class Setup:
+    """Device caches (replicas), per-layer inputs and output buffers."""
+
+    def __init__(self, wl, seed, replicas, want_oracle):
+        import torch
+
+        import fp4_kv_cache_decode_amd.csa2 as K
+        from fp4_kv_cache_decode_amd import datagen as G
+        self.K, self.G, self.wl = K, G, wl
+        B, N, L = wl.B, wl.N, len(wl.layers)
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        self.dev = dev
+        self.caches = [K.Cache(wl.n_seq, wl.cap, L, wl.w_cap) for _ in range(replicas)]
+        self.oc = None
+        if want_oracle:
+            import oracle as O
+            self.oc = O.Cache(wl.n_seq, wl.cap, L, wl.w_cap)
+        c0 = self.caches[0]
+        t0 = time.time()
+        w0 = max(0, N - G.WINDOW)
+        for s in range(wl.n_seq):
+            chunks = [(p, min(N, p + G.CHUNK)) for p in range(0, N, G.CHUNK)]
+            gen = G.parallel_map(lambda pr: G.kv_rows(seed, s, pr[0], pr[1]), chunks)
+            for (p0, p1), (k, v, ik) in zip(chunks, gen):
+                seq = np.full(p1 - p0, s, np.int32)
+                pos = np.arange(p0, p1, dtype=np.int64)
+                K.quantize_kv(c0, dev(k), dev(v), dev(seq), dev(pos), idx_k=dev(ik))
+                if self.oc is not None:
+                    self.oc.quantize(k, v, ik, None, None, seq, pos)
+            wk = np.stack([G.window_rows(seed, l, s, w0, N)[0] for l in range(L)])
+            wv = np.stack([G.window_rows(seed, l, s, w0, N)[1] for l in range(L)])
+            k, v, ik = G.kv_rows(seed, s, w0, N)
+            seq = np.full(N - w0, s, np.int32)
+            pos = np.arange(w0, N, dtype=np.int64)
+            K.quantize_kv(c0, dev(k), dev(v), dev(seq), dev(pos), win_k=dev(wk), win_v=dev(wv))
+            if self.oc is not None:
+                self.oc.quantize(k, v, None, wk, wv, seq, pos)
+            torch.cuda.synchronize()
+            log(f"[bench] cache seq {s + 1}/{wl.n_seq} built ({time.time() - t0:.1f}s)")
+        for c in self.caches[1:]:
+            c.kv.copy_(c0.kv)
+            c.idxk.copy_(c0.idxk)
+            c.wk.copy_(c0.wk)
+            c.wv.copy_(c0.wv)
+        torch.cuda.synchronize()
+
+        # the new token of every sequence: rows of position N-1 (already in the
+        # cache; re-writing them is the step's quantise-on-write work)
+        nk, nv, nik, nwk, nwv = [], [], [], [], []
+        for s in range(wl.n_seq):
+            k, v, ik = G.kv_rows(seed, s, N - 1, N)
+            nk.append(k), nv.append(v), nik.append(ik)
+            nwk.append(np.stack([G.window_rows(seed, l, s, N - 1, N)[0][0] for l in range(L)]))
+            nwv.append(np.stack([G.window_rows(seed, l, s, N - 1, N)[1][0] for l in range(L)]))
+        self.new = dict(k=dev(np.concatenate(nk)), v=dev(np.concatenate(nv)),
+                        ik=dev(np.concatenate(nik)),
+                        wk=dev(np.stack(nwk, axis=1)), wv=dev(np.stack(nwv, axis=1)),
+                        seq=dev(np.arange(wl.n_seq, dtype=np.int32)),
+                        pos=dev(np.full(wl.n_seq, N - 1, np.int64)))
+        self.np_new = dict(k=np.concatenate(nk), v=np.concatenate(nv), ik=np.concatenate(nik),
+                           wk=np.stack(nwk, axis=1), wv=np.stack(nwv, axis=1))
+        # per-layer queries
+        self.q = [G.attn_queries(seed, l, B) for l in range(L)]
+        self.qi = {l: G.index_queries(seed, l, B) for l in wl.index_layers()}
+        self.dq = [dev(x) for x in self.q]
+        self.dqi = {l: (dev(a), dev(b)) for l, (a, b) in self.qi.items()}
+        self.seq = dev(wl.seq())
+        self.ctx = dev(wl.ctx())
+        self.M = torch.empty((B, K.block_stride(N)), dtype=torch.float32, device="cuda")
+        self.pool = torch.empty((B, G.N_BLOCKS), dtype=torch.int32, device="cuda")
+        self.idx = torch.empty((B, G.TOPK), dtype=torch.int32, device="cuda")
+        self.out = torch.empty((L, B, G.H, G.D), dtype=torch.float32, device="cuda")
+        self.ws_ri = K.alloc_workspace(K.OP_INDEX_REINDEX, B)
+        self.ws_sel = K.alloc_workspace(K.OP_SELECT_POOL, B, N)
+        self.ws_at = K.alloc_workspace(K.OP_DECODE_ATTN, B)
+
+    def step(self, r, ev=None):
+        K, wl = self.K, self.wl
+        c = self.caches[r % len(self.caches)]
+        n = self.new
+        K.quantize_kv(c, n["k"], n["v"], n["seq"], n["pos"], idx_k=n["ik"], win_k=n["wk"],
+                      win_v=n["wv"])
+        for l, mode in enumerate(wl.layers):
+            if mode == "F":
+                qi, wi = self.dqi[l]
+                if ev is not None:
+                    ev[0].record()
+                K.index_block_scores(c, qi, wi, self.seq, self.ctx, wl.N, self.M)
+                if ev is not None:
+                    ev[1].record()
+                K.index_select_pool(self.M, self.ctx, wl.N, self.pool, self.ws_sel)
+                K.index_reindex(c, qi, wi, self.seq, self.ctx, self.pool, self.idx, self.ws_ri)
+            elif mode == "I":
+                qi, wi = self.dqi[l]
+                K.index_reindex(c, qi, wi, self.seq, self.ctx, self.pool, self.idx, self.ws_ri)
+            K.decode_attn(c, l, self.dq[l], self.idx, self.seq, self.ctx, self.out[l],
+                          self.ws_at)
+
+
+def oracle_step(S) -> float:
+    """One step of the same workload through the oracle; returns seconds."""
+    wl, oc = S.wl, S.oc
+    seq, ctx = wl.seq(), wl.ctx()
+    nn = S.np_new
+    t0 = time.perf_counter()
+    oc.quantize(nn["k"], nn["v"], nn["ik"], nn["wk"], nn["wv"], seq,
+                np.full(wl.n_seq, wl.N - 1, np.int64))
+    pool = idx = None
+    for l, mode in enumerate(wl.layers):
+        if mode == "F":
+            qi, wi = S.qi[l]
+            pool, idx, _, _ = oc.index_full(qi, wi, seq, ctx)
+        elif mode == "I":
+            qi, wi = S.qi[l]
+            idx, _ = oc.index_reindex(qi, wi, seq, ctx, pool)
+        oc.decode_attn(l, S.q[l], idx, seq, ctx)
+    return time.perf_counter() - t0
+
+
+def copy_bandwidth(nbytes=1 << 30, reps=10):
+    """Device-to-device copy rate (read + write bytes / time) as a measured peak."""
+    import torch
+    a = torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    b = torch.empty_like(a)
+    for _ in range(2):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    return 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decoder20_1m_b4")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--replicas", type=int, default=2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+              "the decode path needs no collectives and shards by sequence, so run one "
+              "process per GPU", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_probe:
+        log(f"[bench] copy probe: {copy_bandwidth():.0f} GB/s")
+        return
+
+    from fp4_kv_cache_decode_amd import datagen as G
+    wl = G.WORKLOADS[args.workload]
+    if wl.prefill:
+        print("bench.py: prefill workloads are parity cases, not bench lines", file=sys.stderr)
+        sys.exit(2)
+    B, N = wl.B, wl.N
+    want_cpu = not args.no_cpu_baseline
+    log(f"[bench] workload {wl.name}: B={B} N={N} layers={''.join(wl.layers)}")
+    S = Setup(wl, args.seed, args.replicas, want_cpu)
+
+    copy_gbs = copy_bandwidth()
+    log(f"[bench] device copy {copy_gbs:.0f} GB/s")
+
+    for i in range(args.warmup):
+        S.step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        S.step(args.warmup + i, evs[i])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    score_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    log(f"[bench] {ms:.3f} ms/step, Full-layer scan {score_ms * 1e3:.1f} us")
+
+    # roofline of the dominant kernel: the Full layer's indexer scan
+    n_keys = B * N
+    alg_bytes = n_keys * 64 + B * (-(-N // 8)) * 4 + B * (4 * 64 + 4) * 4
+    achieved = alg_bytes / (score_ms * 1e-3) / 1e9
+    traffic = counter_traffic(wl.name)
+
+    cpu = None
+    if want_cpu:
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        secs = oracle_step(S)
+        cpu = {"value": B / secs, "unit": "queries/s", "cores": threads, "kind": "oracle",
+               "sample": f"one full decode step of {wl.name} ({B} queries x {len(wl.layers)} "
+                         f"layers at {N} tokens) through the fp64 C oracle, OpenMP over "
+                         f"positions/queries, {secs:.1f} s wall"}
+        log(f"[bench] oracle step {secs:.2f} s")
+
+    res = {
+        "metric": METRIC,
+        "value": B / (ms * 1e-3),
+        "unit": "queries/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "batch": B, "ctx": N, "layers": "".join(wl.layers),
+                   "topk": G.TOPK, "window": G.WINDOW, "pool_blocks": G.N_BLOCKS,
+                   "block": G.BLOCK, "replicas": args.replicas, "seed": args.seed},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
+                     "traffic": traffic,
+                     "kernel": "score_kernel<false> (csa2_index_block_scores)",
+                     "avg_us": score_ms * 1e3, "alg_bytes": alg_bytes},
+        "cpu_baseline": cpu,
+        "hbm_copy_gbs": copy_gbs,
+    }
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

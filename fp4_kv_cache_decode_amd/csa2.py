@@ -15,7 +15,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH = range(5)
-OP_INDEX_FULL, OP_INDEX_REINDEX, OP_DECODE_ATTN = 1, 2, 3
+OP_INDEX_FULL, OP_INDEX_REINDEX, OP_DECODE_ATTN, OP_SELECT_POOL = 1, 2, 3, 4
 
 D, HEADS, IDX_HEADS, IDX_DIM, WINDOW, RECORD, BLOCK = 128, 16, 4, 64, 128, 144, 8
 
@@ -55,6 +55,10 @@ def lib():
                                       C.c_int32, C.c_int32, C.c_int32, _P, _P, _P, C.c_size_t, _P]
         L.csa2_index_reindex.argtypes = [C.POINTER(csa2_cache), _P, _P, _P, _P, C.c_int32, _P,
                                          C.c_int32, C.c_int32, C.c_int32, _P, _P, C.c_size_t, _P]
+        L.csa2_index_block_scores.argtypes = [C.POINTER(csa2_cache), _P, _P, _P, _P, C.c_int32,
+                                              C.c_int64, _P, C.c_int64, _P]
+        L.csa2_index_select_pool.argtypes = [_P, C.c_int64, _P, C.c_int32, C.c_int64, C.c_int32,
+                                             _P, _P, C.c_size_t, _P]
         L.csa2_decode_attn.argtypes = [C.POINTER(csa2_cache), C.POINTER(csa2_window), C.c_int32,
                                        _P, _P, _P, _P, C.c_int32, C.c_int32, C.c_float, _P, _P,
                                        C.c_size_t, _P]
@@ -64,7 +68,7 @@ def lib():
         L.csa2_status_string.argtypes = [C.c_int]
         L.csa2_status_string.restype = C.c_char_p
         for f in ("csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex",
-                  "csa2_decode_attn"):
+                  "csa2_decode_attn", "csa2_index_block_scores", "csa2_index_select_pool"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -164,6 +168,40 @@ def index_full(cache: Cache, q_idx, w, seq, ctx, max_ctx: int, pool, idx, ws,
     _check(st, "csa2_index_full")
 
 
+def block_stride(max_ctx: int) -> int:
+    """Row stride (floats) for block scores of contexts up to max_ctx."""
+    nb = -(-max_ctx // BLOCK)
+    return -(-nb // 64) * 64
+
+
+def index_block_scores(cache: Cache, q_idx, w, seq, ctx, max_ctx: int, M, stream=None) -> None:
+    B = q_idx.shape[0]
+    _need(q_idx, torch.float32, (B, IDX_HEADS, IDX_DIM), "q_idx")
+    _need(w, torch.float32, (B, IDX_HEADS), "w")
+    _need(seq, torch.int32, (B,), "seq")
+    _need(ctx, torch.int64, (B,), "ctx")
+    _need(M, torch.float32, None, "M")
+    if M.dim() != 2 or M.shape[0] != B:
+        raise ValueError("M: expected [B, m_stride]")
+    st = lib().csa2_index_block_scores(C.byref(cache.c), _ptr(q_idx), _ptr(w), _ptr(seq),
+                                       _ptr(ctx), B, max_ctx, _ptr(M), M.shape[1],
+                                       _stream(stream))
+    _check(st, "csa2_index_block_scores")
+
+
+def index_select_pool(M, ctx, max_ctx: int, pool, ws=None, stream=None) -> None:
+    B, n_blocks = pool.shape
+    _need(M, torch.float32, None, "M")
+    _need(ctx, torch.int64, (B,), "ctx")
+    _need(pool, torch.int32, (B, n_blocks), "pool")
+    if ws is not None:
+        _need(ws, torch.uint8, None, "ws")
+    st = lib().csa2_index_select_pool(_ptr(M), M.shape[1], _ptr(ctx), B, max_ctx, n_blocks,
+                                      _ptr(pool), _ptr(ws), 0 if ws is None else ws.numel(),
+                                      _stream(stream))
+    _check(st, "csa2_index_select_pool")
+
+
 def index_reindex(cache: Cache, q_idx, w, seq, ctx, pool, idx, ws, block: int = 8,
                   topk: int = 512, stream=None) -> None:
     B = q_idx.shape[0]
@@ -201,6 +239,6 @@ def decode_attn(cache: Cache, layer: int, q, idx, seq, ctx, out, ws, sm_scale=No
 def alloc_workspace(op: int, B: int, max_ctx: int = 0, n_blocks: int = 2048, topk: int = 512,
                     device="cuda") -> torch.Tensor:
     n = workspace_bytes(op, B, max_ctx, n_blocks, BLOCK, topk)
-    if n == 0 and B > 0:
+    if n == 0 and B > 0 and op != OP_SELECT_POOL:      # selection may need none
         raise Csa2Error(ERR_INVALID_ARG, "csa2_workspace_bytes")
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)

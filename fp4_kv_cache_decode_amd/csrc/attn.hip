@@ -96,6 +96,24 @@ __global__ void __launch_bounds__(AT_THREADS) attn_kernel(AttnArgs a) {
     const bool is_main = tile < a.n_main;
     float* part = a.part + ((int64_t)b * a.n_tiles + tile) * ATTN_PART_FLOATS;
 
+    // ---- query fragments first, independent of the gather chain (A operand,
+    // hi/lo f16): Q[h = lane%16][16ks + 4(lane/16) + 0..3]
+    half4_t qhi[8], qlo[8];
+    {
+        const int h = lane & 15, g = lane >> 4;
+        const float* qrow = a.q + ((int64_t)b * HEADS + h) * D + 4 * g;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const float4 v = *reinterpret_cast<const float4*>(qrow + 16 * ks);
+            const float x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                _Float16 hi = (_Float16)x[i];
+                qhi[ks][i] = hi;
+                qlo[ks][i] = (_Float16)(x[i] - (float)hi);
+            }
+        }
+    }
     // ---- gather + dequantise: 4 threads per entry, 32 channels each
     {
         const int e = t >> 2, q4 = t & 3;
@@ -159,23 +177,6 @@ __global__ void __launch_bounds__(AT_THREADS) attn_kernel(AttnArgs a) {
         if (q4 == 0) sh.valid[e] = ok;
     }
 
-    // ---- query fragments (A operand, hi/lo f16): Q[h = lane%16][16ks + 4(lane/16) + 0..3]
-    half4_t qhi[8], qlo[8];
-    {
-        const int h = lane & 15, g = lane >> 4;
-        const float* qrow = a.q + ((int64_t)b * HEADS + h) * D + 4 * g;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const float4 v = *reinterpret_cast<const float4*>(qrow + 16 * ks);
-            const float x[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                _Float16 hi = (_Float16)x[i];
-                qhi[ks][i] = hi;
-                qlo[ks][i] = (_Float16)(x[i] - (float)hi);
-            }
-        }
-    }
     __syncthreads();
 
     // ---- S = Q K^T for entries 16*wave .. +15
@@ -274,24 +275,37 @@ __global__ void __launch_bounds__(AT_THREADS) attn_kernel(AttnArgs a) {
 }
 
 // Combine the tiles of each query: out = sum_t e^(m_t - M) o_t / sum_t e^(m_t - M) l_t.
+// The tiles' (m, l) pairs are staged in LDS first; each thread then owns 8
+// output dims of one head and streams the tiles' partial outputs with several
+// loads in flight.
+constexpr int MAX_TILES = CSA2_MAX_TOPK / TILE + 2;
+
 __global__ void __launch_bounds__(AT_THREADS) attn_merge_kernel(const float* part, int32_t n_tiles,
                                                                  float* out) {
+    __shared__ float s_m[MAX_TILES][HEADS];
+    __shared__ float s_l[MAX_TILES][HEADS];
     const int b = blockIdx.x;
     const int t = threadIdx.x;
+    const float* pb = part + (int64_t)b * n_tiles * ATTN_PART_FLOATS;
+    for (int i = t; i < n_tiles * HEADS; i += AT_THREADS) {
+        const int tile = i / HEADS, h = i % HEADS;
+        s_m[tile][h] = pb[tile * ATTN_PART_FLOATS + h];
+        s_l[tile][h] = pb[tile * ATTN_PART_FLOATS + HEADS + h];
+    }
+    __syncthreads();
     const int h = t >> 4;                 // 16 threads per head
     const int d0 = (t & 15) * 8;          // 8 dims each
-    const float* pb = part + (int64_t)b * n_tiles * ATTN_PART_FLOATS;
     float M = NEG_INF;
-    for (int i = 0; i < n_tiles; ++i) M = fmaxf(M, pb[i * ATTN_PART_FLOATS + h]);
+    for (int i = 0; i < n_tiles; ++i) M = fmaxf(M, s_m[i][h]);
     float L = 0.0f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (M != NEG_INF) {
+#pragma unroll 4
         for (int i = 0; i < n_tiles; ++i) {
-            const float* pt = pb + i * ATTN_PART_FLOATS;
-            const float mt = pt[h];
-            if (mt == NEG_INF) continue;
-            const float wgt = expf(mt - M);
-            L += wgt * pt[HEADS + h];
-            const float4* o = reinterpret_cast<const float4*>(pt + 2 * HEADS + h * D + d0);
+            const float mt = s_m[i][h];
+            const float wgt = mt == NEG_INF ? 0.0f : expf(mt - M);
+            L += wgt * s_l[i][h];
+            const float4* o =
+                reinterpret_cast<const float4*>(pb + i * ATTN_PART_FLOATS + 2 * HEADS + h * D + d0);
             const float4 o0 = o[0], o1 = o[1];
             acc[0] += wgt * o0.x;
             acc[1] += wgt * o0.y;

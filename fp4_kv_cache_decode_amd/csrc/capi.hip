@@ -21,8 +21,13 @@ int64_t m_stride(int64_t max_ctx) {
     return (nb + 63) / 64 * 64;
 }
 
+// Workspace of the top-k stages for rows of up to max_n entries.
+size_t select_bytes(int32_t B, int64_t max_n) {
+    return align_up(csa2::topk_workspace_bytes(B, max_n));
+}
+
 struct FullLayout {
-    size_t m_off, pool_off, s_off, total;
+    size_t m_off, pool_off, s_off, sel_off, total;
 };
 
 FullLayout full_layout(int32_t B, int64_t max_ctx, int32_t n_blocks) {
@@ -30,12 +35,16 @@ FullLayout full_layout(int32_t B, int64_t max_ctx, int32_t n_blocks) {
     L.m_off = 0;
     L.pool_off = align_up(L.m_off + (size_t)B * (size_t)m_stride(max_ctx) * sizeof(float));
     L.s_off = align_up(L.pool_off + (size_t)B * (size_t)n_blocks * sizeof(int32_t));
-    L.total = align_up(L.s_off + (size_t)B * (size_t)n_blocks * BLOCK * sizeof(float));
+    L.sel_off = align_up(L.s_off + (size_t)B * (size_t)n_blocks * BLOCK * sizeof(float));
+    const size_t sel_blocks = select_bytes(B, (max_ctx + BLOCK - 1) / BLOCK);
+    const size_t sel_pool = select_bytes(B, (int64_t)n_blocks * BLOCK);
+    L.total = L.sel_off + (sel_blocks > sel_pool ? sel_blocks : sel_pool);
     return L;
 }
 
 size_t reindex_bytes(int32_t B, int32_t n_blocks) {
-    return align_up((size_t)B * (size_t)n_blocks * BLOCK * sizeof(float));
+    return align_up((size_t)B * (size_t)n_blocks * BLOCK * sizeof(float)) +
+           select_bytes(B, (int64_t)n_blocks * BLOCK);
 }
 
 size_t attn_bytes(int32_t B, int32_t topk) {
@@ -71,6 +80,15 @@ csa2_status check_select(int32_t B, int32_t n_blocks, int32_t block, int32_t top
 
 csa2_status launched(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_LAUNCH; }
 
+// Keys per scoring workgroup: about 2048 workgroups in total (several per CU on
+// 256 CUs), each a multiple of 256 keys (4 waves x 64), at most 4096.
+int32_t keys_per_wg(int32_t B, int64_t max_ctx) {
+    const int64_t total = (int64_t)B * max_ctx;
+    int64_t kpw = (total + 2047) / 2048;
+    kpw = (kpw + 255) / 256 * 256;
+    return (int32_t)(kpw < 256 ? 256 : (kpw > 4096 ? 4096 : kpw));
+}
+
 }  // namespace
 
 extern "C" {
@@ -99,6 +117,9 @@ size_t csa2_workspace_bytes(int32_t op, int32_t B, int64_t max_ctx, int32_t n_bl
         case CSA2_OP_DECODE_ATTN:
             if (topk < 1 || topk > CSA2_MAX_TOPK) return 0;
             return attn_bytes(B, topk);
+        case CSA2_OP_SELECT_POOL:
+            if (max_ctx < 0 || n_blocks < 1 || n_blocks > CSA2_MAX_POOL) return 0;
+            return select_bytes(B, (max_ctx + BLOCK - 1) / BLOCK);
     }
     return 0;
 }
@@ -140,24 +161,50 @@ csa2_status csa2_index_full(const csa2_cache* cache, const float* q_idx, const f
     float* M = reinterpret_cast<float*>(base + L.m_off);
     int32_t* pool_out = pool ? pool : reinterpret_cast<int32_t*>(base + L.pool_off);
     float* S = reinterpret_cast<float*>(base + L.s_off);
-
-    // enough workgroups to fill 256 CUs several times over
-    const int64_t total = (int64_t)B * max_ctx;
-    int64_t kpw = (total + 2047) / 2048;
-    kpw = (kpw + 255) / 256 * 256;
-    kpw = kpw < 256 ? 256 : (kpw > 4096 ? 4096 : kpw);
+    void* sel = base + L.sel_off;
 
     hipError_t e = csa2::launch_score_blocks(*cache, q_idx, w, seq, ctx, B, max_ctx,
-                                             m_stride(max_ctx), M, (int32_t)kpw, stream);
+                                             m_stride(max_ctx), M, keys_per_wg(B, max_ctx),
+                                             stream);
     if (e != hipSuccess) return CSA2_ERR_LAUNCH;
     e = csa2::launch_topk(M, m_stride(max_ctx), ctx, max_ctx, 0, nullptr, 0, B, n_blocks,
-                          pool_out, stream);
+                          pool_out, sel, stream);
     if (e != hipSuccess) return CSA2_ERR_LAUNCH;
     e = csa2::launch_score_pool(*cache, q_idx, w, seq, ctx, B, pool_out, n_blocks, S, stream);
     if (e != hipSuccess) return CSA2_ERR_LAUNCH;
     return launched(csa2::launch_topk(S, (int64_t)n_blocks * BLOCK, nullptr, 0,
-                                      n_blocks * BLOCK, pool_out, n_blocks, B, topk, idx,
+                                      n_blocks * BLOCK, pool_out, n_blocks, B, topk, idx, sel,
                                       stream));
+}
+
+csa2_status csa2_index_block_scores(const csa2_cache* cache, const float* q_idx, const float* w,
+                                    const int32_t* seq, const int64_t* ctx, int32_t B,
+                                    int64_t max_ctx, float* M, int64_t m_stride_,
+                                    hipStream_t stream) {
+    csa2_status st = check_cache(cache, false, true);
+    if (st != CSA2_OK) return st;
+    if (!q_idx || !w || !seq || !ctx || !M || B < 0) return CSA2_ERR_INVALID_ARG;
+    if (B > 65535) return CSA2_ERR_UNSUPPORTED;
+    if (max_ctx < 0 || max_ctx > cache->cap) return CSA2_ERR_INVALID_ARG;
+    if (m_stride_ < (max_ctx + BLOCK - 1) / BLOCK) return CSA2_ERR_INVALID_ARG;
+    if (B == 0 || max_ctx == 0) return CSA2_OK;
+    return launched(csa2::launch_score_blocks(*cache, q_idx, w, seq, ctx, B, max_ctx, m_stride_,
+                                              M, keys_per_wg(B, max_ctx), stream));
+}
+
+csa2_status csa2_index_select_pool(const float* M, int64_t m_stride_, const int64_t* ctx,
+                                   int32_t B, int64_t max_ctx, int32_t n_blocks, int32_t* pool,
+                                   void* ws, size_t ws_bytes, hipStream_t stream) {
+    if (!M || !ctx || !pool || B < 0 || max_ctx < 0) return CSA2_ERR_INVALID_ARG;
+    if (B > 65535 || n_blocks < 1 || n_blocks > CSA2_MAX_POOL) return CSA2_ERR_UNSUPPORTED;
+    if (m_stride_ < (max_ctx + BLOCK - 1) / BLOCK) return CSA2_ERR_INVALID_ARG;
+    // rows are read as float4: 16-byte aligned rows
+    if ((reinterpret_cast<uintptr_t>(M) & 15) || (m_stride_ & 3)) return CSA2_ERR_INVALID_ARG;
+    if (B == 0) return CSA2_OK;
+    const size_t need = select_bytes(B, (max_ctx + BLOCK - 1) / BLOCK);
+    if (need && (!ws || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
+    return launched(csa2::launch_topk(M, m_stride_, ctx, max_ctx, 0, nullptr, 0, B, n_blocks,
+                                      pool, ws, stream));
 }
 
 csa2_status csa2_index_reindex(const csa2_cache* cache, const float* q_idx, const float* w,
@@ -173,11 +220,14 @@ csa2_status csa2_index_reindex(const csa2_cache* cache, const float* q_idx, cons
     if (B == 0) return CSA2_OK;
     if (!ws || ws_bytes < reindex_bytes(B, n_blocks)) return CSA2_ERR_WORKSPACE;
     float* S = static_cast<float*>(ws);
+    void* sel = static_cast<char*>(ws) +
+                align_up((size_t)B * (size_t)n_blocks * BLOCK * sizeof(float));
     hipError_t e = csa2::launch_score_pool(*cache, q_idx, w, seq, ctx, B, pool, n_blocks, S,
                                            stream);
     if (e != hipSuccess) return CSA2_ERR_LAUNCH;
     return launched(csa2::launch_topk(S, (int64_t)n_blocks * BLOCK, nullptr, 0,
-                                      n_blocks * BLOCK, pool, n_blocks, B, topk, idx, stream));
+                                      n_blocks * BLOCK, pool, n_blocks, B, topk, idx, sel,
+                                      stream));
 }
 
 csa2_status csa2_decode_attn(const csa2_cache* cache, const csa2_window* win, int32_t layer,

@@ -31,12 +31,14 @@ hipError_t launch_score_pool(const csa2_cache& c, const float* q_idx, const floa
 
 // Top-k select per row, ties to the lower index, output ascending, -1 padded.
 // Row b has n = ceil(ctx[b]/8) entries (ctx != null, block mode) or n_fixed
-// entries (pool mode, -inf entries are absent).  With pool != null an entry i
-// is reported as pool[b][i/8]*8 + i%8, else as i.
+// entries (pool mode); -inf entries are absent.  With pool != null an entry i
+// is reported as pool[b][i/8]*8 + i%8, else as i.  ws must hold
+// topk_workspace_bytes(B, longest row) bytes (may be null when that is 0).
 hipError_t launch_topk(const float* vals, int64_t stride, const int64_t* ctx,
                        int64_t max_ctx, int32_t n_fixed, const int32_t* pool,
-                       int32_t n_blocks, int32_t B, int32_t k, int32_t* out,
+                       int32_t n_blocks, int32_t B, int32_t k, int32_t* out, void* ws,
                        hipStream_t stream);
+size_t topk_workspace_bytes(int32_t B, int64_t max_n);
 
 // Split-K gather/dequant attention for one layer plus the cross-split merge.
 hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,

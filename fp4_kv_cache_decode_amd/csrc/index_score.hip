@@ -8,15 +8,16 @@
 //     score_t = sum_h w_h * max(0, q_h . khat_t),  khat_t = E4M3(code_t) * scale,
 // with 4 heads of 64 dims, and a block's score as the max over its 8 positions.
 //
-// Design (gfx950, wave64, HBM-bound): a wave scores 64 keys (4 KB) per step.
-// Each key is split over a lane pair: lane 2m+r holds dims 32r..32r+31 of keys
-// m and 32+m, so a lane keeps only half of the 4x64 query in VGPRs (128 regs)
-// and streams its keys with 16-byte loads.  The FP8->fp32 conversion uses the
-// packed converter (2 values per instruction) and the dot products are plain
-// fp32 FMAs (the 1e-5 relative score budget rules out f16 query math).  One
-// DPP exchange per head finishes each key: the lane pair swaps the half-sums of
-// the key it does not keep.  Block maxima come from row_ror DPP max over lanes
-// of equal parity, so no LDS is touched in the hot loop.
+// Design (gfx950, wave64, HBM-bound): one key per lane, 64 keys (4 KB) per wave
+// step.  The query is the same for the whole workgroup, so it is read as scalar
+// (SGPR) operands of v_fma_f32 straight from the scalar cache, one head (64
+// floats) at a time: no lane holds a copy of it, no cross-lane reduction is
+// needed, and a lane needs only its key (16 dwords raw, 64 floats converted)
+// plus the next key in flight, which keeps occupancy at 4 waves per SIMD while
+// loads for step i+1 overlap the arithmetic of step i.  FP8->fp32 uses the
+// packed converter (2 values per instruction); the dot products are plain fp32
+// FMAs (the 1e-5 relative score budget rules out f16 query math).  Block maxima
+// come from DPP/swizzle max over the 8 lanes of a block, no LDS involved.
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
@@ -25,7 +26,8 @@ namespace csa2 {
 namespace {
 
 constexpr int SC_THREADS = 256;
-constexpr int KEYS_PER_STEP = 64;        // per wave
+constexpr int STEP = 64;                 // keys per wave step
+constexpr int WAVES = SC_THREADS / 64;
 constexpr float NEG_INF = -__builtin_huge_valf();
 
 struct ScoreArgs {
@@ -45,122 +47,122 @@ struct ScoreArgs {
     float scale;
 };
 
-// Dot products of one lane's 32 dims of a key with the 4 head half-queries.
-__device__ __forceinline__ void half_dots(const uint4& a, const uint4& b, const float (&qv)[4][32],
-                                          float (&acc)[4]) {
-    const uint32_t dw[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int h = 0; h < 4; ++h) acc[h] = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        float2 lo = e4m3x2_to_f32<false>(dw[i]);
-        float2 hi = e4m3x2_to_f32<true>(dw[i]);
-#pragma unroll
-        for (int h = 0; h < 4; ++h) {
-            acc[h] = fmaf(qv[h][4 * i + 0], lo.x, acc[h]);
-            acc[h] = fmaf(qv[h][4 * i + 1], lo.y, acc[h]);
-            acc[h] = fmaf(qv[h][4 * i + 2], hi.x, acc[h]);
-            acc[h] = fmaf(qv[h][4 * i + 3], hi.y, acc[h]);
-        }
-    }
+struct Raw {
+    uint4 d[4];
+};
+
+// Lanes whose key is not visible load key 0 of the sequence (always in bounds)
+// and have their score masked later: no branch, no register clearing.
+__device__ __forceinline__ void load_key(Raw& r, const uint8_t* keys, int64_t t, bool ok) {
+    const uint4* p = reinterpret_cast<const uint4*>(keys + (ok ? t : 0) * IDX_DIM);
+    r.d[0] = p[0];
+    r.d[1] = p[1];
+    r.d[2] = p[2];
+    r.d[3] = p[3];
 }
 
-// Finish a lane-pair key: returns the score of the key this lane keeps.
-__device__ __forceinline__ float finish_score(const float (&accA)[4], const float (&accB)[4],
-                                              bool odd, const float (&wh)[4], float scale) {
+// Score of one key (64 E4M3 codes) against the workgroup's query.
+__device__ __forceinline__ float key_score(const Raw& r, const float* __restrict__ q,
+                                           const float (&wh)[4], float scale) {
+    float kf[64];
+    const uint32_t dw[16] = {r.d[0].x, r.d[0].y, r.d[0].z, r.d[0].w, r.d[1].x, r.d[1].y,
+                             r.d[1].z, r.d[1].w, r.d[2].x, r.d[2].y, r.d[2].z, r.d[2].w,
+                             r.d[3].x, r.d[3].y, r.d[3].z, r.d[3].w};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const float2 lo = e4m3x2_to_f32<false>(dw[i]);
+        const float2 hi = e4m3x2_to_f32<true>(dw[i]);
+        kf[4 * i] = lo.x;
+        kf[4 * i + 1] = lo.y;
+        kf[4 * i + 2] = hi.x;
+        kf[4 * i + 3] = hi.y;
+    }
     float s = 0.0f;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-        float keep = odd ? accB[h] : accA[h];
-        float send = odd ? accA[h] : accB[h];
-        float dot = (keep + dpp_f32<DPP_XOR1>(send)) * scale;
-        s = fmaf(wh[h], fmaxf(dot, 0.0f), s);
+        const float* qh = q + 64 * h;
+        float a0 = 0.0f, a1 = 0.0f;
+#pragma unroll
+        for (int d = 0; d < 64; d += 2) {
+            a0 = fmaf(qh[d], kf[d], a0);
+            a1 = fmaf(qh[d + 1], kf[d + 1], a1);
+        }
+        s = fmaf(wh[h], fmaxf((a0 + a1) * scale, 0.0f), s);
     }
     return s + 0.0f;
 }
 
+// q, keys and out are distinct buffers (restrict), so the query loads are
+// provably unclobbered and can be scalar loads.  `zero` is 0 at run time; adding
+// zero * step to the query address makes it loop-variant, so the compiler
+// reloads one head at a time (64 SGPRs) instead of hoisting all 256 floats.
 template <bool POOL>
-__global__ void __launch_bounds__(SC_THREADS) score_kernel(ScoreArgs a) {
+__global__ void __launch_bounds__(SC_THREADS)
+score_kernel(ScoreArgs a, const float* __restrict__ q_all, const uint8_t* __restrict__ idxk,
+             float* __restrict__ out_all, int64_t zero) {
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
-    const bool odd = lane & 1;
-    const int m = lane >> 1;
+    // wave index is uniform per wave; say so, so that k0 and the query address are SGPRs
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t N = clamp64(a.ctx[b], 0, a.max_ctx);
     const int32_t s = a.seq[b];
     if (s < 0 || s >= a.n_seq) return;
     const int64_t n_items = POOL ? (int64_t)a.n_blocks * BLOCK : N;
     const int64_t wg0 = (int64_t)blockIdx.x * a.keys_per_wg;
     if (wg0 >= n_items) return;
+    const int64_t wg_end = wg0 + a.keys_per_wg < n_items ? wg0 + a.keys_per_wg : n_items;
 
-    const uint8_t* keys = a.idxk + (int64_t)s * a.cap * IDX_DIM;
-    float qv[4][32];
+    const uint8_t* keys = idxk + (int64_t)s * a.cap * IDX_DIM;
+    const float* q = q_all + (int64_t)b * IDX_HEADS * IDX_DIM;
     float wh[4];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-        const float4* qp = reinterpret_cast<const float4*>(a.q_idx + ((int64_t)b * 4 + h) * 64 + 32 * odd);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float4 t = qp[i];
-            qv[h][4 * i] = t.x;
-            qv[h][4 * i + 1] = t.y;
-            qv[h][4 * i + 2] = t.z;
-            qv[h][4 * i + 3] = t.w;
-        }
-        wh[h] = a.w[(int64_t)b * 4 + h];
-    }
+    for (int h = 0; h < 4; ++h) wh[h] = a.w[(int64_t)b * IDX_HEADS + h];
+    float* out = out_all + (int64_t)b * a.out_stride;
     const int32_t* pool = POOL ? a.pool + (int64_t)b * a.n_blocks : nullptr;
-    float* out = a.out + (int64_t)b * a.out_stride;
 
-    const int64_t wg_end = wg0 + a.keys_per_wg < n_items ? wg0 + a.keys_per_wg : n_items;
-    for (int64_t k0 = wg0 + (int64_t)wave * KEYS_PER_STEP; k0 < wg_end;
-         k0 += (int64_t)KEYS_PER_STEP * (SC_THREADS / 64)) {
-        // item indices of the two keys this lane touches
-        const int64_t iA = k0 + m, iB = k0 + 32 + m;
-        int64_t tA = iA, tB = iB;
-        bool vA, vB;
+    // position of item i (pool mode maps through the block list); ok = visible
+    auto locate = [&](int64_t i, int64_t& t) -> bool {
         if (POOL) {
-            int32_t pa = iA < n_items ? pool[iA >> 3] : -1;
-            int32_t pb = iB < n_items ? pool[iB >> 3] : -1;
-            tA = (int64_t)pa * BLOCK + (iA & 7);
-            tB = (int64_t)pb * BLOCK + (iB & 7);
-            vA = pa >= 0 && tA < N;
-            vB = pb >= 0 && tB < N;
-        } else {
-            vA = iA < N;
-            vB = iB < N;
+            const int32_t pb = i < n_items ? pool[i >> 3] : -1;
+            t = (int64_t)pb * BLOCK + (i & 7);
+            return pb >= 0 && t < N;
         }
-        uint4 a0 = make_uint4(0, 0, 0, 0), a1 = a0, b0 = a0, b1 = a0;
-        if (vA) {
-            const uint4* p = reinterpret_cast<const uint4*>(keys + tA * IDX_DIM + 32 * odd);
-            a0 = p[0];
-            a1 = p[1];
-        }
-        if (vB) {
-            const uint4* p = reinterpret_cast<const uint4*>(keys + tB * IDX_DIM + 32 * odd);
-            b0 = p[0];
-            b1 = p[1];
-        }
-        float accA[4], accB[4];
-        half_dots(a0, a1, qv, accA);
-        half_dots(b0, b1, qv, accB);
-        float sc = finish_score(accA, accB, odd, wh, a.scale);
-        const bool valid = odd ? vB : vA;     // the kept key
-        sc = valid ? sc : NEG_INF;
+        t = i;
+        return i < N;
+    };
+    auto finish = [&](const Raw& r, int64_t k0, bool ok) {
+        float sc = key_score(r, q + zero * k0, wh, a.scale);
+        sc = ok ? sc : NEG_INF;
+        const int64_t item = k0 + lane;
         if (POOL) {
-            const int64_t item = odd ? iB : iA;
             if (item < n_items) out[item] = sc;
         } else {
-            // same-parity lanes of a 16-lane row hold one block of 8 keys
-            float mx = fmaxf(sc, dpp_f32<DPP_ROR2>(sc));
-            mx = fmaxf(mx, dpp_f32<DPP_ROR4>(mx));
-            mx = fmaxf(mx, dpp_f32<DPP_ROR8>(mx));
-            if ((lane & 14) == 0) {           // lanes 16c and 16c+1
-                const int c = lane >> 4;
-                const int64_t blk = (k0 >> 3) + c + 4 * odd;
-                if (blk * BLOCK < N) out[blk] = mx;
-            }
+            // lanes 8m..8m+7 hold block (k0/8 + m)
+            float mx = fmaxf(sc, dpp_f32<DPP_XOR1>(sc));
+            mx = fmaxf(mx, dpp_f32<DPP_XOR2>(mx));
+            mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(mx), 0x101f)));
+            const int64_t blk = (k0 >> 3) + (lane >> 3);
+            if ((lane & 7) == 0 && blk * BLOCK < N) out[blk] = mx;
         }
+    };
+
+    // ping-pong: the loads of the next step are in flight during this step
+    const int64_t stride = (int64_t)STEP * WAVES;
+    int64_t k0 = wg0 + (int64_t)wave * STEP;
+    Raw A, B;
+    int64_t tA, tB;
+    bool okA = k0 < wg_end && locate(k0 + lane, tA);
+    load_key(A, keys, tA, okA);
+    for (; k0 < wg_end; k0 += 2 * stride) {
+        const int64_t k1 = k0 + stride;
+        const bool okB = k1 < wg_end && locate(k1 + lane, tB);
+        load_key(B, keys, tB, okB);
+        finish(A, k0, okA);
+        if (k1 >= wg_end) break;
+        const int64_t k2 = k1 + stride;
+        okA = k2 < wg_end && locate(k2 + lane, tA);
+        load_key(A, keys, tA, okA);
+        finish(B, k1, okB);
     }
 }
 
@@ -185,7 +187,8 @@ hipError_t launch_score_blocks(const csa2_cache& c, const float* q_idx, const fl
     a.scale = c.idxk_scale;
     dim3 grid((unsigned)((max_ctx + keys_per_wg - 1) / keys_per_wg), (unsigned)B);
     if (grid.x == 0) return hipSuccess;
-    hipLaunchKernelGGL(score_kernel<false>, grid, dim3(SC_THREADS), 0, stream, a);
+    hipLaunchKernelGGL(score_kernel<false>, grid, dim3(SC_THREADS), 0, stream, a, q_idx, c.idxk,
+                       M, (int64_t)0);
     return hipGetLastError();
 }
 
@@ -206,11 +209,12 @@ hipError_t launch_score_pool(const csa2_cache& c, const float* q_idx, const floa
     a.out_stride = (int64_t)n_blocks * BLOCK;
     a.n_seq = c.n_seq;
     a.n_blocks = n_blocks;
-    a.keys_per_wg = 1024;
+    a.keys_per_wg = STEP * WAVES;           // one step per wave: latency, not bandwidth
     a.scale = c.idxk_scale;
     const int64_t items = (int64_t)n_blocks * BLOCK;
     dim3 grid((unsigned)((items + a.keys_per_wg - 1) / a.keys_per_wg), (unsigned)B);
-    hipLaunchKernelGGL(score_kernel<true>, grid, dim3(SC_THREADS), 0, stream, a);
+    hipLaunchKernelGGL(score_kernel<true>, grid, dim3(SC_THREADS), 0, stream, a, q_idx, c.idxk,
+                       S, (int64_t)0);
     return hipGetLastError();
 }
 

@@ -101,7 +101,12 @@ typedef struct csa2_window {
 } csa2_window;
 
 /* Operation ids for csa2_workspace_bytes. */
-enum { CSA2_OP_INDEX_FULL = 1, CSA2_OP_INDEX_REINDEX = 2, CSA2_OP_DECODE_ATTN = 3 };
+enum {
+    CSA2_OP_INDEX_FULL = 1,
+    CSA2_OP_INDEX_REINDEX = 2,
+    CSA2_OP_DECODE_ATTN = 3,
+    CSA2_OP_SELECT_POOL = 4
+};
 
 /*
  * csa2_quantize_kv - quantise-on-write of n new tokens.
@@ -168,6 +173,31 @@ csa2_status csa2_index_reindex(const csa2_cache* cache, const float* q_idx, cons
                                const int32_t* pool, int32_t n_blocks, int32_t block,
                                int32_t topk, int32_t* idx, void* ws, size_t ws_bytes,
                                hipStream_t stream);
+
+/*
+ * Stages of csa2_index_full, for callers that schedule (or time) them apart.
+ * csa2_index_full(q, w) is exactly csa2_index_block_scores, then
+ * csa2_index_select_pool, then csa2_index_reindex with the same q and w.
+ *
+ * csa2_index_block_scores - M[b][j] = max of score_t over block j's positions
+ * t < N, for j < ceil(N/8); entries j >= ceil(N/8) are left untouched.
+ *   M         [B][m_stride] fp32 out, m_stride >= ceil(max_ctx/8).
+ */
+csa2_status csa2_index_block_scores(const csa2_cache* cache, const float* q_idx, const float* w,
+                                    const int32_t* seq, const int64_t* ctx, int32_t B,
+                                    int64_t max_ctx, float* M, int64_t m_stride,
+                                    hipStream_t stream);
+
+/*
+ * csa2_index_select_pool - pool[b] = the n_blocks largest of M[b][0..ceil(N/8))
+ * (ties to the lower block), ascending, -1 padded.  n_blocks in 1..4096.  M must
+ * be 16-byte aligned with m_stride a multiple of 4; -inf entries count as absent.
+ *   ws        csa2_workspace_bytes(CSA2_OP_SELECT_POOL, B, max_ctx, n_blocks, 8, 1)
+ *             bytes (zero for rows of up to 16,384 blocks; ws may then be NULL).
+ */
+csa2_status csa2_index_select_pool(const float* M, int64_t m_stride, const int64_t* ctx,
+                                   int32_t B, int64_t max_ctx, int32_t n_blocks, int32_t* pool,
+                                   void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
  * csa2_decode_attn - gather, dequantise and attend for one layer.

@@ -332,3 +332,30 @@ def test_determinism(K):
         torch.cuda.synchronize()
         outs.append(out.cpu().numpy())
     assert np.array_equal(outs[0], outs[1])
+
+
+def test_index_full_equals_its_stages(K):
+    """csa2_index_full == block scores -> select pool -> reindex with the same query."""
+    _say("index_full vs stages")
+    N, B = 70001, 3
+    oc, gc = _setup(K, 41, B, N)
+    q, w = G.index_queries(41, 0, B)
+    seq = np.arange(B, dtype=np.int32)
+    ctx = np.array([N, N - 9, 30000], np.int64)
+    gpool, gidx = _run_full(K, gc, q, w, seq, ctx, N)
+    M = torch.empty((B, K.block_stride(N)), dtype=torch.float32, device="cuda")
+    pool = torch.empty((B, 2048), dtype=torch.int32, device="cuda")
+    idx = torch.empty((B, 512), dtype=torch.int32, device="cuda")
+    ws = K.alloc_workspace(K.OP_INDEX_REINDEX, B)
+    K.index_block_scores(gc, dev(q), dev(w), dev(seq), dev(ctx), N, M)
+    K.index_select_pool(M, dev(ctx), N, pool, K.alloc_workspace(K.OP_SELECT_POOL, B, N))
+    K.index_reindex(gc, dev(q), dev(w), dev(seq), dev(ctx), pool, idx, ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(pool.cpu().numpy(), gpool)
+    assert np.array_equal(idx.cpu().numpy(), gidx)
+    # block scores against the oracle's block maxima (fp32 vs fp64 scores)
+    Mh = M.cpu().numpy()
+    for b in range(B):
+        sc = oc.scores(b, q[b], w[b], int(ctx[b]))
+        want = block_scores(sc, int(ctx[b]))
+        np.testing.assert_allclose(Mh[b, :len(want)], want, rtol=2e-6, atol=1e-6)
