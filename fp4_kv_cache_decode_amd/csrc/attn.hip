@@ -18,6 +18,11 @@
 // fp32-accurate, far inside the 2e-3 output budget.  Each tile writes its
 // running max m, sum l and unnormalised output o; a merge kernel rescales and
 // combines the tiles (the same algebra an unsplit online softmax uses).
+//
+// FP4 dequantisation: the f16 encodings of the E2M1 magnitudes {0, .5, 1, 1.5,
+// 2, 3, 4, 6} differ only in their high byte, so v_perm_b32 with an 8-byte table
+// turns four code nibbles into four f16 high bytes in one instruction; a packed
+// f16 multiply by the group's E4M3 scale is exact (at most 6 significant bits).
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
@@ -65,22 +70,34 @@ struct AttnShared {
     int valid[TILE];
 };
 
-__device__ __forceinline__ _Float16 h_from_bits(uint32_t b) {
-    unsigned short s = (unsigned short)b;
-    return __builtin_bit_cast(_Float16, s);
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+
+// f16 high bytes of the E2M1 magnitudes 0..3 and 4..7 (a v_perm_b32 table).
+constexpr uint32_t E2M1_HB_LO = 0x3E3C3800u;
+constexpr uint32_t E2M1_HB_HI = 0x46444240u;
+
+// f16 value of a signed E4M3 scale code (exact).
+__device__ __forceinline__ half2_t scale_h2(uint32_t code) {
+    const float s = e4m3_value_pos(code & 0x7f) * ((code & 0x80) ? -1.0f : 1.0f);
+    const _Float16 h = (_Float16)s;
+    return half2_t{h, h};
 }
 
-// Dequantise 32 FP4 channels (16 code bytes) with two E4M3 group scales.
-__device__ __forceinline__ void fp4x32_to_f16(const uint4& codes, uint32_t sc0, uint32_t sc1,
-                                              _Float16 (&o)[32]) {
-    const uint32_t w[4] = {codes.x, codes.y, codes.z, codes.w};
-    const float s0 = e4m3_value_pos(sc0 & 0x7f) * ((sc0 & 0x80) ? -1.0f : 1.0f);
-    const float s1 = e4m3_value_pos(sc1 & 0x7f) * ((sc1 & 0x80) ? -1.0f : 1.0f);
+// 8 FP4 codes (one dword; channel 2j in the low nibble of byte j) -> 4 f16x2
+// words (channels 2j, 2j+1 in word j), times the group scale.
+__device__ __forceinline__ void fp4x8_to_f16x2(uint32_t w, half2_t scale, uint32_t* o) {
+    // high bytes of channels 0,2,4,6 and 1,3,5,7; sign bit = nibble bit 3
+    const uint32_t he = __builtin_amdgcn_perm(E2M1_HB_HI, E2M1_HB_LO, w & 0x07070707u) |
+                        ((w << 4) & 0x80808080u);
+    const uint32_t ho = __builtin_amdgcn_perm(E2M1_HB_HI, E2M1_HB_LO, (w >> 4) & 0x07070707u) |
+                        (w & 0x80808080u);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-        uint32_t nib = (w[i >> 3] >> (4 * (i & 7))) & 15u;
-        float v = (float)h_from_bits(e2m1_to_f16_bits(nib));
-        o[i] = (_Float16)(v * (i < 16 ? s0 : s1));
+    for (int j = 0; j < 4; ++j) {
+        // bytes: 0x00, even high byte j, 0x00, odd high byte j (selector 12 = 0x00)
+        const uint32_t sel = 0x0Cu | ((uint32_t)j << 8) | (0x0Cu << 16) | ((uint32_t)(4 + j) << 24);
+        const uint32_t x = __builtin_amdgcn_perm(ho, he, sel);
+        const half2_t v = __builtin_bit_cast(half2_t, x) * scale;
+        o[j] = __builtin_bit_cast(uint32_t, v);
     }
 }
 
@@ -118,7 +135,7 @@ __global__ void __launch_bounds__(AT_THREADS) attn_kernel(AttnArgs a) {
     {
         const int e = t >> 2, q4 = t & 3;
         bool ok = false;
-        _Float16 kh[32], vh[32];
+        uint32_t kw[16], vw[16];      // f16x2 words: channels 32*q4 + 2j, 2j+1
         if (is_main) {
             const int j = tile * TILE + e;
             const int32_t pos = (j < a.topk) ? a.idx[(int64_t)b * a.topk + j] : -1;
@@ -128,15 +145,20 @@ __global__ void __launch_bounds__(AT_THREADS) attn_kernel(AttnArgs a) {
                 const uint4 kc = *reinterpret_cast<const uint4*>(rec + 16 * q4);
                 const uint4 vc = *reinterpret_cast<const uint4*>(rec + 64 + 16 * q4);
                 const uint4 sc = *reinterpret_cast<const uint4*>(rec + 128);
-                const uint32_t scw[4] = {sc.x, sc.y, sc.z, sc.w};
-                // K scales are bytes 0..7 of sc, V scales bytes 8..15
-                const int kb = 2 * q4, vb = 8 + 2 * q4;
-                uint32_t ks0 = (scw[kb >> 2] >> (8 * (kb & 3))) & 0xff;
-                uint32_t ks1 = (scw[(kb + 1) >> 2] >> (8 * ((kb + 1) & 3))) & 0xff;
-                uint32_t vs0 = (scw[vb >> 2] >> (8 * (vb & 3))) & 0xff;
-                uint32_t vs1 = (scw[(vb + 1) >> 2] >> (8 * ((vb + 1) & 3))) & 0xff;
-                fp4x32_to_f16(kc, ks0, ks1, kh);
-                fp4x32_to_f16(vc, vs0, vs1, vh);
+                // K scales are bytes 0..7 of sc, V scales bytes 8..15; this
+                // thread's 32 channels are groups 2*q4 and 2*q4 + 1
+                const uint32_t ks = (q4 < 2 ? sc.x : sc.y) >> (16 * (q4 & 1));
+                const uint32_t vs = (q4 < 2 ? sc.z : sc.w) >> (16 * (q4 & 1));
+                const half2_t k0 = scale_h2(ks & 0xff), k1 = scale_h2((ks >> 8) & 0xff);
+                const half2_t v0 = scale_h2(vs & 0xff), v1 = scale_h2((vs >> 8) & 0xff);
+                fp4x8_to_f16x2(kc.x, k0, kw + 0);
+                fp4x8_to_f16x2(kc.y, k0, kw + 4);
+                fp4x8_to_f16x2(kc.z, k1, kw + 8);
+                fp4x8_to_f16x2(kc.w, k1, kw + 12);
+                fp4x8_to_f16x2(vc.x, v0, vw + 0);
+                fp4x8_to_f16x2(vc.y, v0, vw + 4);
+                fp4x8_to_f16x2(vc.z, v1, vw + 8);
+                fp4x8_to_f16x2(vc.w, v1, vw + 12);
             }
         } else {
             const int64_t u0 = N > WINDOW ? N - WINDOW : 0;
@@ -148,31 +170,32 @@ __global__ void __launch_bounds__(AT_THREADS) attn_kernel(AttnArgs a) {
                 const uint4* kp = reinterpret_cast<const uint4*>(a.wk + slot);
                 const uint4* vp = reinterpret_cast<const uint4*>(a.wv + slot);
                 const uint4 k0 = kp[0], k1 = kp[1], v0 = vp[0], v1 = vp[1];
-                const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-                const uint32_t vw[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+                const uint32_t kr[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+                const uint32_t vr[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    float2 a0 = e4m3x2_to_f32<false>(kw[i]), a1 = e4m3x2_to_f32<true>(kw[i]);
-                    float2 b0 = e4m3x2_to_f32<false>(vw[i]), b1 = e4m3x2_to_f32<true>(vw[i]);
-                    kh[4 * i] = (_Float16)a0.x;
-                    kh[4 * i + 1] = (_Float16)a0.y;
-                    kh[4 * i + 2] = (_Float16)a1.x;
-                    kh[4 * i + 3] = (_Float16)a1.y;
-                    vh[4 * i] = (_Float16)b0.x;
-                    vh[4 * i + 1] = (_Float16)b0.y;
-                    vh[4 * i + 2] = (_Float16)b1.x;
-                    vh[4 * i + 3] = (_Float16)b1.y;
+                    const float2 a0 = e4m3x2_to_f32<false>(kr[i]), a1 = e4m3x2_to_f32<true>(kr[i]);
+                    const float2 b0 = e4m3x2_to_f32<false>(vr[i]), b1 = e4m3x2_to_f32<true>(vr[i]);
+                    kw[2 * i] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)a0.x, (_Float16)a0.y});
+                    kw[2 * i + 1] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)a1.x, (_Float16)a1.y});
+                    vw[2 * i] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)b0.x, (_Float16)b0.y});
+                    vw[2 * i + 1] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)b1.x, (_Float16)b1.y});
                 }
             }
         }
         if (!ok) {
 #pragma unroll
-            for (int i = 0; i < 32; ++i) kh[i] = vh[i] = (_Float16)0.0f;
+            for (int i = 0; i < 16; ++i) kw[i] = vw[i] = 0u;
         }
+        uint4* krow = reinterpret_cast<uint4*>(&sh.K[e * KROW + 32 * q4]);
 #pragma unroll
-        for (int i = 0; i < 32; ++i) {
-            sh.K[e * KROW + 32 * q4 + i] = kh[i];
-            sh.Vt[(32 * q4 + i) * VROW + e] = vh[i];
+        for (int i = 0; i < 4; ++i)
+            krow[i] = make_uint4(kw[4 * i], kw[4 * i + 1], kw[4 * i + 2], kw[4 * i + 3]);
+        unsigned short* vt = reinterpret_cast<unsigned short*>(sh.Vt);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            vt[(32 * q4 + 2 * i) * VROW + e] = (unsigned short)(vw[i] & 0xffffu);
+            vt[(32 * q4 + 2 * i + 1) * VROW + e] = (unsigned short)(vw[i] >> 16);
         }
         if (q4 == 0) sh.valid[e] = ok;
     }

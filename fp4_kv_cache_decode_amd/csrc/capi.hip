@@ -80,13 +80,14 @@ csa2_status check_select(int32_t B, int32_t n_blocks, int32_t block, int32_t top
 
 csa2_status launched(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_LAUNCH; }
 
-// Keys per scoring workgroup: about 2048 workgroups in total (several per CU on
-// 256 CUs), each a multiple of 256 keys (4 waves x 64), at most 4096.
+// Keys per scoring workgroup: enough workgroups for one full wave of the chip
+// (256 CUs x 4 resident workgroups = 1024), so each workgroup runs many steps
+// and pays its cold start once; a multiple of 256 keys (4 waves x 64), 256..16384.
 int32_t keys_per_wg(int32_t B, int64_t max_ctx) {
     const int64_t total = (int64_t)B * max_ctx;
-    int64_t kpw = (total + 2047) / 2048;
+    int64_t kpw = (total + 1023) / 1024;
     kpw = (kpw + 255) / 256 * 256;
-    return (int32_t)(kpw < 256 ? 256 : (kpw > 4096 ? 4096 : kpw));
+    return (int32_t)(kpw < 256 ? 256 : (kpw > 16384 ? 16384 : kpw));
 }
 
 }  // namespace

@@ -61,9 +61,10 @@ __device__ __forceinline__ void load_key(Raw& r, const uint8_t* keys, int64_t t,
     r.d[3] = p[3];
 }
 
-// Score of one key (64 E4M3 codes) against the workgroup's query.
+// Score of one key (64 E4M3 codes) against the workgroup's query; wh already
+// carries the key scale (w_h * max(0, s*d) = (w_h * s) * max(0, d) for s > 0).
 __device__ __forceinline__ float key_score(const Raw& r, const float* __restrict__ q,
-                                           const float (&wh)[4], float scale) {
+                                           const float (&wh)[4]) {
     float kf[64];
     const uint32_t dw[16] = {r.d[0].x, r.d[0].y, r.d[0].z, r.d[0].w, r.d[1].x, r.d[1].y,
                              r.d[1].z, r.d[1].w, r.d[2].x, r.d[2].y, r.d[2].z, r.d[2].w,
@@ -87,7 +88,7 @@ __device__ __forceinline__ float key_score(const Raw& r, const float* __restrict
             a0 = fmaf(qh[d], kf[d], a0);
             a1 = fmaf(qh[d + 1], kf[d + 1], a1);
         }
-        s = fmaf(wh[h], fmaxf((a0 + a1) * scale, 0.0f), s);
+        s = fmaf(wh[h], fmaxf(a0 + a1, 0.0f), s);
     }
     return s + 0.0f;
 }
@@ -116,7 +117,7 @@ score_kernel(ScoreArgs a, const float* __restrict__ q_all, const uint8_t* __rest
     const float* q = q_all + (int64_t)b * IDX_HEADS * IDX_DIM;
     float wh[4];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) wh[h] = a.w[(int64_t)b * IDX_HEADS + h];
+    for (int h = 0; h < 4; ++h) wh[h] = a.w[(int64_t)b * IDX_HEADS + h] * a.scale;
     float* out = out_all + (int64_t)b * a.out_stride;
     const int32_t* pool = POOL ? a.pool + (int64_t)b * a.n_blocks : nullptr;
 
@@ -131,7 +132,7 @@ score_kernel(ScoreArgs a, const float* __restrict__ q_all, const uint8_t* __rest
         return i < N;
     };
     auto finish = [&](const Raw& r, int64_t k0, bool ok) {
-        float sc = key_score(r, q + zero * k0, wh, a.scale);
+        float sc = key_score(r, q + zero * k0, wh);
         sc = ok ? sc : NEG_INF;
         const int64_t item = k0 + lane;
         if (POOL) {
@@ -146,7 +147,9 @@ score_kernel(ScoreArgs a, const float* __restrict__ q_all, const uint8_t* __rest
         }
     };
 
-    // ping-pong: the loads of the next step are in flight during this step
+    // ping-pong key buffers: the next step's loads are issued first and pinned
+    // there (the scheduler may not sink them into the arithmetic), so they are
+    // in flight for a whole step of FMAs
     const int64_t stride = (int64_t)STEP * WAVES;
     int64_t k0 = wg0 + (int64_t)wave * STEP;
     Raw A, B;
@@ -157,11 +160,13 @@ score_kernel(ScoreArgs a, const float* __restrict__ q_all, const uint8_t* __rest
         const int64_t k1 = k0 + stride;
         const bool okB = k1 < wg_end && locate(k1 + lane, tB);
         load_key(B, keys, tB, okB);
+        __builtin_amdgcn_sched_barrier(0);
         finish(A, k0, okA);
         if (k1 >= wg_end) break;
         const int64_t k2 = k1 + stride;
         okA = k2 < wg_end && locate(k2 + lane, tA);
         load_key(A, keys, tA, okA);
+        __builtin_amdgcn_sched_barrier(0);
         finish(B, k1, okB);
     }
 }

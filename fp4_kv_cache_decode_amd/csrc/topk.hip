@@ -14,9 +14,10 @@
 //      even when every value shares one exponent) and the bin d holding the
 //      k-th largest value;
 //   3. values in bins above d are chosen; bin d's values go to an LDS candidate
-//      list, where an 11/11/10-bit radix on the exact order keys finds the
-//      threshold key T and how many keys equal to T to take; an ordered
-//      popcount scan over an "equal" bitmap keeps the lowest-index ones.
+//      list.  Up to 256 candidates are ranked directly in (value desc, index
+//      asc) order; larger lists take an 11/11/10-bit radix on the exact order
+//      keys for the threshold key T and how many keys equal to T to take, and an
+//      ordered popcount scan over an "equal" bitmap keeps the lowest-index ones.
 // The choice lives in an LDS bitmap over indices; an ordered popcount scan of
 // the bitmap writes ascending indices.
 //
@@ -44,6 +45,7 @@ constexpr int SEG = SEG_T * VPT;         // 4,096
 constexpr int FAST_MAX_N = 131072;
 constexpr int BM_WORDS = FAST_MAX_N / 32;
 constexpr int CAND_CAP = 4096;
+constexpr int RANK_MAX = 256;            // candidate sets ranked directly
 constexpr int UNROLL = 8;
 constexpr uint32_t KEY_ABSENT = 0x007fffffu;   // order_key(-inf)
 constexpr float NEG_INF = -__builtin_huge_valf();
@@ -120,25 +122,33 @@ __device__ uint32_t block_incl_scan(uint32_t v, Shared<NT>& sh, uint32_t* total)
     return v + before;
 }
 
+// Block-wide count, min and max in one LDS round.
 template <int NT>
-__device__ void block_minmax(float lo, float hi, Shared<NT>& sh, float* mn, float* mx) {
+__device__ void block_stats(uint32_t cnt, float lo, float hi, Shared<NT>& sh, uint32_t* total,
+                            float* mn, float* mx) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     lo = wave_min(lo);
     hi = wave_max(hi);
+#pragma unroll
+    for (int d = 32; d > 0; d >>= 1) cnt += __shfl_xor(cnt, d);
     if (lane == 0) {
         sh.wave_f[0][wave] = lo;
         sh.wave_f[1][wave] = hi;
+        sh.wave_u[wave] = cnt;
     }
     __syncthreads();
     float a = sh.wave_f[0][0], c = sh.wave_f[1][0];
+    uint32_t n = sh.wave_u[0];
 #pragma unroll
     for (int i = 1; i < NT / 64; ++i) {
         a = fminf(a, sh.wave_f[0][i]);
         c = fmaxf(c, sh.wave_f[1][i]);
+        n += sh.wave_u[i];
     }
     __syncthreads();
     *mn = a;
     *mx = c;
+    *total = n;
 }
 
 // Digit d of hist[0..nbins) with count(> d) < kk <= count(>= d); returns d and
@@ -195,9 +205,8 @@ __device__ bool select_core(Shared<NT>& sh, const float (&v)[VPT], const uint32_
         hi = ok ? fmaxf(hi, v[j]) : hi;
     }
     uint32_t n_valid;
-    block_incl_scan<NT>(cnt, sh, &n_valid);
     float vmin, vmax;
-    block_minmax<NT>(lo, hi, sh, &vmin, &vmax);
+    block_stats<NT>(cnt, lo, hi, sh, &n_valid, &vmin, &vmax);
     if (t == 0) sh.misc[4] = n_valid;
     if (n_valid <= k) {
 #pragma unroll
@@ -238,6 +247,21 @@ __device__ bool select_core(Shared<NT>& sh, const float (&v)[VPT], const uint32_
     __syncthreads();
     const uint32_t m = sh.misc[2];
     if (m > (uint32_t)CAND_CAP) return false;
+    if (m <= (uint32_t)RANK_MAX) {
+        // few candidates: rank each against all others in (key desc, index asc)
+        // order and keep the kk best; the LDS reads are broadcasts
+        for (uint32_t j = t; j < m; j += NT) {
+            const uint32_t kj = sh.ckey[j], ij = sh.cidx[j];
+            uint32_t rank = 0;
+            for (uint32_t i = 0; i < m; ++i) {
+                const uint32_t ki = sh.ckey[i], ii = sh.cidx[i];
+                rank += (ki > kj || (ki == kj && ii < ij)) ? 1u : 0u;
+            }
+            if (rank < kk) atomicOr(&sh.sel_bits[ij >> 5], 1u << (ij & 31));
+        }
+        __syncthreads();
+        return true;
+    }
     // exact threshold among the candidates: 11/11/10-bit radix on their keys
     uint32_t prefix = 0, pmask = 0;
     for (int pass = 0; pass < 3; ++pass) {

@@ -359,3 +359,28 @@ def test_index_full_equals_its_stages(K):
         sc = oc.scores(b, q[b], w[b], int(ctx[b]))
         want = block_scores(sc, int(ctx[b]))
         np.testing.assert_allclose(Mh[b, :len(want)], want, rtol=2e-6, atol=1e-6)
+
+
+def test_attention_workspace_reuse_across_shapes(K):
+    """One zeroed attention workspace serves calls of different B and topk in a
+    row: each call leaves the arrival counters at zero for the next."""
+    _say("attention workspace reuse")
+    N, L = 3000, 2
+    oc = O.Cache(3, N, L)
+    gc = K.Cache(3, N, L)
+    fill_both(17, 3, N, L, oc, gc)
+    ws = K.alloc_workspace(K.OP_DECODE_ATTN, 3, topk=1024)
+    qi, wi = G.index_queries(17, 0, 3)
+    seq = np.arange(3, dtype=np.int32)
+    ctx = np.array([N, N - 100, 700], np.int64)
+    _, idx512, _, _ = oc.index_full(qi, wi, seq, ctx)
+    for B, topk, layer in [(3, 512, 0), (1, 512, 1), (2, 200, 0), (3, 1024, 1), (3, 512, 1)]:
+        idx = np.full((B, topk), -1, np.int32)
+        m = min(topk, 512)
+        idx[:, :m] = idx512[:B, :m]
+        q = G.attn_queries(17, layer + 10 * B, B)
+        out = torch.empty((B, 16, 128), dtype=torch.float32, device="cuda")
+        K.decode_attn(gc, layer, dev(q), dev(idx), dev(seq[:B]), dev(ctx[:B]), out, ws)
+        torch.cuda.synchronize()
+        want = oc.decode_attn(layer, q, idx, seq[:B], ctx[:B])
+        assert np.max(np.abs(out.cpu().numpy() - want)) <= 1e-4, (B, topk, layer)
