@@ -67,6 +67,7 @@ struct AttnShared {
     _Float16 Phi[HEADS * PROW];
     _Float16 Plo[HEADS * PROW];
     float red[4][HEADS];
+    float lsum[4][HEADS];
     int valid[TILE];
 };
 
@@ -253,14 +254,13 @@ __global__ void __launch_bounds__(AT_THREADS) attn_kernel(AttnArgs a) {
         sh.Phi[h * PROW + ent] = ph;
         sh.Plo[h * PROW + ent] = (_Float16)(p[r] - (float)ph);
     }
-    __syncthreads();   // P written; red[] reads done
     if ((lane & 15) == 0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sh.red[wave][4 * (lane >> 4) + r] = lsum[r];
+        for (int r = 0; r < 4; ++r) sh.lsum[wave][4 * (lane >> 4) + r] = lsum[r];
     }
-    __syncthreads();
+    __syncthreads();   // P and the per-wave sums written
     if (t < HEADS) {
-        part[HEADS + t] = sh.red[0][t] + sh.red[1][t] + sh.red[2][t] + sh.red[3][t];
+        part[HEADS + t] = sh.lsum[0][t] + sh.lsum[1][t] + sh.lsum[2][t] + sh.lsum[3][t];
     }
 
     // ---- O = P V for dims 32*wave .. +31 (two 16-dim tiles)
@@ -298,47 +298,55 @@ __global__ void __launch_bounds__(AT_THREADS) attn_kernel(AttnArgs a) {
 }
 
 // Combine the tiles of each query: out = sum_t e^(m_t - M) o_t / sum_t e^(m_t - M) l_t.
-// The tiles' (m, l) pairs are staged in LDS first; each thread then owns 8
-// output dims of one head and streams the tiles' partial outputs with several
-// loads in flight.
-constexpr int MAX_TILES = CSA2_MAX_TOPK / TILE + 2;
+// Each thread owns 8 output dims of one head; it loads the partials of up to
+// MERGE_BATCH tiles at once (one memory round trip for the default 10 tiles).
+constexpr int MERGE_BATCH = 12;     // tiles whose loads are in flight together
 
 __global__ void __launch_bounds__(AT_THREADS) attn_merge_kernel(const float* part, int32_t n_tiles,
                                                                  float* out) {
-    __shared__ float s_m[MAX_TILES][HEADS];
-    __shared__ float s_l[MAX_TILES][HEADS];
     const int b = blockIdx.x;
     const int t = threadIdx.x;
-    const float* pb = part + (int64_t)b * n_tiles * ATTN_PART_FLOATS;
-    for (int i = t; i < n_tiles * HEADS; i += AT_THREADS) {
-        const int tile = i / HEADS, h = i % HEADS;
-        s_m[tile][h] = pb[tile * ATTN_PART_FLOATS + h];
-        s_l[tile][h] = pb[tile * ATTN_PART_FLOATS + HEADS + h];
-    }
-    __syncthreads();
     const int h = t >> 4;                 // 16 threads per head
     const int d0 = (t & 15) * 8;          // 8 dims each
-    float M = NEG_INF;
-    for (int i = 0; i < n_tiles; ++i) M = fmaxf(M, s_m[i][h]);
-    float L = 0.0f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    if (M != NEG_INF) {
-#pragma unroll 4
-        for (int i = 0; i < n_tiles; ++i) {
-            const float mt = s_m[i][h];
-            const float wgt = mt == NEG_INF ? 0.0f : expf(mt - M);
-            L += wgt * s_l[i][h];
-            const float4* o =
-                reinterpret_cast<const float4*>(pb + i * ATTN_PART_FLOATS + 2 * HEADS + h * D + d0);
-            const float4 o0 = o[0], o1 = o[1];
-            acc[0] += wgt * o0.x;
-            acc[1] += wgt * o0.y;
-            acc[2] += wgt * o0.z;
-            acc[3] += wgt * o0.w;
-            acc[4] += wgt * o1.x;
-            acc[5] += wgt * o1.y;
-            acc[6] += wgt * o1.z;
-            acc[7] += wgt * o1.w;
+    const float* pb = part + (int64_t)b * n_tiles * ATTN_PART_FLOATS;
+    float M = NEG_INF, L = 0.0f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    // groups of MERGE_BATCH tiles: every load of a group is issued before use,
+    // and M / L / acc are rescaled online when a group raises the max
+    for (int i0 = 0; i0 < n_tiles; i0 += MERGE_BATCH) {
+        float m[MERGE_BATCH], l[MERGE_BATCH];
+        float4 o[MERGE_BATCH][2];
+#pragma unroll
+        for (int u = 0; u < MERGE_BATCH; ++u) {
+            const int i = i0 + u < n_tiles ? i0 + u : n_tiles - 1;
+            const float* pt = pb + (int64_t)i * ATTN_PART_FLOATS;
+            m[u] = i0 + u < n_tiles ? pt[h] : NEG_INF;
+            l[u] = pt[HEADS + h];
+            const float4* po = reinterpret_cast<const float4*>(pt + 2 * HEADS + h * D + d0);
+            o[u][0] = po[0];
+            o[u][1] = po[1];
         }
+        float Mn = M;
+#pragma unroll
+        for (int u = 0; u < MERGE_BATCH; ++u) Mn = fmaxf(Mn, m[u]);
+        if (Mn == NEG_INF) continue;
+        const float c = M == NEG_INF ? 0.0f : expf(M - Mn);
+        L *= c;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] *= c;
+#pragma unroll
+        for (int u = 0; u < MERGE_BATCH; ++u) {
+            const float wgt = m[u] == NEG_INF ? 0.0f : expf(m[u] - Mn);
+            L += wgt * l[u];
+            acc[0] += wgt * o[u][0].x;
+            acc[1] += wgt * o[u][0].y;
+            acc[2] += wgt * o[u][0].z;
+            acc[3] += wgt * o[u][0].w;
+            acc[4] += wgt * o[u][1].x;
+            acc[5] += wgt * o[u][1].y;
+            acc[6] += wgt * o[u][1].z;
+            acc[7] += wgt * o[u][1].w;
+        }
+        M = Mn;
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     float4* o = reinterpret_cast<float4*>(out + ((int64_t)b * HEADS + h) * D + d0);
