@@ -80,16 +80,6 @@ csa2_status check_select(int32_t B, int32_t n_blocks, int32_t block, int32_t top
 
 csa2_status launched(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_LAUNCH; }
 
-// Keys per scoring workgroup: enough workgroups for one full wave of the chip
-// (256 CUs x 4 resident workgroups = 1024), so each workgroup runs many steps
-// and pays its cold start once; a multiple of 256 keys (4 waves x 64), 256..16384.
-int32_t keys_per_wg(int32_t B, int64_t max_ctx) {
-    const int64_t total = (int64_t)B * max_ctx;
-    int64_t kpw = (total + 1023) / 1024;
-    kpw = (kpw + 255) / 256 * 256;
-    return (int32_t)(kpw < 256 ? 256 : (kpw > 16384 ? 16384 : kpw));
-}
-
 }  // namespace
 
 extern "C" {
@@ -165,7 +155,7 @@ csa2_status csa2_index_full(const csa2_cache* cache, const float* q_idx, const f
     void* sel = base + L.sel_off;
 
     hipError_t e = csa2::launch_score_blocks(*cache, q_idx, w, seq, ctx, B, max_ctx,
-                                             m_stride(max_ctx), M, keys_per_wg(B, max_ctx),
+                                             m_stride(max_ctx), M,
                                              stream);
     if (e != hipSuccess) return CSA2_ERR_LAUNCH;
     e = csa2::launch_topk(M, m_stride(max_ctx), ctx, max_ctx, 0, nullptr, 0, B, n_blocks,
@@ -190,7 +180,7 @@ csa2_status csa2_index_block_scores(const csa2_cache* cache, const float* q_idx,
     if (m_stride_ < (max_ctx + BLOCK - 1) / BLOCK) return CSA2_ERR_INVALID_ARG;
     if (B == 0 || max_ctx == 0) return CSA2_OK;
     return launched(csa2::launch_score_blocks(*cache, q_idx, w, seq, ctx, B, max_ctx, m_stride_,
-                                              M, keys_per_wg(B, max_ctx), stream));
+                                              M, stream));
 }
 
 csa2_status csa2_index_select_pool(const float* M, int64_t m_stride_, const int64_t* ctx,

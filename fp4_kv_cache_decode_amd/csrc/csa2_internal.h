@@ -16,11 +16,10 @@ hipError_t launch_quantize(const csa2_cache& c, const csa2_window* w, const floa
                            int64_t n, hipStream_t stream);
 
 // Full-context scoring: block maxima M[b][j] for blocks j < ceil(ctx[b]/8).
-// keys_per_wg is a multiple of 256.
 hipError_t launch_score_blocks(const csa2_cache& c, const float* q_idx, const float* w,
                                const int32_t* seq, const int64_t* ctx, int32_t B,
                                int64_t max_ctx, int64_t m_stride, float* M,
-                               int32_t keys_per_wg, hipStream_t stream);
+                               hipStream_t stream);
 
 // Pool scoring: S[b][i] = score of position pool[b][i/8]*8 + i%8, or -inf when
 // the pool slot is -1 or the position is >= ctx[b].

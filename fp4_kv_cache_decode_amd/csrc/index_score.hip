@@ -78,6 +78,7 @@ __device__ __forceinline__ float key_score(const Raw& r, const float* __restrict
         kf[4 * i + 2] = hi.x;
         kf[4 * i + 3] = hi.y;
     }
+    // two accumulator chains per head (a single 64-long chain measured slower)
     float s = 0.0f;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
@@ -153,7 +154,7 @@ score_kernel(ScoreArgs a, const float* __restrict__ q_all, const uint8_t* __rest
     const int64_t stride = (int64_t)STEP * WAVES;
     int64_t k0 = wg0 + (int64_t)wave * STEP;
     Raw A, B;
-    int64_t tA, tB;
+    int64_t tA = 0, tB = 0;
     bool okA = k0 < wg_end && locate(k0 + lane, tA);
     load_key(A, keys, tA, okA);
     for (; k0 < wg_end; k0 += 2 * stride) {
@@ -171,12 +172,196 @@ score_kernel(ScoreArgs a, const float* __restrict__ q_all, const uint8_t* __rest
     }
 }
 
+// ---------------------------------------------------------------------------
+// Full-context scan with an LDS staging ring.
+//
+// Each wave streams its own 64-key (4 KB) steps into a private ring of
+// SCAN_STAGES LDS slots with global_load_lds_dwordx4: one instruction moves a
+// contiguous 1 KB of keys (lane l's 16 bytes land at slot + 16 l), so every
+// load is fully coalesced and no VGPR holds data in flight.  The wave then
+// reads its own key (64 bytes) from LDS and scores it as above.
+// SCAN_STAGES - 1 steps are in flight while one is scored.
+//
+// Bank-conflict-free reads: a key occupies 64 bytes of LDS, and 16 lanes
+// reading the same 16-byte chunk of 16 consecutive keys would hit only four
+// distinct 16-byte bank groups.  The 16-byte chunks of key j (j mod 16) are
+// therefore stored rotated by chunk_rot(j): chunk m sits at position
+// (m + chunk_rot(j)) mod 4 of the key's 64 bytes.  The rotation is applied on
+// the load side (each lane fetches the chunk that belongs at its LDS position,
+// the same contiguous 1 KB per instruction) and undone by per-lane read
+// addresses, so register m still holds channels 16m..16m+15 for every lane.
+// chunk_rot is a permutation within every group of 4 keys with equal j mod 4
+// (16-lane passes over 64 banks) and within every group of 4 keys of equal
+// parity in an aligned run of 8 (8-lane passes over 32 banks).
+//
+// The loads are written as inline asm so that the compiler neither reorders
+// them nor inserts a full vmcnt(0) drain before every LDS read; the waits are
+// explicit: with j steps issued after step i, "s_waitcnt vmcnt(4 j)" leaves
+// only the later steps' loads outstanding (loads complete in order; the block
+// maxima stores in between only make the wait stricter).  The asm statements
+// carry a memory clobber, which keeps the LDS reads of a step after its wait
+// and before the next refill of the same slot.
+constexpr int SCAN_STAGES = 3;
+constexpr int SCAN_STEP_BYTES = STEP * IDX_DIM;   // 4096
+
+__device__ __forceinline__ int chunk_rot(int j) { return ((j >> 1) ^ (j >> 3)) & 3; }
+
+// m0 is named as clobbered: it carries the LDS address of the copy, and no
+// other code of these kernels keeps a value in m0.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma_1k(uint32_t voff, const uint8_t* sbase, uint32_t lds_addr) {
+    asm volatile(
+        "s_mov_b32 m0, %2\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %0, %1"
+        :
+        : "v"(voff), "s"(sbase), "s"(lds_addr)
+        : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// One workgroup per CU: 12 waves (3 per SIMD), each with a private LDS ring.
+// The workgroup's 64-key steps are handed out by an LDS counter, so a wave
+// that the SIMD's issue order favours simply takes more steps and all waves
+// of the CU finish within one step of each other (with a static split, the
+// oldest wave on a SIMD finishes first and the last one runs alone, with its
+// memory latency exposed).
+constexpr int SCAN_WAVES = 12;
+constexpr int SCAN_THREADS = SCAN_WAVES * 64;
+
+__global__ void __launch_bounds__(SCAN_THREADS)
+scan_kernel(ScoreArgs a, const float* __restrict__ q_all, const uint8_t* __restrict__ idxk,
+            float* __restrict__ out_all, int64_t zero) {
+    __shared__ __attribute__((aligned(16))) uint8_t ring[SCAN_WAVES][SCAN_STAGES][SCAN_STEP_BYTES];
+    __shared__ int next_step;
+    const int b = blockIdx.y;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int64_t N = clamp64(a.ctx[b], 0, a.max_ctx);
+    const int32_t s = a.seq[b];
+    if (s < 0 || s >= a.n_seq) return;
+    const int64_t wg0 = (int64_t)blockIdx.x * a.keys_per_wg;
+    if (wg0 >= N) return;
+    const int64_t wg_end = wg0 + a.keys_per_wg < N ? wg0 + a.keys_per_wg : N;
+    const int n_steps = (int)((wg_end - wg0 + STEP - 1) / STEP);
+    if (threadIdx.x == 0) next_step = 0;
+    __syncthreads();
+
+    const uint8_t* keys = idxk + (int64_t)s * a.cap * IDX_DIM;
+    const float* q = q_all + (int64_t)b * IDX_HEADS * IDX_DIM;
+    float wh[4];
+#pragma unroll
+    for (int h = 0; h < 4; ++h) wh[h] = a.w[(int64_t)b * IDX_HEADS + h] * a.scale;
+    float* out = out_all + (int64_t)b * a.out_stride;
+
+    uint8_t* const my_ring = &ring[wave][0][0];
+    const uint32_t lds0 = (uint32_t)(uintptr_t)my_ring;
+
+    // load side: lane l fills position l & 3 of key l >> 2 of each 1 KB group
+    const int kl = lane >> 2;
+    const int chunk_here = ((lane & 3) - chunk_rot(kl)) & 3;
+    const uint32_t dma_off = (uint32_t)(64 * kl + 16 * chunk_here);
+    // read side: channels 16m..16m+15 of this lane's key
+    const uint8_t* rd[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        rd[m] = my_ring + 64 * lane + 16 * ((m + chunk_rot(lane & 15)) & 3);
+
+    // next step of the workgroup for this wave, or -1 when none is left
+    auto grab = [&]() -> int {
+        int t = 0;
+        if (lane == 0) t = atomicAdd(&next_step, 1);
+        t = __builtin_amdgcn_readfirstlane(t);
+        return t < n_steps ? t : -1;
+    };
+    // issue step t into `slot`; a step that reaches past N loads key N - 1 in
+    // place of the missing keys (in bounds; their scores are masked)
+    auto issue = [&](int t, int slot) {
+        const int64_t kb = wg0 + (int64_t)t * STEP;
+        const uint8_t* g = keys + kb * IDX_DIM;
+        const uint32_t l = lds0 + (uint32_t)(slot * SCAN_STEP_BYTES);
+        if (kb + STEP <= N) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) dma_1k(dma_off, g + 1024 * c, l + 1024 * c);
+        } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+                int64_t j = kb + 16 * c + kl;
+                j = j < N ? j : N - 1;
+                dma_1k((uint32_t)((j - kb) * IDX_DIM + 16 * chunk_here), g, l + 1024 * c);
+            }
+        }
+    };
+
+    // sid[slot]: the step held in that slot (-1: none).  Steps are taken in
+    // increasing order, so once a grab fails every later one fails too.
+    int sid[SCAN_STAGES];
+#pragma unroll
+    for (int i = 0; i < SCAN_STAGES - 1; ++i) {
+        sid[i] = i == 0 || sid[i - 1] >= 0 ? grab() : -1;
+        if (sid[i] >= 0) issue(sid[i], i);
+    }
+    sid[SCAN_STAGES - 1] = -1;
+
+    // score the step held in `slot` after topping up the ring; false when done
+    auto step = [&](const int slot) -> bool {
+        const int t = sid[slot];
+        if (t < 0) return false;
+        const int ns = (slot + SCAN_STAGES - 1) % SCAN_STAGES;
+        sid[ns] = sid[(slot + SCAN_STAGES - 2) % SCAN_STAGES] >= 0 ? grab() : -1;
+        if (sid[ns] >= 0) issue(sid[ns], ns);
+        // steps issued after t: the valid ones among the next SCAN_STAGES - 1 slots
+        int after = 0;
+#pragma unroll
+        for (int d = 1; d < SCAN_STAGES; ++d) after += sid[(slot + d) % SCAN_STAGES] >= 0;
+        if (after >= SCAN_STAGES - 1) wait_vm<4 * (SCAN_STAGES - 1)>();
+        else if (SCAN_STAGES > 2 && after == 1) wait_vm<4>();
+        else wait_vm<0>();
+        const int64_t k0 = wg0 + (int64_t)t * STEP;
+        Raw r;
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+            r.d[m] = *reinterpret_cast<const uint4*>(rd[m] + slot * SCAN_STEP_BYTES);
+        float sc = key_score(r, q + zero * k0, wh);
+        const bool whole = k0 + STEP <= N;    // uniform
+        if (!whole) sc = k0 + lane < N ? sc : NEG_INF;
+        float mx = fmaxf(sc, dpp_f32<DPP_XOR1>(sc));
+        mx = fmaxf(mx, dpp_f32<DPP_XOR2>(mx));
+        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(mx), 0x101f)));
+        // lanes 8m..8m+7 hold block k0/8 + m; a block is visible iff its first key is
+        float* ob = out + (k0 >> 3);
+        if ((lane & 7) == 0 && (whole || k0 + lane < N)) ob[lane >> 3] = mx;
+        return true;
+    };
+    static_assert(SCAN_STAGES == 3, "the slot rotation below is written out for 3 slots");
+    while (step(0) && step(1) && step(2)) {
+    }
+}
+
 }  // namespace
+
+// Keys per scan workgroup: one workgroup per CU (256 of them) across all
+// rows, each a multiple of one 64-key step.
+int32_t scan_keys_per_wg(int32_t B, int64_t max_ctx) {
+    const int64_t total = (int64_t)B * max_ctx;
+    int64_t kpw = (total + 255) / 256;
+    kpw = (kpw + STEP - 1) / STEP * STEP;
+    const int64_t row = (max_ctx + STEP - 1) / STEP * STEP;
+    if (kpw > row) kpw = row;
+    return (int32_t)(kpw < STEP ? STEP : (kpw > (1 << 30) ? (1 << 30) : kpw));
+}
 
 hipError_t launch_score_blocks(const csa2_cache& c, const float* q_idx, const float* w,
                                const int32_t* seq, const int64_t* ctx, int32_t B,
                                int64_t max_ctx, int64_t m_stride, float* M,
-                               int32_t keys_per_wg, hipStream_t stream) {
+                               hipStream_t stream) {
+    const int32_t keys_per_wg = scan_keys_per_wg(B, max_ctx);
     ScoreArgs a{};
     a.idxk = c.idxk;
     a.q_idx = q_idx;
@@ -192,8 +377,8 @@ hipError_t launch_score_blocks(const csa2_cache& c, const float* q_idx, const fl
     a.scale = c.idxk_scale;
     dim3 grid((unsigned)((max_ctx + keys_per_wg - 1) / keys_per_wg), (unsigned)B);
     if (grid.x == 0) return hipSuccess;
-    hipLaunchKernelGGL(score_kernel<false>, grid, dim3(SC_THREADS), 0, stream, a, q_idx, c.idxk,
-                       M, (int64_t)0);
+    hipLaunchKernelGGL(scan_kernel, grid, dim3(SCAN_THREADS), 0, stream, a, q_idx, c.idxk, M,
+                       (int64_t)0);
     return hipGetLastError();
 }
 
