@@ -28,29 +28,40 @@ def rows_for(seed, s, p0, p1, n_layers, N, wlo=None):
     return k, v, ik, (w0, w1, wk, wv)
 
 
-def fill_both(seed, n_seq, N, n_layers, ocache, gcache=None, chunk=1 << 18, wlo=None):
+def fill_both(seed, n_seq, N, n_layers, ocache, gcache=None, chunk=1 << 18, wlo=None,
+              workers=1):
     """Write positions [0,N) of every sequence into the oracle cache and (if
-    given) the device cache through csa2_quantize_kv."""
+    given) the device cache through csa2_quantize_kv.  With workers > 1 the
+    rows of up to `workers` chunks are generated in parallel threads."""
     import torch
     from fp4_kv_cache_decode_amd import csa2
     for s in range(n_seq):
-        for p0 in range(0, N, chunk):
-            p1 = min(N, p0 + chunk)
-            k, v, ik, (w0, w1, wk, wv) = rows_for(seed, s, p0, p1, n_layers, N, wlo)
-            seq = np.full(p1 - p0, s, np.int32)
-            pos = np.arange(p0, p1, dtype=np.int64)
-            if ocache is not None:
-                ocache.quantize(k, v, ik, None, None, seq, pos)
-                if wk is not None:
-                    ocache.quantize(k[w0 - p0:], v[w0 - p0:], None, wk, wv, seq[w0 - p0:],
-                                    pos[w0 - p0:])
-            if gcache is not None:
-                dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-                csa2.quantize_kv(gcache, dev(k), dev(v), dev(seq), dev(pos), idx_k=dev(ik))
-                if wk is not None:
-                    csa2.quantize_kv(gcache, dev(k[w0 - p0:]), dev(v[w0 - p0:]),
-                                     dev(seq[w0 - p0:]), dev(pos[w0 - p0:]), win_k=dev(wk),
-                                     win_v=dev(wv))
+        starts = list(range(0, N, chunk))
+        for g0 in range(0, len(starts), workers):
+            group = [(p0, min(N, p0 + chunk)) for p0 in starts[g0:g0 + workers]]
+            made = G.parallel_map(lambda pr: rows_for(seed, s, pr[0], pr[1], n_layers, N, wlo),
+                                  group, workers) if workers > 1 else \
+                [rows_for(seed, s, p0, p1, n_layers, N, wlo) for p0, p1 in group]
+            for (p0, p1), rows in zip(group, made):
+                _write_rows(s, p0, p1, rows, ocache, gcache, torch, csa2)
+
+
+def _write_rows(s, p0, p1, rows, ocache, gcache, torch, csa2):
+    k, v, ik, (w0, w1, wk, wv) = rows
+    seq = np.full(p1 - p0, s, np.int32)
+    pos = np.arange(p0, p1, dtype=np.int64)
+    if ocache is not None:
+        ocache.quantize(k, v, ik, None, None, seq, pos)
+        if wk is not None:
+            ocache.quantize(k[w0 - p0:], v[w0 - p0:], None, wk, wv, seq[w0 - p0:],
+                            pos[w0 - p0:])
+    if gcache is not None:
+        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+        csa2.quantize_kv(gcache, dev(k), dev(v), dev(seq), dev(pos), idx_k=dev(ik))
+        if wk is not None:
+            csa2.quantize_kv(gcache, dev(k[w0 - p0:]), dev(v[w0 - p0:]),
+                             dev(seq[w0 - p0:]), dev(pos[w0 - p0:]), win_k=dev(wk),
+                             win_v=dev(wv))
 
 
 def check_index_set(got, want, scores, kth, rel=REL_EXEMPT, exact=False):

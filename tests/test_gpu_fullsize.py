@@ -1,0 +1,180 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times.
+
+* decoder20_1m_b4: 4 sequences x 1,048,576 positions, the 20-layer pattern
+  [Full + 3 Reuse] + 4 x [Reindex + 3 Reuse].  Every output of the step is
+  checked: block maxima, pool, the Full and Reindex index sets, and all 20
+  layers' attention outputs.
+* prefill_8k_over_128k: 8,192 causal queries over a 131,072-position prefix
+  plus the chunk itself (seq = 0 for all, ctx_i = 131,073 + i).  The GPU runs all
+  8,192 queries in one call per stage; the oracle checks a strided sample.
+
+Stages are isolated as in the smaller parity tests: Reindex receives the
+oracle's pool and attention the oracle's index sets, so that an exempt near tie
+cannot cascade; the GPU-only chain is compared end to end where its index sets
+equal the oracle's.
+"""
+import sys
+import time
+
+import numpy as np
+import pytest
+
+import oracle as O
+from fp4_kv_cache_decode_amd import datagen as G
+from parity import ATTN_TOL, REL_EXEMPT, block_scores, check_index_set, fill_both
+
+pytestmark = [pytest.mark.gpu, pytest.mark.timeout(1200)]
+
+torch = pytest.importorskip("torch")
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def K():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from fp4_kv_cache_decode_amd import csa2
+    csa2.lib()
+    return csa2
+
+
+def dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _check_block_maxima(gM, sc, N):
+    """GPU block maxima against the oracle's fp64 scores (fp32 rounding only)."""
+    want = block_scores(sc, N)
+    got = gM[:want.size].astype(np.float64)
+    err = np.abs(got - want) / (np.abs(want) + 1.0)
+    assert float(err.max()) <= REL_EXEMPT, float(err.max())
+    return float(err.max())
+
+
+def test_decoder20_1m_b4_step(K):
+    wl = G.WORKLOADS["decoder20_1m_b4"]
+    B, N, L = wl.B, wl.N, len(wl.layers)
+    seed = 0
+    _say(f"decoder20_1m_b4: building caches B={B} N={N} L={L}")
+    t0 = time.time()
+    oc = O.Cache(wl.n_seq, wl.cap, L, wl.w_cap)
+    gc = K.Cache(wl.n_seq, wl.cap, L, wl.w_cap)
+    fill_both(seed, wl.n_seq, N, L, oc, gc, chunk=G.CHUNK, workers=16)
+    torch.cuda.synchronize()
+    _say(f"  caches built in {time.time() - t0:.1f}s")
+    # the stored bytes are identical (quantise-on-write parity at full size)
+    assert torch.equal(gc.idxk.cpu(), torch.from_numpy(oc.idxk))
+    assert torch.equal(gc.kv.cpu(), torch.from_numpy(oc.kv))
+    assert np.array_equal(gc.wk.cpu().numpy()[:, :, :], oc.wk) and \
+        np.array_equal(gc.wv.cpu().numpy(), oc.wv)
+
+    seq, ctx = wl.seq(), wl.ctx()
+    dseq, dctx = dev(seq), dev(ctx)
+    M = torch.empty((B, K.block_stride(N)), dtype=torch.float32, device="cuda")
+    gpool_t = torch.empty((B, G.N_BLOCKS), dtype=torch.int32, device="cuda")
+    gidx_t = torch.empty((B, G.TOPK), dtype=torch.int32, device="cuda")
+    out_t = torch.empty((B, G.H, G.D), dtype=torch.float32, device="cuda")
+    ws_ri = K.alloc_workspace(K.OP_INDEX_REINDEX, B)
+    ws_sel = K.alloc_workspace(K.OP_SELECT_POOL, B, N)
+    ws_at = K.alloc_workspace(K.OP_DECODE_ATTN, B)
+
+    opool = oidx = None
+    gpu_chain_equal = True
+    n_exempt = 0
+    for l, mode in enumerate(wl.layers):
+        if mode in "FI":
+            qi, wi = G.index_queries(seed, l, B)
+            scs = [oc.scores(int(seq[b]), qi[b], wi[b], int(ctx[b])) for b in range(B)]
+        if mode == "F":
+            # the benchmark's Full-layer chain: scan, pool select, pool top-k
+            K.index_block_scores(gc, dev(qi), dev(wi), dseq, dctx, N, M)
+            K.index_select_pool(M, dctx, N, gpool_t, ws_sel)
+            K.index_reindex(gc, dev(qi), dev(wi), dseq, dctx, gpool_t, gidx_t, ws_ri)
+            torch.cuda.synchronize()
+            opool, oidx, kb, kp = oc.index_full(qi, wi, seq, ctx)
+            gM, gpool, gidx = M.cpu().numpy(), gpool_t.cpu().numpy(), gidx_t.cpu().numpy()
+            for b in range(B):
+                e = _check_block_maxima(gM[b], scs[b], N)
+                Mb = block_scores(scs[b], N)
+                n_exempt += check_index_set(gpool[b], opool[b], lambda j: Mb[j], kb[b])
+                n_exempt += check_index_set(gidx[b], oidx[b], lambda t: scs[b][t], kp[b])
+            _say(f"  layer {l} Full: block maxima rel err {e:.2g}, exempt diffs {n_exempt}")
+            gpu_chain_equal &= np.array_equal(gidx, oidx)
+        elif mode == "I":
+            # Reindex on the oracle's pool (isolated) ...
+            K.index_reindex(gc, dev(qi), dev(wi), dseq, dctx, dev(opool), gidx_t, ws_ri)
+            torch.cuda.synchronize()
+            oidx, kp = oc.index_reindex(qi, wi, seq, ctx, opool)
+            gidx = gidx_t.cpu().numpy()
+            for b in range(B):
+                n_exempt += check_index_set(gidx[b], oidx[b], lambda t: scs[b][t], kp[b])
+            gpu_chain_equal &= np.array_equal(gidx, oidx)
+            _say(f"  layer {l} Reindex: exempt diffs so far {n_exempt}")
+        # attention of every layer on the group's (oracle) index set; Reuse
+        # layers pass the same idx again
+        q = G.attn_queries(seed, l, B)
+        K.decode_attn(gc, l, dev(q), dev(oidx), dseq, dctx, out_t, ws_at)
+        torch.cuda.synchronize()
+        want = oc.decode_attn(l, q, oidx, seq, ctx)
+        err = float(np.max(np.abs(out_t.cpu().numpy() - want)))
+        assert err <= ATTN_TOL, (l, err)
+        if mode != "R":
+            _say(f"  layer {l} attention max-abs err {err:.3g}")
+    _say(f"  GPU index sets equal the oracle's in every layer: {gpu_chain_equal}")
+
+
+def test_prefill_chunk_8k_over_128k(K):
+    wl = G.WORKLOADS["prefill_8k_over_128k"]
+    B, N0 = wl.B, wl.N                 # 8,192 queries after a 131,072-position prefix
+    cap = wl.cap                       # 139,264 positions written
+    seed = 0
+    _say(f"prefill_8k_over_128k: building cache cap={cap} w_cap={wl.w_cap}")
+    oc = O.Cache(1, cap, 1, wl.w_cap)
+    gc = K.Cache(1, cap, 1, wl.w_cap)
+    # window rows for every position a query's window can reach
+    fill_both(seed, 1, cap, 1, oc, gc, chunk=G.CHUNK, wlo=N0 - G.WINDOW, workers=16)
+    torch.cuda.synchronize()
+    assert torch.equal(gc.kv.cpu(), torch.from_numpy(oc.kv))
+    assert torch.equal(gc.idxk.cpu(), torch.from_numpy(oc.idxk))
+    assert np.array_equal(gc.wk.cpu().numpy(), oc.wk)
+
+    seq, ctx = wl.seq(), wl.ctx()
+    qi, wi = G.index_queries(seed, 0, B)
+    q = G.attn_queries(seed, 0, B)
+    pool_t = torch.empty((B, G.N_BLOCKS), dtype=torch.int32, device="cuda")
+    idx_t = torch.empty((B, G.TOPK), dtype=torch.int32, device="cuda")
+    ws = K.alloc_workspace(K.OP_INDEX_FULL, B, cap)
+    t0 = time.time()
+    K.index_full(gc, dev(qi), dev(wi), dev(seq), dev(ctx), cap, pool_t, idx_t, ws)
+    torch.cuda.synchronize()
+    _say(f"  GPU index_full over {B} queries: {time.time() - t0:.2f}s (incl. launch)")
+    gpool, gidx = pool_t.cpu().numpy(), idx_t.cpu().numpy()
+
+    sample = np.unique(np.r_[0, 1, 7, 127, 128, 1000, 4095, 4096, 6000, 8190, 8191,
+                             np.arange(257, B, 1031)])
+    opool, oidx, kb, kp = oc.index_full(qi[sample], wi[sample], seq[sample], ctx[sample])
+    n_exempt = 0
+    for j, b in enumerate(sample):
+        sc = oc.scores(0, qi[b], wi[b], int(ctx[b]))
+        Mb = block_scores(sc, int(ctx[b]))
+        n_exempt += check_index_set(gpool[b], opool[j], lambda t: Mb[t], kb[j])
+        n_exempt += check_index_set(gidx[b], oidx[j], lambda t: sc[t], kp[j])
+    _say(f"  {sample.size} sampled queries: pool and top-512 match, exempt diffs {n_exempt}")
+
+    # attention for all queries in one call; the sampled rows use the oracle's sets
+    idx_mixed = gidx.copy()
+    idx_mixed[sample] = oidx
+    out_t = torch.empty((B, G.H, G.D), dtype=torch.float32, device="cuda")
+    ws_at = K.alloc_workspace(K.OP_DECODE_ATTN, B)
+    K.decode_attn(gc, 0, dev(q), dev(idx_mixed), dev(seq), dev(ctx), out_t, ws_at)
+    torch.cuda.synchronize()
+    got = out_t.cpu().numpy()[sample]
+    want = oc.decode_attn(0, q[sample], oidx, seq[sample], ctx[sample])
+    err = float(np.max(np.abs(got - want)))
+    _say(f"  attention max-abs err over the sample {err:.3g}")
+    assert err <= ATTN_TOL
