@@ -33,6 +33,7 @@ sys.path.insert(0, ROOT)
 import numpy as np  # noqa: E402
 
 PEAK_HBM_GBS = 8000.0
+PEAK_FP32_TFS = 157.3      # MI355X published fp32 vector peak (packed FMA)
 METRIC = "CSA2 decode queries/s at 1M ctx + achieved HBM GB/s as % of MI355X peak"
 SCORE_SRC = os.path.join(ROOT, "fp4_kv_cache_decode_amd", "csrc", "index_score.hip")
 COUNTER_FILE = os.path.join(ROOT, "profiles", "scan_decoder20_1m_b4_counters.txt")
@@ -234,6 +235,232 @@ def copy_bandwidth(nbytes=1 << 30, reps=10):
     return 2 * nbytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
 
 
+# ---------------------------------------------------------------------------
+# Per-row measurements (not the default line): each times one hot-path row at
+# its own bandwidth- or ALU-bound shape and reports it against its roofline.
+
+def _common(args, metric, value, unit, ms, cfg, roofline, cpu=None, hib=True):
+    return {"metric": metric, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": hib,
+            "scaling": "weak", "vs_baseline": None, "dtype": cfg.pop("dtype"),
+            "data": "synthetic", "config": cfg, "roofline": roofline, "cpu_baseline": cpu}
+
+
+def _event_loop(fn, steps, warmup):
+    """Average milliseconds of fn(i) between HIP events on the current stream."""
+    import torch
+    for i in range(warmup):
+        fn(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for i in range(steps):
+        evs[i][0].record()
+        fn(warmup + i)
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    return sum(a.elapsed_time(b) for a, b in evs) / steps
+
+
+def row_quantize(args):
+    """Bulk quantise-on-write of decoder20_1m_b4's cache: 4 x 1,048,576 rows of
+    post-RoPE K, V and indexer keys in one call."""
+    import torch
+    import fp4_kv_cache_decode_amd.csa2 as K
+    from fp4_kv_cache_decode_amd import datagen as G
+    wl = G.WORKLOADS["decoder20_1m_b4"]
+    n = wl.n_seq * wl.N
+    t0 = time.time()
+    k = torch.empty((n, G.D), dtype=torch.float32, device="cuda")
+    v = torch.empty_like(k)
+    ik = torch.empty((n, G.DI), dtype=torch.float32, device="cuda")
+    jobs = [(s, p) for s in range(wl.n_seq) for p in range(0, wl.N, G.CHUNK)]
+    for j0 in range(0, len(jobs), 16):
+        part = jobs[j0:j0 + 16]
+        rows = G.parallel_map(lambda sp: G.kv_rows(args.seed, sp[0], sp[1], sp[1] + G.CHUNK), part)
+        for (s_, p), (kk, vv, ii) in zip(part, rows):
+            r0 = s_ * wl.N + p
+            k[r0:r0 + G.CHUNK].copy_(torch.from_numpy(kk))
+            v[r0:r0 + G.CHUNK].copy_(torch.from_numpy(vv))
+            ik[r0:r0 + G.CHUNK].copy_(torch.from_numpy(ii))
+    seq = torch.arange(wl.n_seq, dtype=torch.int32, device="cuda").repeat_interleave(wl.N)
+    pos = torch.arange(wl.N, dtype=torch.int64, device="cuda").repeat(wl.n_seq)
+    caches = [K.Cache(wl.n_seq, wl.cap, 1) for _ in range(2)]
+    torch.cuda.synchronize()
+    log(f"[bench] quantize inputs ready ({time.time() - t0:.1f}s): {n} rows")
+    ms = _event_loop(lambda i: K.quantize_kv(caches[i % 2], k, v, seq, pos, idx_k=ik),
+                     args.steps, args.warmup)
+    per_row = 2 * G.D * 4 + G.DI * 4 + 4 + 8 + 144 + 64
+    alg = n * per_row
+    gbs = alg / (ms * 1e-3) / 1e9
+    log(f"[bench] bulk quantize {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
+    cfg = {"workload": "bulk quantize of decoder20_1m_b4 (4 x 1,048,576 rows)", "rows": n,
+           "bytes_per_row": per_row, "dtype": "fp32"}
+    roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+            "kernel": "quantize_kernel (csa2_quantize_kv)", "avg_us": ms * 1e3, "alg_bytes": alg}
+    return _common(args, "CSA2 quantise-on-write rows/s", n / (ms * 1e-3), "rows/s", ms, cfg,
+                   roof)
+
+
+def row_gather(args):
+    """Gather/dequant/attention at a bandwidth-bound shape: B=1,024 sequences of
+    65,536 positions, top-512 plus the 128-token window, one layer per call,
+    rotating over 4 (index set, layer) pairs so the 108 MB each call touches is
+    read from HBM, not from the 256 MB Infinity Cache."""
+    import torch
+    import fp4_kv_cache_decode_amd.csa2 as K
+    from fp4_kv_cache_decode_amd import datagen as G
+    B, N, L, R = 1024, 65536, 4, 4
+    t0 = time.time()
+    c = K.Cache(B, N, L)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    # sequence 0 from the generator, then replicated to every sequence
+    for p in range(0, N, G.CHUNK):
+        kk, vv, _ = G.kv_rows(args.seed, 0, p, p + G.CHUNK)
+        K.quantize_kv(c, dev(kk), dev(vv), dev(np.zeros(G.CHUNK, np.int32)),
+                      dev(np.arange(p, p + G.CHUNK, dtype=np.int64)))
+    w0 = N - G.WINDOW
+    kk, vv, _ = G.kv_rows(args.seed, 0, w0, N)
+    wk = np.stack([G.window_rows(args.seed, l, 0, w0, N)[0] for l in range(L)])
+    wv = np.stack([G.window_rows(args.seed, l, 0, w0, N)[1] for l in range(L)])
+    K.quantize_kv(c, dev(kk), dev(vv), dev(np.zeros(G.WINDOW, np.int32)),
+                  dev(np.arange(w0, N, dtype=np.int64)), win_k=dev(wk), win_v=dev(wv))
+    c.kv[1:].copy_(c.kv[0:1].expand(B - 1, -1, -1))
+    c.wk[:, 1:].copy_(c.wk[:, 0:1].expand(-1, B - 1, -1, -1))
+    c.wv[:, 1:].copy_(c.wv[:, 0:1].expand(-1, B - 1, -1, -1))
+    rng = np.random.default_rng(args.seed)
+    idxs = []
+    for r in range(R):
+        sel = np.sort(np.argpartition(rng.random((B, N), dtype=np.float32), G.TOPK, axis=1)
+                      [:, :G.TOPK], axis=1).astype(np.int32)
+        idxs.append(dev(sel))
+    qs = [dev(G.attn_queries(args.seed, l, B)) for l in range(L)]
+    seq = dev(np.arange(B, dtype=np.int32))
+    ctx = dev(np.full(B, N, np.int64))
+    out = torch.empty((B, G.H, G.D), dtype=torch.float32, device="cuda")
+    ws = K.alloc_workspace(K.OP_DECODE_ATTN, B)
+    torch.cuda.synchronize()
+    log(f"[bench] gather inputs ready ({time.time() - t0:.1f}s)")
+    ms = _event_loop(lambda i: K.decode_attn(c, i % L, qs[i % L], idxs[i % R], seq, ctx, out, ws),
+                     args.steps, args.warmup)
+    per_q = G.TOPK * 144 + G.WINDOW * 2 * G.D + G.H * G.D * 4 + G.TOPK * 4 + 12 + G.H * G.D * 4
+    alg = B * per_q
+    gbs = alg / (ms * 1e-3) / 1e9
+    log(f"[bench] gather-attention {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
+    cfg = {"workload": "gather_attention_b1024_n64k", "batch": B, "ctx": N, "topk": G.TOPK,
+           "window": G.WINDOW, "rotations": R, "dtype": "fp32"}
+    roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+            "kernel": "attn_kernel + attn_merge_kernel (csa2_decode_attn)", "avg_us": ms * 1e3,
+            "alg_bytes": alg}
+    return _common(args, "CSA2 gather/dequant/attention queries/s", B / (ms * 1e-3), "queries/s",
+                   ms, cfg, roof)
+
+
+def row_prefill(args):
+    """The 8,192-token prefill chunk over a 131,072-token prefix: quantise the
+    chunk (main KV, indexer keys, window rows), then the Full-layer indexer and
+    attention for all 8,192 causal queries (seq 0, ctx_i = 131,073 + i)."""
+    import torch
+    import fp4_kv_cache_decode_amd.csa2 as K
+    from fp4_kv_cache_decode_amd import datagen as G
+    wl = G.WORKLOADS["prefill_8k_over_128k"]
+    B, N0, cap = wl.B, wl.N, wl.cap
+    t0 = time.time()
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    c = K.Cache(1, cap, 1, wl.w_cap)
+    w_lo = N0 - G.WINDOW
+    oc = None
+    if not args.no_cpu_baseline:
+        import oracle as O
+        oc = O.Cache(1, cap, 1, wl.w_cap)
+    for p in range(0, N0, G.CHUNK):
+        kk, vv, ii = G.kv_rows(args.seed, 0, p, p + G.CHUNK)
+        sq, ps = np.zeros(G.CHUNK, np.int32), np.arange(p, p + G.CHUNK, dtype=np.int64)
+        K.quantize_kv(c, dev(kk), dev(vv), dev(sq), dev(ps), idx_k=dev(ii))
+        if oc is not None:
+            oc.quantize(kk, vv, ii, None, None, sq, ps)
+    kk, vv, _ = G.kv_rows(args.seed, 0, w_lo, N0)
+    wk, wv = G.window_rows(args.seed, 0, 0, w_lo, N0)
+    sq, ps = np.zeros(G.WINDOW, np.int32), np.arange(w_lo, N0, dtype=np.int64)
+    K.quantize_kv(c, dev(kk), dev(vv), dev(sq), dev(ps), win_k=dev(wk[None]), win_v=dev(wv[None]))
+    if oc is not None:
+        oc.quantize(kk, vv, None, wk[None], wv[None], sq, ps)
+    # the chunk: its rows are written inside every timed step
+    ck, cv, ci = G.kv_rows(args.seed, 0, N0, cap)
+    cwk, cwv = G.window_rows(args.seed, 0, 0, N0, cap)
+    chunk = dict(k=dev(ck), v=dev(cv), ik=dev(ci), wk=dev(cwk[None]), wv=dev(cwv[None]),
+                 seq=dev(np.zeros(B, np.int32)), pos=dev(np.arange(N0, cap, dtype=np.int64)))
+    if oc is not None:
+        oc.quantize(ck, cv, ci, cwk[None], cwv[None], np.zeros(B, np.int32),
+                    np.arange(N0, cap, dtype=np.int64))
+    seq_np, ctx_np = wl.seq(), wl.ctx()
+    qi_np, wi_np = G.index_queries(args.seed, 0, B)
+    q_np = G.attn_queries(args.seed, 0, B)
+    seq, ctx, qi, wi, q = dev(seq_np), dev(ctx_np), dev(qi_np), dev(wi_np), dev(q_np)
+    M = torch.empty((B, K.block_stride(cap)), dtype=torch.float32, device="cuda")
+    pool = torch.empty((B, G.N_BLOCKS), dtype=torch.int32, device="cuda")
+    idx = torch.empty((B, G.TOPK), dtype=torch.int32, device="cuda")
+    out = torch.empty((B, G.H, G.D), dtype=torch.float32, device="cuda")
+    ws_sel = K.alloc_workspace(K.OP_SELECT_POOL, B, cap)
+    ws_ri = K.alloc_workspace(K.OP_INDEX_REINDEX, B)
+    ws_at = K.alloc_workspace(K.OP_DECODE_ATTN, B)
+    torch.cuda.synchronize()
+    log(f"[bench] prefill inputs ready ({time.time() - t0:.1f}s)")
+
+    scan_ev = []
+
+    def step(i, timed=False):
+        K.quantize_kv(c, chunk["k"], chunk["v"], chunk["seq"], chunk["pos"], idx_k=chunk["ik"],
+                      win_k=chunk["wk"], win_v=chunk["wv"])
+        if timed:
+            e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            e[0].record()
+        K.index_block_scores(c, qi, wi, seq, ctx, cap, M)
+        if timed:
+            e[1].record()
+            scan_ev.append(e)
+        K.index_select_pool(M, ctx, cap, pool, ws_sel)
+        K.index_reindex(c, qi, wi, seq, ctx, pool, idx, ws_ri)
+        K.decode_attn(c, 0, q, idx, seq, ctx, out, ws_at)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, timed=True)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t1) * 1e3 / args.steps
+    scan_ms = sum(a.elapsed_time(b) for a, b in scan_ev) / len(scan_ev)
+    key_evals = int(ctx_np.sum())
+    flops = 2 * G.HI * G.DI * key_evals
+    tfs = flops / (scan_ms * 1e-3) / 1e12
+    log(f"[bench] prefill chunk {ms:.2f} ms, scan {scan_ms:.2f} ms = {tfs:.1f} TFLOP/s")
+    cpu = None
+    if oc is not None:
+        # a strided sample of the chunk's queries through the oracle (index + attention)
+        sample = np.arange(0, B, 256)
+        ts = time.perf_counter()
+        _, oidx, _, _ = oc.index_full(qi_np[sample], wi_np[sample], seq_np[sample], ctx_np[sample])
+        oc.decode_attn(0, q_np[sample], oidx, seq_np[sample], ctx_np[sample])
+        secs = time.perf_counter() - ts
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        cpu = {"value": sample.size / secs, "unit": "queries/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{sample.size} of the chunk's 8,192 queries (every 256th) through "
+                         f"the fp64 C oracle's indexer and attention, {secs:.1f} s wall"}
+    cfg = {"workload": wl.name, "queries": B, "prefix": N0, "topk": G.TOPK,
+           "pool_blocks": G.N_BLOCKS, "window": G.WINDOW, "key_evals": key_evals, "dtype": "fp32"}
+    roof = {"bound": "alu", "achieved": tfs, "peak": PEAK_FP32_TFS, "unit": "TFLOP/s",
+            "frac": tfs / PEAK_FP32_TFS, "traffic": None,
+            "kernel": "scan_kernel (csa2_index_block_scores)", "avg_us": scan_ms * 1e3,
+            "flops": flops}
+    return _common(args, "CSA2 chunked-prefill queries/s", B / (ms * 1e-3), "queries/s", ms, cfg,
+                   roof, cpu)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,6 +474,10 @@ def main():
                     help="launch every kernel from Python instead of replaying HIP graphs")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
+    ap.add_argument("--row", default="decode", choices=["decode", "quantize", "gather", "prefill"],
+                    help="decode: the whole decode step (default); quantize: bulk quantise-on-write "
+                         "of the 1M-context cache; gather: gather/dequant/attention at B=1024; "
+                         "prefill: the 8,192-query chunk over a 131,072-token prefix")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -261,6 +492,10 @@ def main():
         sys.exit(1)
     if args.copy_probe:
         log(f"[bench] copy probe: {copy_bandwidth():.0f} GB/s")
+        return
+    if args.row != "decode":
+        res = {"quantize": row_quantize, "gather": row_gather, "prefill": row_prefill}[args.row](args)
+        print(json.dumps(res), flush=True)
         return
 
     from fp4_kv_cache_decode_amd import datagen as G
