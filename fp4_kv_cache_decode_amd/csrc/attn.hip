@@ -8,16 +8,34 @@
 // Bounded Replay").  Reading taken here: one softmax per head over the valid
 // main rows and the window rows [max(0,N-128), N), logits (q.k)*sm_scale.
 //
-// Design: split-K over 64-entry tiles.  Workgroup (tile, b) gathers its 64
-// entries (144-byte records, or 256-byte window rows), dequantises them into
-// LDS as f16 (exact: an E2M1 value times an E4M3 scale has at most 5
-// significant bits, an E4M3 value has 4), and runs the 16-head x 64-entry x
-// 128-dim contraction on MFMA (v_mfma_f32_16x16x16_f16).  The fp32 query and
-// the fp32 softmax weights are each split into f16 hi + lo parts and issued as
-// two MFMAs, so products are exact and accumulation is fp32: the result is
-// fp32-accurate, far inside the 2e-3 output budget.  Each tile writes its
-// running max m, sum l and unnormalised output o; a merge kernel rescales and
-// combines the tiles (the same algebra an unsplit online softmax uses).
+// Two kernels share the partial format and the merge kernel.  For few queries
+// (the decode batches of long contexts) the tile kernel runs one workgroup per
+// (query, 64-entry tile) so that every tile's gather starts at once.  For many
+// queries the stream kernel below keeps fewer, longer-lived workgroups busy.
+//
+// Stream kernel (gfx950, wave64): each wave streams 16-entry steps of one query with
+// its own online softmax (flash-decoding).  For a step, lane (c, g) (c = lane
+// mod 16, g = lane / 16) gathers entry c: 32 K channels 32g..32g+31 and 32 V
+// channels {8g + 32k + i}.  Scores are computed transposed, S^T = K Q^T, on
+// v_mfma_f32_16x16x16_f16 with K as the A operand straight from the gathering
+// lane's registers: the contraction over channels is taken in the order
+// d = 32g + 4ks + j, which is the order the lane holds them in, and the query
+// fragments are loaded in the same order.  The result leaves lane (c, g) with
+// the scores of head c for entries 4g..4g+3, which is exactly the B-operand
+// layout of O^T = V^T P^T, so the softmax weights never move between lanes.
+// Only V is transposed, through a per-wave LDS tile; no barrier is needed
+// inside the loop because every wave touches only its own tile.  The next
+// step's records are in flight while a step is computed.
+//
+// Precision: dequantised values are exact in f16 (an E2M1 value times an E4M3
+// scale has at most 5 significant bits, an E4M3 value has 4).  The fp32 query
+// and the fp32 softmax weights are split into f16 hi + lo parts and issued as
+// two MFMAs, so products are exact and accumulation is fp32.
+//
+// A workgroup (4 waves) owns a range of a query's steps; the waves' (m, l, O)
+// are combined in LDS.  With one workgroup per query (large batches) it writes
+// the output directly; otherwise each split writes (m, l, O) partials and a
+// merge kernel combines them (the same algebra an unsplit softmax uses).
 //
 // FP4 dequantisation: the f16 encodings of the E2M1 magnitudes {0, .5, 1, 1.5,
 // 2, 3, 4, 6} differ only in their high byte, so v_perm_b32 with an 8-byte table
@@ -34,13 +52,18 @@ typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
 
 constexpr int AT_THREADS = 256;
+constexpr int AT_WAVES = AT_THREADS / 64;
+constexpr int SUB = 16;                   // entries per wave step
+constexpr int VT_STRIDE = 20;             // f16 per transposed V row (16 entries + 4 pad)
+constexpr float NEG_INF = -__builtin_huge_valf();
+// tile kernel (small batches): used while B x tiles fits one wave of workgroups
+constexpr int64_t TILE_KERNEL_MAX_WG = 768;
 constexpr int TILE = 64;
 constexpr int KROW = 136;    // f16 per K row in LDS (128 + 8 pad)
 constexpr int VROW = 72;     // f16 per transposed V row (64 + 8 pad)
 constexpr int PROW = 72;     // f16 per P row
-constexpr float NEG_INF = -__builtin_huge_valf();
 
-struct AttnArgs {
+struct StreamArgs {
     const uint8_t* kv;
     const uint8_t* wk;
     const uint8_t* wv;
@@ -48,27 +71,30 @@ struct AttnArgs {
     const int32_t* idx;
     const int32_t* seq;
     const int64_t* ctx;
-    float* part;
+    float* part;             // [B][n_split][ATTN_PART_FLOATS] when n_split > 1
+    float* out;              // [B][16][128] when n_split == 1
     int64_t cap;
     int32_t n_seq;
     int32_t w_cap;
     int32_t layer;
     int32_t topk;
-    int32_t n_main;          // main tiles
-    int32_t n_tiles;
+    int32_t n_sub_main;      // steps over the index list
+    int32_t n_sub;           // plus the window's steps
+    int32_t n_split;         // workgroups per query
     float wk_scale;
     float wv_scale;
     float sm_scale;
 };
 
-struct AttnShared {
-    _Float16 K[TILE * KROW];
-    _Float16 Vt[D * VROW];
-    _Float16 Phi[HEADS * PROW];
-    _Float16 Plo[HEADS * PROW];
-    float red[4][HEADS];
-    float lsum[4][HEADS];
-    int valid[TILE];
+struct StreamShared {
+    union {
+        _Float16 vt[AT_WAVES][D * VT_STRIDE];      // per-wave V^T of one step
+        struct {
+            float o[AT_WAVES][HEADS * D];
+            float m[AT_WAVES][HEADS];
+            float l[AT_WAVES][HEADS];
+        } mg;                                      // the waves' softmax states
+    };
 };
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
@@ -102,8 +128,57 @@ __device__ __forceinline__ void fp4x8_to_f16x2(uint32_t w, half2_t scale, uint32
     }
 }
 
-__global__ void __launch_bounds__(AT_THREADS) attn_kernel(AttnArgs a) {
-    __shared__ AttnShared sh;
+// 4 E4M3 bytes -> 4 f16 (exact) packed in two dwords.
+__device__ __forceinline__ void fp8x4_to_f16x4(uint32_t w, uint32_t* o) {
+    const float2 a = e4m3x2_to_f32<false>(w), b = e4m3x2_to_f32<true>(w);
+    o[0] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)a.x, (_Float16)a.y});
+    o[1] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)b.x, (_Float16)b.y});
+}
+
+__device__ __forceinline__ float xor32_f32(float v) {
+    const int lane = __lane_id();
+    return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(v)));
+}
+
+// ---------------------------------------------------------------------------
+// Tile kernel (small batches, latency): one workgroup per (query, 64-entry
+// tile).  Four threads gather an entry, the dequantised K and V^T of the tile
+// are staged in LDS, the 4 waves each take 16 entries of S = Q K^T and 32
+// output dims of P V, and the tile writes its (m, l, O) partial.
+
+struct TileArgs {
+    const uint8_t* kv;
+    const uint8_t* wk;
+    const uint8_t* wv;
+    const float* q;
+    const int32_t* idx;
+    const int32_t* seq;
+    const int64_t* ctx;
+    float* part;
+    int64_t cap;
+    int32_t n_seq;
+    int32_t w_cap;
+    int32_t layer;
+    int32_t topk;
+    int32_t n_main;          // main tiles
+    int32_t n_tiles;
+    float wk_scale;
+    float wv_scale;
+    float sm_scale;
+};
+
+struct TileShared {
+    _Float16 K[TILE * KROW];
+    _Float16 Vt[D * VROW];
+    _Float16 Phi[HEADS * PROW];
+    _Float16 Plo[HEADS * PROW];
+    float red[4][HEADS];
+    float lsum[4][HEADS];
+    int valid[TILE];
+};
+
+__global__ void __launch_bounds__(AT_THREADS) attn_tile_kernel(TileArgs a) {
+    __shared__ TileShared sh;
     const int tile = blockIdx.x;
     const int b = blockIdx.y;
     const int t = threadIdx.x;
@@ -297,6 +372,271 @@ __global__ void __launch_bounds__(AT_THREADS) attn_kernel(AttnArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Stream kernel (large batches, bandwidth): see the file header.
+
+// Raw bytes of one step's entry for this lane, loaded ahead of use.
+//  main:   r[0..3] K codes of channels 32g..32g+31, r[4..7] V codes of channels
+//          8g+32k..8g+32k+7 (k = 0..3), r[8..11] the record's 16 scale bytes
+//  window: r[0..7] K bytes of channels 32g..32g+31, r[8..15] V bytes of
+//          channels 8g+32k..+7 (two dwords per k)
+struct Raw {
+    uint32_t r[16];
+};
+
+// 3 workgroups (12 waves) per CU: 148 VGPRs without spills
+__global__ void __launch_bounds__(AT_THREADS, 3) attn_stream_kernel(StreamArgs a) {
+    __shared__ StreamShared sh;
+    const int split = blockIdx.x;
+    const int b = blockIdx.y;
+    const int t = threadIdx.x;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int c = lane & 15, g = lane >> 4;
+    const int32_t s = a.seq[b];
+    const int64_t N = clamp64(a.ctx[b], 0, a.cap);
+    const bool seq_ok = s >= 0 && s < a.n_seq;
+    const int64_t u0 = N > WINDOW ? N - WINDOW : 0;
+    // this workgroup's steps [t_begin, t_end); wave w takes t_begin + w, + 4, ...
+    const int t_begin = (int)((int64_t)split * a.n_sub / a.n_split);
+    const int t_end = (int)((int64_t)(split + 1) * a.n_sub / a.n_split);
+    const int main_end = t_end < a.n_sub_main ? t_end : a.n_sub_main;
+    const int32_t* idx_row = a.idx + (int64_t)b * a.topk;
+
+    // ---- query fragments (B operand of S^T = K Q^T): Q[h = c][32g + 4ks + j],
+    // split into f16 hi + lo
+    half4_t qhi[8], qlo[8];
+    {
+        const float* qrow = a.q + ((int64_t)b * HEADS + c) * D + 32 * g;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const float4 v = *reinterpret_cast<const float4*>(qrow + 4 * ks);
+            const float x[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const _Float16 hi = (_Float16)x[i];
+                qhi[ks][i] = hi;
+                qlo[ks][i] = (_Float16)(x[i] - (float)hi);
+            }
+        }
+    }
+
+    auto load_idx = [&](int st) -> int32_t {
+        const int j = SUB * st + c;
+        return (st < main_end && j < a.topk) ? idx_row[j] : -1;
+    };
+    // issue the loads of step st for this lane; returns whether the entry is valid
+    auto fetch = [&](int st, int32_t pos, Raw& w) -> bool {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) w.r[i] = 0u;
+        if (st < a.n_sub_main) {
+            const bool ok = seq_ok && pos >= 0 && pos < N;
+            const uint8_t* rec = a.kv + (ok ? ((int64_t)s * a.cap + pos) * RECORD : 0);
+            const uint4 kc = *reinterpret_cast<const uint4*>(rec + 16 * g);
+            const uint4 sc = *reinterpret_cast<const uint4*>(rec + 128);
+            w.r[0] = kc.x; w.r[1] = kc.y; w.r[2] = kc.z; w.r[3] = kc.w;
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                w.r[4 + k] = *reinterpret_cast<const uint32_t*>(rec + 64 + 4 * g + 16 * k);
+            w.r[8] = sc.x; w.r[9] = sc.y; w.r[10] = sc.z; w.r[11] = sc.w;
+            return ok;
+        }
+        const int64_t u = u0 + (int64_t)(st - a.n_sub_main) * SUB + c;
+        const bool ok = seq_ok && u < N;
+        const int64_t row = ok ? (((int64_t)a.layer * a.n_seq + s) * a.w_cap + u % a.w_cap) * D : 0;
+        const uint4 k0 = *reinterpret_cast<const uint4*>(a.wk + row + 32 * g);
+        const uint4 k1 = *reinterpret_cast<const uint4*>(a.wk + row + 32 * g + 16);
+        w.r[0] = k0.x; w.r[1] = k0.y; w.r[2] = k0.z; w.r[3] = k0.w;
+        w.r[4] = k1.x; w.r[5] = k1.y; w.r[6] = k1.z; w.r[7] = k1.w;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint2 v = *reinterpret_cast<const uint2*>(a.wv + row + 8 * g + 32 * k);
+            w.r[8 + 2 * k] = v.x;
+            w.r[9 + 2 * k] = v.y;
+        }
+        return ok;
+    };
+
+    // softmax state of head c (lanes c, c+16, c+32, c+48 hold the same m; l is
+    // this lane's partial sum) and O^T[d = 16 mt + 4g + r][h = c]
+    float m_run = NEG_INF, l_run = 0.0f;
+    float4_t o[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) o[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    _Float16* vt = sh.vt[wave];
+
+    int st = t_begin + wave;
+    Raw cur, nxt;
+    bool ok_cur = false, ok_nxt = false;
+    int32_t idx_next = -1;
+    if (st < t_end) {
+        ok_cur = fetch(st, load_idx(st), cur);
+        idx_next = load_idx(st + AT_WAVES);
+    }
+    for (; st < t_end; st += AT_WAVES) {
+        const bool is_main = st < a.n_sub_main;
+        // ---- dequantise this step: K into A-operand fragments, V into LDS (V^T)
+        half4_t kf[8];
+        uint32_t vv[16];                      // f16x2: channels 8g+32k+2i, +1 in vv[4k+i]
+        if (is_main) {
+            const uint32_t sk = ((g >> 1) ? cur.r[9] : cur.r[8]) >> (16 * (g & 1));   // K scales 2g, 2g+1
+            const half2_t k0 = scale_h2(sk & 0xff), k1 = scale_h2((sk >> 8) & 0xff);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                uint32_t w4[4];
+                fp4x8_to_f16x2(cur.r[i], i < 2 ? k0 : k1, w4);
+                kf[2 * i] = __builtin_bit_cast(half4_t, make_uint2(w4[0], w4[1]));
+                kf[2 * i + 1] = __builtin_bit_cast(half4_t, make_uint2(w4[2], w4[3]));
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                // V group of channels 8g+32k.. is 2k + g/2: scale byte 8 + 2k + g/2,
+                // i.e. byte 2(k&1) + g/2 of scale dword 10 + k/2
+                const uint32_t code =
+                    (cur.r[10 + (k >> 1)] >> (8 * (2 * (k & 1) + (g >> 1)))) & 0xff;
+                fp4x8_to_f16x2(cur.r[4 + k], scale_h2(code), vv + 4 * k);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                uint32_t w2[2];
+                fp8x4_to_f16x4(cur.r[i], w2);
+                kf[i] = __builtin_bit_cast(half4_t, make_uint2(w2[0], w2[1]));
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                fp8x4_to_f16x4(cur.r[8 + 2 * k], vv + 4 * k);
+                fp8x4_to_f16x4(cur.r[9 + 2 * k], vv + 4 * k + 2);
+            }
+        }
+        if (!ok_cur) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) kf[i] = half4_t{0, 0, 0, 0};
+#pragma unroll
+            for (int i = 0; i < 16; ++i) vv[i] = 0u;
+        }
+        const uint64_t vmask = __ballot(ok_cur);     // bit e (e < 16): entry e valid
+        {
+            unsigned short* vts = reinterpret_cast<unsigned short*>(vt);
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int d = 8 * g + 32 * k + 2 * i;
+                    vts[d * VT_STRIDE + c] = (unsigned short)(vv[4 * k + i] & 0xffffu);
+                    vts[(d + 1) * VT_STRIDE + c] = (unsigned short)(vv[4 * k + i] >> 16);
+                }
+        }
+        // the V^T tile is private to this wave and LDS executes a wave's
+        // operations in order; this only keeps the compiler from moving the
+        // tile's reads above its writes
+        asm volatile("" ::: "memory");
+        // ---- the next step's loads go out now and overlap the MFMA work below
+        const int sn = st + AT_WAVES;
+        if (sn < t_end) {
+            ok_nxt = fetch(sn, idx_next, nxt);
+            idx_next = load_idx(sn + AT_WAVES);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+
+        // ---- S^T = K Q^T: lane (c, g) gets S[head c][entry 4g + r]
+        float4_t sacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            sacc = __builtin_amdgcn_mfma_f32_16x16x16f16(kf[ks], qhi[ks], sacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_16x16x16f16(kf[ks], qlo[ks], sacc, 0, 0, 0);
+        }
+        const float lscale = a.sm_scale * (is_main ? 1.0f : a.wk_scale);
+        float sv[4];
+        float tmax = NEG_INF;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const bool ok = (vmask >> (4 * g + r)) & 1u;
+            sv[r] = ok ? sacc[r] * lscale : NEG_INF;
+            tmax = fmaxf(tmax, sv[r]);
+        }
+        tmax = fmaxf(tmax, swz_xor16(tmax));
+        tmax = fmaxf(tmax, xor32_f32(tmax));
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = m_run == NEG_INF ? 0.0f : expf(m_run - m_new);
+        const float vsc = is_main ? 1.0f : a.wv_scale;
+        half4_t phi, plo;
+        float psum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float p = sv[r] == NEG_INF ? 0.0f : expf(sv[r] - m_new);
+            psum += p;
+            const float pv = p * vsc;
+            const _Float16 h = (_Float16)pv;
+            phi[r] = h;
+            plo[r] = (_Float16)(pv - (float)h);
+        }
+        l_run = l_run * alpha + psum;
+        m_run = m_new;
+        // ---- O^T = O^T * alpha + V^T P^T
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            const half4_t vf =
+                *reinterpret_cast<const half4_t*>(&vt[(16 * mt + c) * VT_STRIDE + 4 * g]);
+            o[mt] *= alpha;
+            o[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, phi, o[mt], 0, 0, 0);
+            o[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, plo, o[mt], 0, 0, 0);
+        }
+        cur = nxt;
+        ok_cur = ok_nxt;
+        asm volatile("" ::: "memory");     // next step's tile writes after these reads
+    }
+
+    // ---- combine the 4 waves: l over the 4 lanes of a head, then LDS
+    l_run += swz_xor16(l_run);
+    l_run += xor32_f32(l_run);
+    __syncthreads();                       // every wave is done with its V^T tile
+    if (g == 0) {
+        sh.mg.m[wave][c] = m_run;
+        sh.mg.l[wave][c] = l_run;
+    }
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+        *reinterpret_cast<float4_t*>(&sh.mg.o[wave][c * D + 16 * mt + 4 * g]) = o[mt];
+    __syncthreads();
+    {
+        const int h = t >> 4, d0 = (t & 15) * 8;
+        float mw[AT_WAVES], M = NEG_INF;
+#pragma unroll
+        for (int w = 0; w < AT_WAVES; ++w) {
+            mw[w] = sh.mg.m[w][h];
+            M = fmaxf(M, mw[w]);
+        }
+        float L = 0.0f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (M != NEG_INF) {
+#pragma unroll
+            for (int w = 0; w < AT_WAVES; ++w) {
+                const float wt = mw[w] == NEG_INF ? 0.0f : expf(mw[w] - M);
+                L += wt * sh.mg.l[w][h];
+                const float4* src = reinterpret_cast<const float4*>(&sh.mg.o[w][h * D + d0]);
+                const float4 x0 = src[0], x1 = src[1];
+                acc[0] += wt * x0.x; acc[1] += wt * x0.y; acc[2] += wt * x0.z; acc[3] += wt * x0.w;
+                acc[4] += wt * x1.x; acc[5] += wt * x1.y; acc[6] += wt * x1.z; acc[7] += wt * x1.w;
+            }
+        }
+        if (a.n_split == 1) {
+            const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+            float4* dst = reinterpret_cast<float4*>(a.out + ((int64_t)b * HEADS + h) * D + d0);
+            dst[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+            dst[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+        } else {
+            float* part = a.part + ((int64_t)b * a.n_split + split) * ATTN_PART_FLOATS;
+            if ((t & 15) == 0) {
+                part[h] = M;
+                part[HEADS + h] = L;
+            }
+            float4* dst = reinterpret_cast<float4*>(part + 2 * HEADS + h * D + d0);
+            dst[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+            dst[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+        }
+    }
+}
+
 // Combine the tiles of each query: out = sum_t e^(m_t - M) o_t / sum_t e^(m_t - M) l_t.
 // Each thread owns 8 output dims of one head; it loads the partials of up to
 // MERGE_BATCH tiles at once (one memory round trip for the default 10 tiles).
@@ -360,7 +700,36 @@ hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
                        const float* q, const int32_t* idx, const int32_t* seq,
                        const int64_t* ctx, int32_t B, int32_t topk, float sm_scale,
                        float* out, float* partials, hipStream_t stream) {
-    AttnArgs a{};
+    const int32_t n_tiles = attn_tiles(topk);
+    if ((int64_t)B * n_tiles <= TILE_KERNEL_MAX_WG) {
+        // few queries: one workgroup per 64-entry tile, the shortest dependency chain
+        TileArgs a{};
+        a.kv = c.kv;
+        a.wk = w.k;
+        a.wv = w.v;
+        a.q = q;
+        a.idx = idx;
+        a.seq = seq;
+        a.ctx = ctx;
+        a.part = partials;
+        a.cap = c.cap;
+        a.n_seq = c.n_seq;
+        a.w_cap = w.w_cap;
+        a.layer = layer;
+        a.topk = topk;
+        a.n_main = (topk + TILE - 1) / TILE;
+        a.n_tiles = n_tiles;
+        a.wk_scale = w.k_scale;
+        a.wv_scale = w.v_scale;
+        a.sm_scale = sm_scale;
+        hipLaunchKernelGGL(attn_tile_kernel, dim3(n_tiles, B), dim3(AT_THREADS), 0, stream, a);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(attn_merge_kernel, dim3(B), dim3(AT_THREADS), 0, stream, partials,
+                           n_tiles, out);
+        return hipGetLastError();
+    }
+    StreamArgs a{};
     a.kv = c.kv;
     a.wk = w.k;
     a.wv = w.v;
@@ -369,21 +738,26 @@ hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
     a.seq = seq;
     a.ctx = ctx;
     a.part = partials;
+    a.out = out;
     a.cap = c.cap;
     a.n_seq = c.n_seq;
     a.w_cap = w.w_cap;
     a.layer = layer;
     a.topk = topk;
-    a.n_main = (topk + TILE - 1) / TILE;
-    a.n_tiles = attn_tiles(topk);
     a.wk_scale = w.k_scale;
     a.wv_scale = w.v_scale;
     a.sm_scale = sm_scale;
-    hipLaunchKernelGGL(attn_kernel, dim3(a.n_tiles, B), dim3(AT_THREADS), 0, stream, a);
+    a.n_sub_main = (topk + SUB - 1) / SUB;
+    a.n_sub = a.n_sub_main + WINDOW / SUB;
+    // about one workgroup per resident slot (256 CUs x 3), at least one step per wave
+    int32_t split = (768 + B - 1) / B;
+    const int32_t max_split = (a.n_sub + AT_WAVES - 1) / AT_WAVES;
+    a.n_split = split < 1 ? 1 : (split > max_split ? max_split : split);
+    hipLaunchKernelGGL(attn_stream_kernel, dim3(a.n_split, B), dim3(AT_THREADS), 0, stream, a);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || a.n_split == 1) return e;
     hipLaunchKernelGGL(attn_merge_kernel, dim3(B), dim3(AT_THREADS), 0, stream, partials,
-                       a.n_tiles, out);
+                       a.n_split, out);
     return hipGetLastError();
 }
 

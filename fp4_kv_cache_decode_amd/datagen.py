@@ -65,10 +65,13 @@ def _normal_rows(seed: int, kind: int, layer: int, seq: int, p0: int, p1: int,
     out = np.empty((p1 - p0, width), np.float32)
     c0, c1 = p0 // CHUNK, (p1 - 1) // CHUNK if p1 > p0 else p0 // CHUNK - 1
     for c in range(c0, c1 + 1):
-        blk = _rng(seed, kind, layer, seq, c).standard_normal((CHUNK, width), dtype=np.float32)
         lo = max(p0, c * CHUNK)
         hi = min(p1, (c + 1) * CHUNK)
-        out[lo - p0:hi - p0] = blk[lo - c * CHUNK:hi - c * CHUNK]
+        # the generator fills row-major, so drawing only the chunk's first
+        # hi - c*CHUNK rows yields the same values as drawing the whole chunk
+        blk = _rng(seed, kind, layer, seq, c).standard_normal((hi - c * CHUNK, width),
+                                                              dtype=np.float32)
+        out[lo - p0:hi - p0] = blk[lo - c * CHUNK:]
     cols = outlier_channels(seed, kind, width, layer)
     out[:, cols] *= np.float32(OUTLIER_GAIN)
     return out

@@ -290,6 +290,39 @@ def test_decode_attn_zero_query_is_mean(K):
     assert np.max(np.abs(out.cpu().numpy() - want)) <= 1e-5
 
 
+@pytest.mark.parametrize("B", [96, 800])
+def test_decode_attn_many_queries(K, B):
+    """Batches past one wave of tile workgroups take the streaming kernel (split
+    into partials at B=96, one workgroup per query at B=800): ragged contexts,
+    padded and partly empty index lists, windows clipped at position 0."""
+    _say(f"decode_attn many queries B={B}")
+    N, L, layer = 700, 2, 1
+    # window stores hold every position (w_cap >= N), so each query's window
+    # [ctx - 128, ctx) is present whatever its ctx
+    oc = O.Cache(B, N, L, w_cap=1024)
+    gc = K.Cache(B, N, L, w_cap=1024)
+    fill_both(40 + B, B, N, L, oc, gc, wlo=0)
+    rng = np.random.default_rng(B)
+    seq = np.arange(B, dtype=np.int32)
+    ctx = rng.integers(1, N + 1, B).astype(np.int64)
+    ctx[:4] = [1, 2, 127, N]
+    idx = np.full((B, 512), -1, np.int32)
+    for b in range(B):
+        n = int(rng.integers(0, min(512, int(ctx[b])) + 1))
+        if b == 5:
+            n = 0                            # window entries only
+        idx[b, :n] = np.sort(rng.choice(int(ctx[b]), n, replace=False))
+    q = G.attn_queries(40 + B, layer, B)
+    want = oc.decode_attn(layer, q, idx, seq, ctx)
+    out = torch.empty((B, 16, 128), dtype=torch.float32, device="cuda")
+    ws = K.alloc_workspace(K.OP_DECODE_ATTN, B)
+    K.decode_attn(gc, layer, dev(q), dev(idx), dev(seq), dev(ctx), out, ws)
+    torch.cuda.synchronize()
+    err = float(np.max(np.abs(out.cpu().numpy() - want)))
+    _say(f"  max-abs err {err:.3g}")
+    assert err <= 1e-4
+
+
 def test_reuse_layers_share_indices(K):
     """Reuse: the group's idx buffer is passed unchanged to every layer."""
     _say("reuse layers")
