@@ -88,7 +88,10 @@ struct StreamArgs {
 
 struct StreamShared {
     union {
-        _Float16 vt[AT_WAVES][D * VT_STRIDE];      // per-wave V^T of one step
+        struct {
+            _Float16 vt[AT_WAVES][D * VT_STRIDE];  // per-wave V^T of one step
+            half4_t q[2][8][64];                   // query fragments (hi, lo) per ks, per lane
+        } st;
         struct {
             float o[AT_WAVES][HEADS * D];
             float m[AT_WAVES][HEADS];
@@ -134,6 +137,31 @@ __device__ __forceinline__ void fp8x4_to_f16x4(uint32_t w, uint32_t* o) {
     o[0] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)a.x, (_Float16)a.y});
     o[1] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)b.x, (_Float16)b.y});
 }
+
+// The gfx950 scaled converters.  Their fp32 scale operand applies only its
+// power of two (E8M0 semantics), so it is 1 here and the E4M3 group scale is
+// applied by a packed f16 multiply (exact: at most 6 significant bits).
+// FP4: byte `sel` of w -> (low nibble, high nibble) as exact E2M1 values.
+template <int SEL>
+__device__ __forceinline__ half2_t fp4x2_h2(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, SEL);
+}
+// FP8: word HI of w -> two exact E4M3 values.
+template <bool HI>
+__device__ __forceinline__ half2_t fp8x2_h2(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, HI);
+}
+// 8 FP4 codes (channel 2j in the low nibble of byte j) times a group scale ->
+// 4 f16x2 words (channels 2j, 2j+1 in word j).
+__device__ __forceinline__ void fp4x8_scaled(uint32_t w, half2_t scale, uint32_t* o) {
+    o[0] = __builtin_bit_cast(uint32_t, fp4x2_h2<0>(w) * scale);
+    o[1] = __builtin_bit_cast(uint32_t, fp4x2_h2<1>(w) * scale);
+    o[2] = __builtin_bit_cast(uint32_t, fp4x2_h2<2>(w) * scale);
+    o[3] = __builtin_bit_cast(uint32_t, fp4x2_h2<3>(w) * scale);
+}
+
+constexpr float LOG2E = 1.4426950408889634f;
+constexpr float LN2 = 0.6931471805599453f;
 
 __device__ __forceinline__ float xor32_f32(float v) {
     const int lane = __lane_id();
@@ -384,8 +412,8 @@ struct Raw {
     uint32_t r[16];
 };
 
-// 3 workgroups (12 waves) per CU: 148 VGPRs without spills
-__global__ void __launch_bounds__(AT_THREADS, 3) attn_stream_kernel(StreamArgs a) {
+// 4 workgroups (16 waves) per CU: at most 128 VGPRs
+__global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a) {
     __shared__ StreamShared sh;
     const int split = blockIdx.x;
     const int b = blockIdx.y;
@@ -397,6 +425,8 @@ __global__ void __launch_bounds__(AT_THREADS, 3) attn_stream_kernel(StreamArgs a
     const int64_t N = clamp64(a.ctx[b], 0, a.cap);
     const bool seq_ok = s >= 0 && s < a.n_seq;
     const int64_t u0 = N > WINDOW ? N - WINDOW : 0;
+    const int32_t slot0 = (int32_t)(u0 % a.w_cap);         // window slot of position u0
+    const int64_t win_base = ((int64_t)a.layer * a.n_seq + (seq_ok ? s : 0)) * a.w_cap;
     // this workgroup's steps [t_begin, t_end); wave w takes t_begin + w, + 4, ...
     const int t_begin = (int)((int64_t)split * a.n_sub / a.n_split);
     const int t_end = (int)((int64_t)(split + 1) * a.n_sub / a.n_split);
@@ -404,22 +434,27 @@ __global__ void __launch_bounds__(AT_THREADS, 3) attn_stream_kernel(StreamArgs a
     const int32_t* idx_row = a.idx + (int64_t)b * a.topk;
 
     // ---- query fragments (B operand of S^T = K Q^T): Q[h = c][32g + 4ks + j],
-    // split into f16 hi + lo
-    half4_t qhi[8], qlo[8];
-    {
+    // split into f16 hi + lo.  Every wave uses the same fragments; wave 0 builds
+    // them once into LDS (in lane order, so the per-step reads are conflict
+    // free) instead of each wave holding 32 VGPRs of them.
+    if (wave == 0) {
         const float* qrow = a.q + ((int64_t)b * HEADS + c) * D + 32 * g;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             const float4 v = *reinterpret_cast<const float4*>(qrow + 4 * ks);
             const float x[4] = {v.x, v.y, v.z, v.w};
+            half4_t hi4, lo4;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const _Float16 hi = (_Float16)x[i];
-                qhi[ks][i] = hi;
-                qlo[ks][i] = (_Float16)(x[i] - (float)hi);
+                hi4[i] = hi;
+                lo4[i] = (_Float16)(x[i] - (float)hi);
             }
+            sh.st.q[0][ks][lane] = hi4;
+            sh.st.q[1][ks][lane] = lo4;
         }
     }
+    __syncthreads();
 
     auto load_idx = [&](int st) -> int32_t {
         const int j = SUB * st + c;
@@ -441,9 +476,11 @@ __global__ void __launch_bounds__(AT_THREADS, 3) attn_stream_kernel(StreamArgs a
             w.r[8] = sc.x; w.r[9] = sc.y; w.r[10] = sc.z; w.r[11] = sc.w;
             return ok;
         }
-        const int64_t u = u0 + (int64_t)(st - a.n_sub_main) * SUB + c;
-        const bool ok = seq_ok && u < N;
-        const int64_t row = ok ? (((int64_t)a.layer * a.n_seq + s) * a.w_cap + u % a.w_cap) * D : 0;
+        const int off = (st - a.n_sub_main) * SUB + c;      // < 128 <= w_cap
+        const bool ok = seq_ok && u0 + off < N;
+        int32_t slot = slot0 + off;                          // (u0 + off) mod w_cap
+        slot = slot >= a.w_cap ? slot - a.w_cap : slot;
+        const int64_t row = ok ? (win_base + slot) * D : 0;
         const uint4 k0 = *reinterpret_cast<const uint4*>(a.wk + row + 32 * g);
         const uint4 k1 = *reinterpret_cast<const uint4*>(a.wk + row + 32 * g + 16);
         w.r[0] = k0.x; w.r[1] = k0.y; w.r[2] = k0.z; w.r[3] = k0.w;
@@ -463,8 +500,12 @@ __global__ void __launch_bounds__(AT_THREADS, 3) attn_stream_kernel(StreamArgs a
     float4_t o[8];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) o[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
-    _Float16* vt = sh.vt[wave];
+    _Float16* vt = sh.st.vt[wave];
 
+    // v_perm selector gathering V scale bytes g/2, g/2 + 2, g/2 + 4, g/2 + 6 of
+    // the record's 8-byte V scale block (dwords r[10], r[11])
+    const uint32_t gh = (uint32_t)(g >> 1);
+    const uint32_t vsel = gh | ((2u + gh) << 8) | ((4u + gh) << 16) | ((6u + gh) << 24);
     int st = t_begin + wave;
     Raw cur, nxt;
     bool ok_cur = false, ok_nxt = false;
@@ -479,34 +520,36 @@ __global__ void __launch_bounds__(AT_THREADS, 3) attn_stream_kernel(StreamArgs a
         half4_t kf[8];
         uint32_t vv[16];                      // f16x2: channels 8g+32k+2i, +1 in vv[4k+i]
         if (is_main) {
-            const uint32_t sk = ((g >> 1) ? cur.r[9] : cur.r[8]) >> (16 * (g & 1));   // K scales 2g, 2g+1
-            const half2_t k0 = scale_h2(sk & 0xff), k1 = scale_h2((sk >> 8) & 0xff);
+            // K scales of groups 2g, 2g+1 (adjacent bytes); V scales of groups
+            // 2k + g/2, k = 0..3 (bytes g/2, g/2 + 2, ... of the V scale block)
+            const half2_t ks2 =
+                fp8x2_h2<false>(((g >> 1) ? cur.r[9] : cur.r[8]) >> (16 * (g & 1)));
+            const uint32_t vsb = __builtin_amdgcn_perm(cur.r[11], cur.r[10], vsel);
+            const half2_t vs01 = fp8x2_h2<false>(vsb), vs23 = fp8x2_h2<true>(vsb);
+            const half2_t k0 = half2_t{ks2.x, ks2.x}, k1 = half2_t{ks2.y, ks2.y};
+            const half2_t vsc[4] = {half2_t{vs01.x, vs01.x}, half2_t{vs01.y, vs01.y},
+                                    half2_t{vs23.x, vs23.x}, half2_t{vs23.y, vs23.y}};
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 uint32_t w4[4];
-                fp4x8_to_f16x2(cur.r[i], i < 2 ? k0 : k1, w4);
+                fp4x8_scaled(cur.r[i], i < 2 ? k0 : k1, w4);
                 kf[2 * i] = __builtin_bit_cast(half4_t, make_uint2(w4[0], w4[1]));
                 kf[2 * i + 1] = __builtin_bit_cast(half4_t, make_uint2(w4[2], w4[3]));
             }
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                // V group of channels 8g+32k.. is 2k + g/2: scale byte 8 + 2k + g/2,
-                // i.e. byte 2(k&1) + g/2 of scale dword 10 + k/2
-                const uint32_t code =
-                    (cur.r[10 + (k >> 1)] >> (8 * (2 * (k & 1) + (g >> 1)))) & 0xff;
-                fp4x8_to_f16x2(cur.r[4 + k], scale_h2(code), vv + 4 * k);
-            }
+            for (int k = 0; k < 4; ++k) fp4x8_scaled(cur.r[4 + k], vsc[k], vv + 4 * k);
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                uint32_t w2[2];
-                fp8x4_to_f16x4(cur.r[i], w2);
-                kf[i] = __builtin_bit_cast(half4_t, make_uint2(w2[0], w2[1]));
-            }
+            for (int i = 0; i < 8; ++i)
+                kf[i] = __builtin_bit_cast(
+                    half4_t, make_uint2(__builtin_bit_cast(uint32_t, fp8x2_h2<false>(cur.r[i])),
+                                        __builtin_bit_cast(uint32_t, fp8x2_h2<true>(cur.r[i]))));
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
-                fp8x4_to_f16x4(cur.r[8 + 2 * k], vv + 4 * k);
-                fp8x4_to_f16x4(cur.r[9 + 2 * k], vv + 4 * k + 2);
+                vv[4 * k] = __builtin_bit_cast(uint32_t, fp8x2_h2<false>(cur.r[8 + 2 * k]));
+                vv[4 * k + 1] = __builtin_bit_cast(uint32_t, fp8x2_h2<true>(cur.r[8 + 2 * k]));
+                vv[4 * k + 2] = __builtin_bit_cast(uint32_t, fp8x2_h2<false>(cur.r[9 + 2 * k]));
+                vv[4 * k + 3] = __builtin_bit_cast(uint32_t, fp8x2_h2<true>(cur.r[9 + 2 * k]));
             }
         }
         if (!ok_cur) {
@@ -543,10 +586,14 @@ __global__ void __launch_bounds__(AT_THREADS, 3) attn_stream_kernel(StreamArgs a
         float4_t sacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
-            sacc = __builtin_amdgcn_mfma_f32_16x16x16f16(kf[ks], qhi[ks], sacc, 0, 0, 0);
-            sacc = __builtin_amdgcn_mfma_f32_16x16x16f16(kf[ks], qlo[ks], sacc, 0, 0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_16x16x16f16(kf[ks], sh.st.q[0][ks][lane], sacc, 0,
+                                                         0, 0);
+            sacc = __builtin_amdgcn_mfma_f32_16x16x16f16(kf[ks], sh.st.q[1][ks][lane], sacc, 0,
+                                                         0, 0);
         }
-        const float lscale = a.sm_scale * (is_main ? 1.0f : a.wk_scale);
+        // logits in log2 units (log2(e) folded into the scale): exp2 is one
+        // v_exp_f32; m_run is kept in the same units
+        const float lscale = a.sm_scale * LOG2E * (is_main ? 1.0f : a.wk_scale);
         float sv[4];
         float tmax = NEG_INF;
 #pragma unroll
@@ -558,13 +605,14 @@ __global__ void __launch_bounds__(AT_THREADS, 3) attn_stream_kernel(StreamArgs a
         tmax = fmaxf(tmax, swz_xor16(tmax));
         tmax = fmaxf(tmax, xor32_f32(tmax));
         const float m_new = fmaxf(m_run, tmax);
-        const float alpha = m_run == NEG_INF ? 0.0f : expf(m_run - m_new);
+        const bool grew = m_new > m_run;
+        const float alpha = m_run == NEG_INF ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
         const float vsc = is_main ? 1.0f : a.wv_scale;
         half4_t phi, plo;
         float psum = 0.0f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const float p = sv[r] == NEG_INF ? 0.0f : expf(sv[r] - m_new);
+            const float p = sv[r] == NEG_INF ? 0.0f : __builtin_amdgcn_exp2f(sv[r] - m_new);
             psum += p;
             const float pv = p * vsc;
             const _Float16 h = (_Float16)pv;
@@ -573,12 +621,16 @@ __global__ void __launch_bounds__(AT_THREADS, 3) attn_stream_kernel(StreamArgs a
         }
         l_run = l_run * alpha + psum;
         m_run = m_new;
-        // ---- O^T = O^T * alpha + V^T P^T
+        // ---- O^T = O^T * alpha + V^T P^T; alpha is exactly 1 for a head whose
+        // running max did not move, so the rescale is skipped when none moved
+        if (__ballot(grew)) {
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) o[mt] *= alpha;
+        }
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
             const half4_t vf =
                 *reinterpret_cast<const half4_t*>(&vt[(16 * mt + c) * VT_STRIDE + 4 * g]);
-            o[mt] *= alpha;
             o[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, phi, o[mt], 0, 0, 0);
             o[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, plo, o[mt], 0, 0, 0);
         }
@@ -611,7 +663,7 @@ __global__ void __launch_bounds__(AT_THREADS, 3) attn_stream_kernel(StreamArgs a
         if (M != NEG_INF) {
 #pragma unroll
             for (int w = 0; w < AT_WAVES; ++w) {
-                const float wt = mw[w] == NEG_INF ? 0.0f : expf(mw[w] - M);
+                const float wt = mw[w] == NEG_INF ? 0.0f : __builtin_amdgcn_exp2f(mw[w] - M);
                 L += wt * sh.mg.l[w][h];
                 const float4* src = reinterpret_cast<const float4*>(&sh.mg.o[w][h * D + d0]);
                 const float4 x0 = src[0], x1 = src[1];
@@ -627,7 +679,7 @@ __global__ void __launch_bounds__(AT_THREADS, 3) attn_stream_kernel(StreamArgs a
         } else {
             float* part = a.part + ((int64_t)b * a.n_split + split) * ATTN_PART_FLOATS;
             if ((t & 15) == 0) {
-                part[h] = M;
+                part[h] = M * LN2;           // partials carry natural-log maxima
                 part[HEADS + h] = L;
             }
             float4* dst = reinterpret_cast<float4*>(part + 2 * HEADS + h * D + d0);
@@ -749,8 +801,8 @@ hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
     a.sm_scale = sm_scale;
     a.n_sub_main = (topk + SUB - 1) / SUB;
     a.n_sub = a.n_sub_main + WINDOW / SUB;
-    // about one workgroup per resident slot (256 CUs x 3), at least one step per wave
-    int32_t split = (768 + B - 1) / B;
+    // about one workgroup per resident slot (256 CUs x 4), at least one step per wave
+    int32_t split = (1024 + B - 1) / B;
     const int32_t max_split = (a.n_sub + AT_WAVES - 1) / AT_WAVES;
     a.n_split = split < 1 ? 1 : (split > max_split ? max_split : split);
     hipLaunchKernelGGL(attn_stream_kernel, dim3(a.n_split, B), dim3(AT_THREADS), 0, stream, a);
