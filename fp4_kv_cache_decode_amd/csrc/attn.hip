@@ -54,7 +54,9 @@ typedef float float4_t __attribute__((ext_vector_type(4)));
 constexpr int AT_THREADS = 256;
 constexpr int AT_WAVES = AT_THREADS / 64;
 constexpr int SUB = 16;                   // entries per wave step
-constexpr int VT_STRIDE = 20;             // f16 per transposed V row (16 entries + 4 pad)
+constexpr int32_t STREAM_WG_TARGET = 1024;  // stream workgroups to aim for per launch
+constexpr int VT_STRIDE = 24;             // f16 per transposed V row (16 entries + 8 pad):
+                                          // conflict-free packed writes and operand reads
 constexpr float NEG_INF = -__builtin_huge_valf();
 // tile kernel (small batches): used while B x tiles fits one wave of workgroups
 constexpr int64_t TILE_KERNEL_MAX_WG = 768;
@@ -433,28 +435,6 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
     const int main_end = t_end < a.n_sub_main ? t_end : a.n_sub_main;
     const int32_t* idx_row = a.idx + (int64_t)b * a.topk;
 
-    // ---- query fragments (B operand of S^T = K Q^T): Q[h = c][32g + 4ks + j],
-    // split into f16 hi + lo.  Every wave uses the same fragments; wave 0 builds
-    // them once into LDS (in lane order, so the per-step reads are conflict
-    // free) instead of each wave holding 32 VGPRs of them.
-    if (wave == 0) {
-        const float* qrow = a.q + ((int64_t)b * HEADS + c) * D + 32 * g;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const float4 v = *reinterpret_cast<const float4*>(qrow + 4 * ks);
-            const float x[4] = {v.x, v.y, v.z, v.w};
-            half4_t hi4, lo4;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const _Float16 hi = (_Float16)x[i];
-                hi4[i] = hi;
-                lo4[i] = (_Float16)(x[i] - (float)hi);
-            }
-            sh.st.q[0][ks][lane] = hi4;
-            sh.st.q[1][ks][lane] = lo4;
-        }
-    }
-    __syncthreads();
 
     auto load_idx = [&](int st) -> int32_t {
         const int j = SUB * st + c;
@@ -502,11 +482,18 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
     for (int mt = 0; mt < 8; ++mt) o[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
     _Float16* vt = sh.st.vt[wave];
 
+    // packed V^T writes: byte selector (even lane: own low half, then the
+    // neighbour's low half; odd lane: the neighbour's high half, then its own)
+    // and the lane's offset inside the tile
+    const uint32_t pair_sel = (c & 1) ? 0x03020706u : 0x05040100u;
+    const int vt_w = (c & 1) ? VT_STRIDE + (c - 1) : c;
     // v_perm selector gathering V scale bytes g/2, g/2 + 2, g/2 + 4, g/2 + 6 of
     // the record's 8-byte V scale block (dwords r[10], r[11])
     const uint32_t gh = (uint32_t)(g >> 1);
     const uint32_t vsel = gh | ((2u + gh) << 8) | ((4u + gh) << 16) | ((6u + gh) << 24);
     int st = t_begin + wave;
+    // two steps in flight: while step i is computed, step i+1 is arriving and
+    // step i+2 is issued (its index list entries were loaded one step earlier)
     Raw cur, nxt;
     bool ok_cur = false, ok_nxt = false;
     int32_t idx_next = -1;
@@ -514,6 +501,29 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
         ok_cur = fetch(st, load_idx(st), cur);
         idx_next = load_idx(st + AT_WAVES);
     }
+    // ---- query fragments (B operand of S^T = K Q^T): Q[h = c][32g + 4ks + j],
+    // split into f16 hi + lo; built after the first steps' loads were issued,
+    // so the two latencies overlap.  Every wave uses the same fragments; wave 0 builds
+    // them once into LDS (in lane order, so the per-step reads are conflict
+    // free) instead of each wave holding 32 VGPRs of them.
+    if (wave == 0) {
+        const float* qrow = a.q + ((int64_t)b * HEADS + c) * D + 32 * g;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+            const float4 v = *reinterpret_cast<const float4*>(qrow + 4 * ks);
+            const float x[4] = {v.x, v.y, v.z, v.w};
+            half4_t hi4, lo4;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const _Float16 hi = (_Float16)x[i];
+                hi4[i] = hi;
+                lo4[i] = (_Float16)(x[i] - (float)hi);
+            }
+            sh.st.q[0][ks][lane] = hi4;
+            sh.st.q[1][ks][lane] = lo4;
+        }
+    }
+    __syncthreads();
     for (; st < t_end; st += AT_WAVES) {
         const bool is_main = st < a.n_sub_main;
         // ---- dequantise this step: K into A-operand fragments, V into LDS (V^T)
@@ -560,21 +570,26 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
         }
         const uint64_t vmask = __ballot(ok_cur);     // bit e (e < 16): entry e valid
         {
-            unsigned short* vts = reinterpret_cast<unsigned short*>(vt);
+            // lanes c and c^1 swap halves so that each writes one dword of two
+            // entries: the even lane (V[c][d], V[c+1][d]) into row d, the odd
+            // lane (V[c-1][d+1], V[c][d+1]) into row d+1
 #pragma unroll
             for (int k = 0; k < 4; ++k)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
+                    const uint32_t x = vv[4 * k + i];
+                    const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, DPP_XOR1, 0xf, 0xf,
+                                                                          false);
                     const int d = 8 * g + 32 * k + 2 * i;
-                    vts[d * VT_STRIDE + c] = (unsigned short)(vv[4 * k + i] & 0xffffu);
-                    vts[(d + 1) * VT_STRIDE + c] = (unsigned short)(vv[4 * k + i] >> 16);
+                    *reinterpret_cast<uint32_t*>(vt + vt_w + d * VT_STRIDE) =
+                        __builtin_amdgcn_perm(y, x, pair_sel);
                 }
         }
         // the V^T tile is private to this wave and LDS executes a wave's
         // operations in order; this only keeps the compiler from moving the
         // tile's reads above its writes
         asm volatile("" ::: "memory");
-        // ---- the next step's loads go out now and overlap the MFMA work below
+        // ---- step i+2's loads go out now and overlap the MFMA work below
         const int sn = st + AT_WAVES;
         if (sn < t_end) {
             ok_nxt = fetch(sn, idx_next, nxt);
@@ -802,7 +817,7 @@ hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
     a.n_sub_main = (topk + SUB - 1) / SUB;
     a.n_sub = a.n_sub_main + WINDOW / SUB;
     // about one workgroup per resident slot (256 CUs x 4), at least one step per wave
-    int32_t split = (1024 + B - 1) / B;
+    int32_t split = (STREAM_WG_TARGET + B - 1) / B;
     const int32_t max_split = (a.n_sub + AT_WAVES - 1) / AT_WAVES;
     a.n_split = split < 1 ? 1 : (split > max_split ? max_split : split);
     hipLaunchKernelGGL(attn_stream_kernel, dim3(a.n_split, B), dim3(AT_THREADS), 0, stream, a);
