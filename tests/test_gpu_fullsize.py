@@ -2,9 +2,10 @@
 benchmark times.
 
 * decoder20_1m_b4: 4 sequences x 1,048,576 positions, the 20-layer pattern
-  [Full + 3 Reuse] + 4 x [Reindex + 3 Reuse].  Every output of the step is
-  checked: block maxima, pool, the Full and Reindex index sets, and all 20
-  layers' attention outputs.
+  [Full + 3 Reuse] + 4 x [Reindex + 3 Reuse]; group_64k_b32: 32 x 65,536,
+  Full + 3 Reuse; hier_256k_b8: 8 x 262,144, Full + Reindex + 3 Reuse.  Every
+  output of the step is checked: block maxima, pool, the Full and Reindex index
+  sets, and every layer's attention output.
 * prefill_8k_over_128k: 8,192 causal queries over a 131,072-position prefix
   plus the chunk itself (seq = 0 for all, ctx_i = 131,073 + i).  The GPU runs all
   8,192 queries in one call per stage; the oracle checks a strided sample.
@@ -56,11 +57,12 @@ def _check_block_maxima(gM, sc, N):
     return float(err.max())
 
 
-def test_decoder20_1m_b4_step(K):
-    wl = G.WORKLOADS["decoder20_1m_b4"]
+@pytest.mark.parametrize("name", ["decoder20_1m_b4", "group_64k_b32", "hier_256k_b8"])
+def test_decode_step_full_size(K, name):
+    wl = G.WORKLOADS[name]
     B, N, L = wl.B, wl.N, len(wl.layers)
     seed = 0
-    _say(f"decoder20_1m_b4: building caches B={B} N={N} L={L}")
+    _say(f"{name}: building caches B={B} N={N} L={L}")
     t0 = time.time()
     oc = O.Cache(wl.n_seq, wl.cap, L, wl.w_cap)
     gc = K.Cache(wl.n_seq, wl.cap, L, wl.w_cap)
