@@ -77,6 +77,7 @@ struct Shared {
     uint32_t wave_u[NT / 64];
     float wave_f[2][NT / 64];
     uint32_t misc[8];        // [0,1] digit search, [2] candidates, [3] flag, [4] valid count
+    int32_t pool[NT == BIG_T ? CSA2_MAX_POOL : 1];   // the row's pool (pool mode), in LDS
 };
 
 __device__ __forceinline__ int64_t row_length(const TopkArgs& a, int b) {
@@ -100,14 +101,74 @@ __device__ __forceinline__ bool seg_plan(int64_t n, int32_t k, int32_t* quota) {
 
 // ------------------------------------------------------------ block collectives
 
+// Wave collectives on DPP and v_readlane only (no LDS round trips, which a
+// chain of shuffles would cost one after another).
+// Inclusive prefix sum over the 64 lanes: Hillis-Steele inside each 16-lane
+// row (row_shr 1, 2, 4, 8), then row_bcast:15 and row_bcast:31 carry the row
+// totals into the rows above.
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);
+    return v;
+}
+
+// The four 16-lane rows reduced inside the row by DPP, then combined from
+// lanes 0, 16, 32, 48 with v_readlane; the result is wave-uniform.
+__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, DPP_XOR1, 0xf, 0xf, false);
+    v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, DPP_XOR2, 0xf, 0xf, false);
+    v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, DPP_ROR4, 0xf, 0xf, false);
+    v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, DPP_ROR8, 0xf, 0xf, false);
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, 0) + (uint32_t)__builtin_amdgcn_readlane((int)v, 16) +
+           (uint32_t)__builtin_amdgcn_readlane((int)v, 32) + (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+}
+__device__ __forceinline__ float rows_min(float v) {
+    auto rl = [](float x, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l)); };
+    v = fminf(v, dpp_f32<DPP_XOR1>(v));
+    v = fminf(v, dpp_f32<DPP_XOR2>(v));
+    v = fminf(v, dpp_f32<DPP_ROR4>(v));
+    v = fminf(v, dpp_f32<DPP_ROR8>(v));
+    return fminf(fminf(rl(v, 0), rl(v, 16)), fminf(rl(v, 32), rl(v, 48)));
+}
+__device__ __forceinline__ float rows_max(float v) {
+    auto rl = [](float x, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l)); };
+    v = fmaxf(v, dpp_f32<DPP_XOR1>(v));
+    v = fmaxf(v, dpp_f32<DPP_XOR2>(v));
+    v = fmaxf(v, dpp_f32<DPP_ROR4>(v));
+    v = fmaxf(v, dpp_f32<DPP_ROR8>(v));
+    return fmaxf(fmaxf(rl(v, 0), rl(v, 16)), fmaxf(rl(v, 32), rl(v, 48)));
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)v, CTRL, 0xf, 0xf, false);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_mov_dpp((int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
+    uint64_t o;
+    o = dpp_u64<DPP_XOR1>(v); v = o < v ? o : v;
+    o = dpp_u64<DPP_XOR2>(v); v = o < v ? o : v;
+    o = dpp_u64<DPP_ROR4>(v); v = o < v ? o : v;
+    o = dpp_u64<DPP_ROR8>(v); v = o < v ? o : v;
+    uint64_t m = ~0ull;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const uint64_t x = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 16 * r) << 32) |
+                           (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, 16 * r);
+        m = x < m ? x : m;
+    }
+    return m;
+}
+
 template <int NT>
 __device__ uint32_t block_incl_scan(uint32_t v, Shared<NT>& sh, uint32_t* total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        uint32_t t = __shfl_up(v, d);
-        if (lane >= d) v += t;
-    }
+    v = wave_incl_scan(v);
     if (lane == 63) sh.wave_u[wave] = v;
     __syncthreads();
     uint32_t before = 0, all = 0;
@@ -127,10 +188,9 @@ template <int NT>
 __device__ void block_stats(uint32_t cnt, float lo, float hi, Shared<NT>& sh, uint32_t* total,
                             float* mn, float* mx) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    lo = wave_min(lo);
-    hi = wave_max(hi);
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) cnt += __shfl_xor(cnt, d);
+    lo = rows_min(lo);
+    hi = rows_max(hi);
+    cnt = wave_sum_u32(cnt);
     if (lane == 0) {
         sh.wave_f[0][wave] = lo;
         sh.wave_f[1][wave] = hi;
@@ -314,8 +374,7 @@ __device__ bool select_core(Shared<NT>& sh, const float (&v)[VPT], const uint32_
 
 // Ordered compaction of the chosen bits into out[0..k), ascending, -1 padded.
 template <int NT>
-__device__ void write_bitmap(Shared<NT>& sh, int words, const int32_t* pool, int32_t* out,
-                             int32_t k) {
+__device__ void write_bitmap(Shared<NT>& sh, int words, bool use_pool, int32_t* out, int32_t k) {
     const int t = threadIdx.x;
     const int wpt = (words + NT - 1) / NT;
     uint32_t c = 0;
@@ -333,7 +392,7 @@ __device__ void write_bitmap(Shared<NT>& sh, int words, const int32_t* pool, int
             const int bit = __ffs(bits) - 1;
             bits &= bits - 1;
             const int32_t i = wi * 32 + bit;
-            if (pos < (uint32_t)k) out[pos] = pool ? pool[i >> 3] * BLOCK + (i & 7) : i;
+            if (pos < (uint32_t)k) out[pos] = use_pool ? sh.pool[i >> 3] * BLOCK + (i & 7) : i;
             ++pos;
         }
     }
@@ -517,6 +576,10 @@ __global__ void __launch_bounds__(BIG_T) topk_small_kernel(TopkArgs a) {
         topk_fallback(sh, row, n, a.k, pool, out);
         return;
     }
+    // the pool is needed only to name the chosen entries; its load overlaps
+    // the values' (select_core synchronises before anything reads it)
+    if (pool)
+        for (int i = threadIdx.x; i < a.n_blocks; i += BIG_T) sh.pool[i] = pool[i];
     float v[VPT];
     uint32_t id[VPT];
     load_values<BIG_T>(row, 0, n, v, id);
@@ -525,7 +588,7 @@ __global__ void __launch_bounds__(BIG_T) topk_small_kernel(TopkArgs a) {
         topk_fallback(sh, row, n, a.k, pool, out);
         return;
     }
-    write_bitmap<BIG_T>(sh, words, pool, out, a.k);
+    write_bitmap<BIG_T>(sh, words, pool != nullptr, out, a.k);
 }
 
 // Stage 1 of long rows: exact top-quota of segment g of row b, written densely
@@ -581,17 +644,8 @@ __global__ void __launch_bounds__(SEG_T) topk_seg_kernel(TopkArgs a) {
             worst = key < worst ? key : worst;
         }
     }
-    uint32_t hi32 = (uint32_t)(worst >> 32), lo32 = (uint32_t)worst;
-#pragma unroll
-    for (int d = 32; d > 0; d >>= 1) {
-        const uint32_t h2 = __shfl_xor(hi32, d), l2 = __shfl_xor(lo32, d);
-        const uint64_t o = ((uint64_t)h2 << 32) | l2;
-        const uint64_t me = ((uint64_t)hi32 << 32) | lo32;
-        const uint64_t mn = o < me ? o : me;
-        hi32 = (uint32_t)(mn >> 32);
-        lo32 = (uint32_t)mn;
-    }
-    if ((t & 63) == 0) wmin[t >> 6] = ((uint64_t)hi32 << 32) | lo32;
+    worst = wave_min_u64(worst);
+    if ((t & 63) == 0) wmin[t >> 6] = worst;
     __syncthreads();
     if (t == 0) {
         uint64_t mn = wmin[0];
@@ -619,6 +673,8 @@ __global__ void __launch_bounds__(BIG_T) topk_merge_kernel(TopkArgs a) {
         topk_fallback(sh, row, n, a.k, pool, out);
         return;
     }
+    if (pool)
+        for (int i = t; i < a.n_blocks; i += BIG_T) sh.pool[i] = pool[i];
     float v[VPT];
     uint32_t id[VPT];
     const uint32_t* meta = a.seg_meta + (int64_t)b * a.n_seg * 2;
@@ -655,7 +711,7 @@ __global__ void __launch_bounds__(BIG_T) topk_merge_kernel(TopkArgs a) {
         topk_fallback(sh, row, n, a.k, pool, out);
         return;
     }
-    write_bitmap<BIG_T>(sh, words, pool, out, a.k);
+    write_bitmap<BIG_T>(sh, words, pool != nullptr, out, a.k);
 }
 
 }  // namespace
