@@ -43,9 +43,21 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def code_hash(text: str) -> str:
+    """First 16 hex digits of the SHA-256 of a C++ source's code: // comments,
+    trailing blanks and empty lines removed, so that editing a comment does not
+    retire counters taken on the same code."""
+    lines = []
+    for line in text.splitlines():
+        line = re.sub(r"//.*$", "", line).rstrip()
+        if line:
+            lines.append(line)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
+
+
 def source_hash(path=SCORE_SRC) -> str:
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    with open(path, encoding="utf-8") as f:
+        return code_hash(f.read())
 
 
 def counter_traffic(workload: str):
