@@ -364,7 +364,7 @@ def row_gather(args):
            "window": G.WINDOW, "rotations": R, "dtype": "fp32"}
     roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
             "frac": gbs / PEAK_HBM_GBS, "traffic": None,
-            "kernel": "attn_kernel + attn_merge_kernel (csa2_decode_attn)", "avg_us": ms * 1e3,
+            "kernel": "attn_stream_kernel (csa2_decode_attn)", "avg_us": ms * 1e3,
             "alg_bytes": alg}
     return _common(args, "CSA2 gather/dequant/attention queries/s", B / (ms * 1e-3), "queries/s",
                    ms, cfg, roof)

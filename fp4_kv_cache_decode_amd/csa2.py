@@ -239,6 +239,6 @@ def decode_attn(cache: Cache, layer: int, q, idx, seq, ctx, out, ws, sm_scale=No
 def alloc_workspace(op: int, B: int, max_ctx: int = 0, n_blocks: int = 2048, topk: int = 512,
                     device="cuda") -> torch.Tensor:
     n = workspace_bytes(op, B, max_ctx, n_blocks, BLOCK, topk)
-    if n == 0 and B > 0 and op != OP_SELECT_POOL:      # selection may need none
+    if n == 0 and B > 0 and op not in (OP_SELECT_POOL, OP_DECODE_ATTN):   # these may need none
         raise Csa2Error(ERR_INVALID_ARG, "csa2_workspace_bytes")
     return torch.empty(max(n, 1), dtype=torch.uint8, device=device)

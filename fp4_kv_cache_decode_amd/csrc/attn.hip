@@ -763,12 +763,38 @@ __global__ void __launch_bounds__(AT_THREADS) attn_merge_kernel(const float* par
 
 }  // namespace
 
+namespace {
+
+// Launch shape of one call: the tile kernel while B x tiles fits one wave of
+// workgroups, else the stream kernel with about one workgroup per resident slot
+// (256 CUs x 4) and at least one step per wave.
+struct AttnPlan {
+    bool tile;
+    int32_t n_split;         // workgroups (partial records) per query
+};
+
+AttnPlan attn_plan(int32_t B, int32_t topk) {
+    const int32_t n_tiles = (topk + TILE - 1) / TILE + WINDOW / TILE;
+    if ((int64_t)B * n_tiles <= TILE_KERNEL_MAX_WG) return {true, n_tiles};
+    const int32_t n_sub = (topk + SUB - 1) / SUB + WINDOW / SUB;
+    const int32_t max_split = (n_sub + AT_WAVES - 1) / AT_WAVES;
+    const int32_t split = (STREAM_WG_TARGET + B - 1) / B;
+    return {false, split < 1 ? 1 : (split > max_split ? max_split : split)};
+}
+
+}  // namespace
+
+int64_t attn_partials(int32_t B, int32_t topk) {
+    const AttnPlan p = attn_plan(B, topk);
+    return p.n_split > 1 ? (int64_t)B * p.n_split : 0;
+}
+
 hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
                        const float* q, const int32_t* idx, const int32_t* seq,
                        const int64_t* ctx, int32_t B, int32_t topk, float sm_scale,
                        float* out, float* partials, hipStream_t stream) {
-    const int32_t n_tiles = attn_tiles(topk);
-    if ((int64_t)B * n_tiles <= TILE_KERNEL_MAX_WG) {
+    const AttnPlan p = attn_plan(B, topk);
+    if (p.tile) {
         // few queries: one workgroup per 64-entry tile, the shortest dependency chain
         TileArgs a{};
         a.kv = c.kv;
@@ -785,15 +811,15 @@ hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
         a.layer = layer;
         a.topk = topk;
         a.n_main = (topk + TILE - 1) / TILE;
-        a.n_tiles = n_tiles;
+        a.n_tiles = p.n_split;
         a.wk_scale = w.k_scale;
         a.wv_scale = w.v_scale;
         a.sm_scale = sm_scale;
-        hipLaunchKernelGGL(attn_tile_kernel, dim3(n_tiles, B), dim3(AT_THREADS), 0, stream, a);
+        hipLaunchKernelGGL(attn_tile_kernel, dim3(a.n_tiles, B), dim3(AT_THREADS), 0, stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(attn_merge_kernel, dim3(B), dim3(AT_THREADS), 0, stream, partials,
-                           n_tiles, out);
+                           a.n_tiles, out);
         return hipGetLastError();
     }
     StreamArgs a{};
@@ -816,10 +842,7 @@ hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
     a.sm_scale = sm_scale;
     a.n_sub_main = (topk + SUB - 1) / SUB;
     a.n_sub = a.n_sub_main + WINDOW / SUB;
-    // about one workgroup per resident slot (256 CUs x 4), at least one step per wave
-    int32_t split = (STREAM_WG_TARGET + B - 1) / B;
-    const int32_t max_split = (a.n_sub + AT_WAVES - 1) / AT_WAVES;
-    a.n_split = split < 1 ? 1 : (split > max_split ? max_split : split);
+    a.n_split = p.n_split;
     hipLaunchKernelGGL(attn_stream_kernel, dim3(a.n_split, B), dim3(AT_THREADS), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_split == 1) return e;

@@ -48,8 +48,7 @@ size_t reindex_bytes(int32_t B, int32_t n_blocks) {
 }
 
 size_t attn_bytes(int32_t B, int32_t topk) {
-    return align_up((size_t)B * (size_t)csa2::attn_tiles(topk) * csa2::ATTN_PART_FLOATS *
-                    sizeof(float));
+    return align_up((size_t)csa2::attn_partials(B, topk) * csa2::ATTN_PART_FLOATS * sizeof(float));
 }
 
 csa2_status check_cache(const csa2_cache* c, bool need_kv, bool need_idxk) {
@@ -234,7 +233,8 @@ csa2_status csa2_decode_attn(const csa2_cache* cache, const csa2_window* win, in
         return CSA2_ERR_INVALID_ARG;
     if (topk < 1 || topk > CSA2_MAX_TOPK || B > 65535) return CSA2_ERR_UNSUPPORTED;
     if (B == 0) return CSA2_OK;
-    if (!ws || ws_bytes < attn_bytes(B, topk)) return CSA2_ERR_WORKSPACE;
+    const size_t need = attn_bytes(B, topk);
+    if (need > 0 && (!ws || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
     return launched(csa2::launch_attn(*cache, *win, layer, q, idx, seq, ctx, B, topk, sm_scale,
                                       out, static_cast<float*>(ws), stream));
 }

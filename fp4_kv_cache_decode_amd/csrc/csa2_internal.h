@@ -45,8 +45,8 @@ hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
                        const int64_t* ctx, int32_t B, int32_t topk, float sm_scale,
                        float* out, float* partials, hipStream_t stream);
 
-// Number of 64-entry tiles of an attention call (main tiles + 2 window tiles).
-inline int32_t attn_tiles(int32_t topk) { return (topk + 63) / 64 + 2; }
+// Partial records an attention call writes (0 when no query is split).
+int64_t attn_partials(int32_t B, int32_t topk);
 constexpr size_t ATTN_PART_FLOATS = 16 + 16 + 16 * 128;
 
 }  // namespace csa2

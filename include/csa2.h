@@ -211,7 +211,9 @@ csa2_status csa2_index_select_pool(const float* M, int64_t m_stride, const int64
  *   q         [B][16][128] fp32, |q| < 65504.
  *   idx       [B][topk] int32 positions (< ctx[b]) or -1.
  *   out       [B][16][128] fp32.  A query with no valid entry gets zeros.
- *   ws        at least csa2_workspace_bytes(CSA2_OP_DECODE_ATTN, B, 0, 0, 0, topk).
+ *   ws        at least csa2_workspace_bytes(CSA2_OP_DECODE_ATTN, B, 0, 0, 0, topk)
+ *             bytes: the split queries' partial results.  That is zero when no
+ *             query is split (B >= 1024); ws may then be NULL.
  */
 csa2_status csa2_decode_attn(const csa2_cache* cache, const csa2_window* win, int32_t layer,
                              const float* q, const int32_t* idx, const int32_t* seq,

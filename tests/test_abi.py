@@ -52,7 +52,11 @@ def test_workspace_sizes(L):
     assert full >= 4 * 131072 * 4 + 4 * 2048 * 4 + 4 * 16384 * 4
     assert full % 256 == 0
     assert K.workspace_bytes(K.OP_INDEX_REINDEX, 4, 0, 2048, 8, 512) == 4 * 16384 * 4
-    assert K.workspace_bytes(K.OP_DECODE_ATTN, 4, 0, 0, 0, 512) >= 4 * 10 * (32 + 2048) * 4
+    # attention: one partial record (m, l, O: 32 + 2048 floats) per split of a query
+    part = (32 + 2048) * 4
+    assert K.workspace_bytes(K.OP_DECODE_ATTN, 4, 0, 0, 0, 512) == 4 * 10 * part     # 10 tiles
+    assert K.workspace_bytes(K.OP_DECODE_ATTN, 96, 0, 0, 0, 512) == 96 * 10 * part   # stream
+    assert K.workspace_bytes(K.OP_DECODE_ATTN, 1024, 0, 0, 0, 512) == 0             # unsplit
     assert K.workspace_bytes(K.OP_INDEX_FULL, 4, 1 << 20, 2048, 4, 512) == 0      # block != 8
     assert K.workspace_bytes(K.OP_INDEX_FULL, 4, 1 << 20, 8192, 8, 512) == 0      # pool too big
     assert K.workspace_bytes(K.OP_DECODE_ATTN, 4, 0, 0, 0, 4096) == 0             # topk too big

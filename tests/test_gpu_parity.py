@@ -395,25 +395,30 @@ def test_index_full_equals_its_stages(K):
 
 
 def test_attention_workspace_reuse_across_shapes(K):
-    """One zeroed attention workspace serves calls of different B and topk in a
-    row: each call leaves the arrival counters at zero for the next."""
+    """One attention workspace, sized for the largest call, serves calls of
+    different B and topk in a row on both kernels (tile kernel for few queries,
+    split stream kernel at B = 80 and 96)."""
     _say("attention workspace reuse")
     N, L = 3000, 2
     oc = O.Cache(3, N, L)
     gc = K.Cache(3, N, L)
     fill_both(17, 3, N, L, oc, gc)
-    ws = K.alloc_workspace(K.OP_DECODE_ATTN, 3, topk=1024)
+    cases = [(3, 512, 0), (1, 512, 1), (96, 512, 1), (2, 200, 0), (3, 1024, 1), (80, 1024, 0),
+             (3, 512, 1)]
+    nbytes = max(K.workspace_bytes(K.OP_DECODE_ATTN, B, 0, 0, 0, topk) for B, topk, _ in cases)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     qi, wi = G.index_queries(17, 0, 3)
-    seq = np.arange(3, dtype=np.int32)
-    ctx = np.array([N, N - 100, 700], np.int64)
-    _, idx512, _, _ = oc.index_full(qi, wi, seq, ctx)
-    for B, topk, layer in [(3, 512, 0), (1, 512, 1), (2, 200, 0), (3, 1024, 1), (3, 512, 1)]:
+    ctx3 = np.array([N, N - 100, 700], np.int64)
+    _, idx512, _, _ = oc.index_full(qi, wi, np.arange(3, dtype=np.int32), ctx3)
+    for B, topk, layer in cases:
+        seq = (np.arange(B) % 3).astype(np.int32)
+        ctx = ctx3[seq]
         idx = np.full((B, topk), -1, np.int32)
         m = min(topk, 512)
-        idx[:, :m] = idx512[:B, :m]
+        idx[:, :m] = idx512[seq, :m]
         q = G.attn_queries(17, layer + 10 * B, B)
         out = torch.empty((B, 16, 128), dtype=torch.float32, device="cuda")
-        K.decode_attn(gc, layer, dev(q), dev(idx), dev(seq[:B]), dev(ctx[:B]), out, ws)
+        K.decode_attn(gc, layer, dev(q), dev(idx), dev(seq), dev(ctx), out, ws)
         torch.cuda.synchronize()
-        want = oc.decode_attn(layer, q, idx, seq[:B], ctx[:B])
+        want = oc.decode_attn(layer, q, idx, seq, ctx)
         assert np.max(np.abs(out.cpu().numpy() - want)) <= 1e-4, (B, topk, layer)
