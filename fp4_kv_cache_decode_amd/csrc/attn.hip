@@ -704,33 +704,28 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
     }
 }
 
-// Combine the tiles of each query: out = sum_t e^(m_t - M) o_t / sum_t e^(m_t - M) l_t.
-// Each thread owns 8 output dims of one head; it loads the partials of up to
-// MERGE_BATCH tiles at once (one memory round trip for the default 10 tiles).
-constexpr int MERGE_BATCH = 12;     // tiles whose loads are in flight together
+// Combine the partials of each query: out = sum_t e^(m_t - M) o_t / sum_t e^(m_t - M) l_t.
+// One workgroup per (head, query) and one thread per output dim, so the partial
+// loads spread over B x 16 compute units; each thread loads its dim of up to
+// MERGE_BATCH partials at once (one memory round trip for the 10 tiles of top-512).
+constexpr int MERGE_BATCH = 12;
 
-__global__ void __launch_bounds__(AT_THREADS) attn_merge_kernel(const float* part, int32_t n_tiles,
-                                                                 float* out) {
-    const int b = blockIdx.x;
-    const int t = threadIdx.x;
-    const int h = t >> 4;                 // 16 threads per head
-    const int d0 = (t & 15) * 8;          // 8 dims each
-    const float* pb = part + (int64_t)b * n_tiles * ATTN_PART_FLOATS;
-    float M = NEG_INF, L = 0.0f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    // groups of MERGE_BATCH tiles: every load of a group is issued before use,
-    // and M / L / acc are rescaled online when a group raises the max
-    for (int i0 = 0; i0 < n_tiles; i0 += MERGE_BATCH) {
-        float m[MERGE_BATCH], l[MERGE_BATCH];
-        float4 o[MERGE_BATCH][2];
+__global__ void __launch_bounds__(D) attn_merge_kernel(const float* part, int32_t n_parts,
+                                                       float* out) {
+    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    const float* pb = part + (int64_t)b * n_parts * ATTN_PART_FLOATS;
+    float M = NEG_INF, L = 0.0f, acc = 0.0f;
+    // groups of MERGE_BATCH partials: every load of a group is issued before
+    // use, and M / L / acc are rescaled online when a group raises the max
+    for (int i0 = 0; i0 < n_parts; i0 += MERGE_BATCH) {
+        float m[MERGE_BATCH], l[MERGE_BATCH], o[MERGE_BATCH];
 #pragma unroll
         for (int u = 0; u < MERGE_BATCH; ++u) {
-            const int i = i0 + u < n_tiles ? i0 + u : n_tiles - 1;
+            const int i = i0 + u < n_parts ? i0 + u : n_parts - 1;
             const float* pt = pb + (int64_t)i * ATTN_PART_FLOATS;
-            m[u] = i0 + u < n_tiles ? pt[h] : NEG_INF;
+            m[u] = i0 + u < n_parts ? pt[h] : NEG_INF;
             l[u] = pt[HEADS + h];
-            const float4* po = reinterpret_cast<const float4*>(pt + 2 * HEADS + h * D + d0);
-            o[u][0] = po[0];
-            o[u][1] = po[1];
+            o[u] = pt[2 * HEADS + h * D + d];
         }
         float Mn = M;
 #pragma unroll
@@ -738,27 +733,16 @@ __global__ void __launch_bounds__(AT_THREADS) attn_merge_kernel(const float* par
         if (Mn == NEG_INF) continue;
         const float c = M == NEG_INF ? 0.0f : expf(M - Mn);
         L *= c;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[j] *= c;
+        acc *= c;
 #pragma unroll
         for (int u = 0; u < MERGE_BATCH; ++u) {
             const float wgt = m[u] == NEG_INF ? 0.0f : expf(m[u] - Mn);
             L += wgt * l[u];
-            acc[0] += wgt * o[u][0].x;
-            acc[1] += wgt * o[u][0].y;
-            acc[2] += wgt * o[u][0].z;
-            acc[3] += wgt * o[u][0].w;
-            acc[4] += wgt * o[u][1].x;
-            acc[5] += wgt * o[u][1].y;
-            acc[6] += wgt * o[u][1].z;
-            acc[7] += wgt * o[u][1].w;
+            acc += wgt * o[u];
         }
         M = Mn;
     }
-    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
-    float4* o = reinterpret_cast<float4*>(out + ((int64_t)b * HEADS + h) * D + d0);
-    o[0] = make_float4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
-    o[1] = make_float4(acc[4] * inv, acc[5] * inv, acc[6] * inv, acc[7] * inv);
+    out[((int64_t)b * HEADS + h) * D + d] = L > 0.0f ? acc * (1.0f / L) : 0.0f;
 }
 
 }  // namespace
@@ -818,7 +802,7 @@ hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
         hipLaunchKernelGGL(attn_tile_kernel, dim3(a.n_tiles, B), dim3(AT_THREADS), 0, stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(attn_merge_kernel, dim3(B), dim3(AT_THREADS), 0, stream, partials,
+        hipLaunchKernelGGL(attn_merge_kernel, dim3(HEADS, B), dim3(D), 0, stream, partials,
                            a.n_tiles, out);
         return hipGetLastError();
     }
@@ -846,7 +830,7 @@ hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
     hipLaunchKernelGGL(attn_stream_kernel, dim3(a.n_split, B), dim3(AT_THREADS), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_split == 1) return e;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(B), dim3(AT_THREADS), 0, stream, partials,
+    hipLaunchKernelGGL(attn_merge_kernel, dim3(HEADS, B), dim3(D), 0, stream, partials,
                        a.n_split, out);
     return hipGetLastError();
 }

@@ -7,7 +7,7 @@
 // Reindex layer (origotech.dev deep dive "Inside DeepSeek V4.1-Flash", section
 // "How the architecture shrinks the KV cache").
 //
-// Select core (one workgroup, values held in registers, 16 per thread):
+// Select core (one workgroup of 1,024 threads, 16 values per thread in registers):
 //   1. min / max / count of the valid values (block reduction);
 //   2. an LDS histogram over 2,048 bins linear in value between min and max
 //      (a monotone map, so ranks survive; linear bins keep LDS atomics spread
@@ -18,14 +18,19 @@
 //      asc) order; larger lists take an 11/11/10-bit radix on the exact order
 //      keys for the threshold key T and how many keys equal to T to take, and an
 //      ordered popcount scan over an "equal" bitmap keeps the lowest-index ones.
-// The choice lives in an LDS bitmap over indices; an ordered popcount scan of
-// the bitmap writes ascending indices.
+// Thread t holds the 16 consecutive positions 16t .. 16t+15, so its share of
+// the choice is a 16-bit register mask and one block scan of the masks'
+// popcounts places the chosen indices in ascending order.  Every instruction
+// of this core is issued by 16 waves on one CU's 4 SIMDs, so it is written for
+// few instructions per value: a single-barrier block reduction, no atomics on
+// the chosen path, one coalesced store.
 //
 // Rows of up to 16,384 entries: one workgroup, one read of the row.
 // Longer rows (up to 131,072): a segment kernel takes the exact top-q of each
-// 4,096-entry segment (q >= 4x a segment's expected share of the top-k); a
-// merge kernel selects the top-k of the union and checks that no segment's
-// worst reported entry was chosen (else that segment might hide more winners).
+// 4,096-entry segment (q >= 4x a segment's expected share of the top-k) and
+// writes it densely in ascending index order; a merge kernel selects the top-k
+// of those slots (slot order is index order) and checks that no segment's worst
+// reported entry was chosen (else that segment might hide more winners).
 // Rows that fail the check, overflow the candidate list (heavy ties), or are
 // longer than 131,072 entries take an exact fallback: three radix sweeps over
 // the row in global memory, an ordered collection and a bitonic sort.
@@ -43,7 +48,7 @@ constexpr int SEG_T = 256;               // threads: segment kernel
 constexpr int SMALL_MAX = BIG_T * VPT;   // 16,384
 constexpr int SEG = SEG_T * VPT;         // 4,096
 constexpr int FAST_MAX_N = 131072;
-constexpr int BM_WORDS = FAST_MAX_N / 32;
+constexpr int STAGE_WORDS = CSA2_MAX_POOL > SMALL_MAX / 32 ? CSA2_MAX_POOL : SMALL_MAX / 32;
 constexpr int CAND_CAP = 4096;
 constexpr int RANK_MAX = 256;            // candidate sets ranked directly
 constexpr int UNROLL = 8;
@@ -70,8 +75,8 @@ struct TopkArgs {
 template <int NT>
 struct Shared {
     uint32_t hist[4096];
-    uint32_t sel_bits[NT == BIG_T ? BM_WORDS : SEG / 32];
-    uint32_t eq_bits[NT == BIG_T ? BM_WORDS : SEG / 32];
+    uint32_t sel_bits[NT == BIG_T ? SMALL_MAX / 32 : SEG / 32];
+    uint32_t eq_bits[NT == BIG_T ? STAGE_WORDS : SEG / 32];   // also the output staging
     uint32_t ckey[CAND_CAP];
     uint32_t cidx[CAND_CAP];
     uint32_t wave_u[NT / 64];
@@ -183,10 +188,15 @@ __device__ uint32_t block_incl_scan(uint32_t v, Shared<NT>& sh, uint32_t* total)
     return v + before;
 }
 
-// Block-wide count, min and max in one LDS round.
+// Block-wide count, min and max in one LDS round: each wave reduces its own
+// values, then lanes 0 .. NT/64 - 1 of every wave read the waves' partials and
+// a 16-lane DPP reduction leaves the block's result in every lane.  The partial
+// arrays are next written after at least one more barrier (every caller's next
+// phase ends in one before any wave_u / wave_f write).
 template <int NT>
 __device__ void block_stats(uint32_t cnt, float lo, float hi, Shared<NT>& sh, uint32_t* total,
                             float* mn, float* mx) {
+    static_assert(NT / 64 <= 16, "one 16-lane row holds every wave's partial");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     lo = rows_min(lo);
     hi = rows_max(hi);
@@ -197,18 +207,25 @@ __device__ void block_stats(uint32_t cnt, float lo, float hi, Shared<NT>& sh, ui
         sh.wave_u[wave] = cnt;
     }
     __syncthreads();
-    float a = sh.wave_f[0][0], c = sh.wave_f[1][0];
-    uint32_t n = sh.wave_u[0];
-#pragma unroll
-    for (int i = 1; i < NT / 64; ++i) {
-        a = fminf(a, sh.wave_f[0][i]);
-        c = fmaxf(c, sh.wave_f[1][i]);
-        n += sh.wave_u[i];
-    }
-    __syncthreads();
-    *mn = a;
-    *mx = c;
-    *total = n;
+    const bool mine = lane < NT / 64;
+    float a = mine ? sh.wave_f[0][lane] : __builtin_huge_valf();
+    float c = mine ? sh.wave_f[1][lane] : NEG_INF;
+    uint32_t n = mine ? sh.wave_u[lane] : 0u;
+    a = fminf(a, dpp_f32<DPP_XOR1>(a));
+    a = fminf(a, dpp_f32<DPP_XOR2>(a));
+    a = fminf(a, dpp_f32<DPP_ROR4>(a));
+    a = fminf(a, dpp_f32<DPP_ROR8>(a));
+    c = fmaxf(c, dpp_f32<DPP_XOR1>(c));
+    c = fmaxf(c, dpp_f32<DPP_XOR2>(c));
+    c = fmaxf(c, dpp_f32<DPP_ROR4>(c));
+    c = fmaxf(c, dpp_f32<DPP_ROR8>(c));
+    n += (uint32_t)__builtin_amdgcn_mov_dpp((int)n, DPP_XOR1, 0xf, 0xf, false);
+    n += (uint32_t)__builtin_amdgcn_mov_dpp((int)n, DPP_XOR2, 0xf, 0xf, false);
+    n += (uint32_t)__builtin_amdgcn_mov_dpp((int)n, DPP_ROR4, 0xf, 0xf, false);
+    n += (uint32_t)__builtin_amdgcn_mov_dpp((int)n, DPP_ROR8, 0xf, 0xf, false);
+    *mn = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a)));
+    *mx = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(c)));
+    *total = (uint32_t)__builtin_amdgcn_readfirstlane((int)n);
 }
 
 // Digit d of hist[0..nbins) with count(> d) < kk <= count(>= d); returns d and
@@ -240,6 +257,9 @@ __device__ void find_digit(Shared<NT>& sh, uint32_t kk, int nbins) {
 
 // ------------------------------------------------------------ select core
 
+template <int NT>
+__device__ bool resolve_candidates(Shared<NT>& sh, uint32_t kk, int words);
+
 // Chooses the k best of the block's register-held values (v, id), -inf absent,
 // ties to the lower id.  Marks the choice in sh.sel_bits, bit (id - id_base),
 // over `words` bitmap words; leaves the number of valid values in misc[4].
@@ -262,7 +282,7 @@ __device__ bool select_core(Shared<NT>& sh, const float (&v)[VPT], const uint32_
         const bool ok = v[j] != NEG_INF;
         cnt += ok ? 1u : 0u;
         lo = ok ? fminf(lo, v[j]) : lo;
-        hi = ok ? fmaxf(hi, v[j]) : hi;
+        hi = fmaxf(hi, v[j]);               // -inf never raises the max
     }
     uint32_t n_valid;
     float vmin, vmax;
@@ -305,6 +325,16 @@ __device__ bool select_core(Shared<NT>& sh, const float (&v)[VPT], const uint32_
         }
     }
     __syncthreads();
+    return resolve_candidates<NT>(sh, kk, words);
+}
+
+// Chooses kk of the m = misc[2] candidates of the threshold bin (order keys in
+// ckey, bitmap positions in cidx) in (value desc, index asc) order and sets
+// their bits in sh.sel_bits.  Expects eq_bits[0, words) zero.  Returns false if
+// the candidate list overflowed.  Ends with a barrier.
+template <int NT>
+__device__ bool resolve_candidates(Shared<NT>& sh, uint32_t kk, int words) {
+    const int t = threadIdx.x;
     const uint32_t m = sh.misc[2];
     if (m > (uint32_t)CAND_CAP) return false;
     if (m <= (uint32_t)RANK_MAX) {
@@ -370,33 +400,6 @@ __device__ bool select_core(Shared<NT>& sh, const float (&v)[VPT], const uint32_
     }
     __syncthreads();
     return true;
-}
-
-// Ordered compaction of the chosen bits into out[0..k), ascending, -1 padded.
-template <int NT>
-__device__ void write_bitmap(Shared<NT>& sh, int words, bool use_pool, int32_t* out, int32_t k) {
-    const int t = threadIdx.x;
-    const int wpt = (words + NT - 1) / NT;
-    uint32_t c = 0;
-    for (int j = 0; j < wpt; ++j) {
-        const int wi = t * wpt + j;
-        c += wi < words ? __popc(sh.sel_bits[wi]) : 0u;
-    }
-    uint32_t total;
-    uint32_t pos = block_incl_scan<NT>(c, sh, &total) - c;
-    for (int j = 0; j < wpt; ++j) {
-        const int wi = t * wpt + j;
-        if (wi >= words) break;
-        uint32_t bits = sh.sel_bits[wi];
-        while (bits) {
-            const int bit = __ffs(bits) - 1;
-            bits &= bits - 1;
-            const int32_t i = wi * 32 + bit;
-            if (pos < (uint32_t)k) out[pos] = use_pool ? sh.pool[i >> 3] * BLOCK + (i & 7) : i;
-            ++pos;
-        }
-    }
-    for (int j = (int)total + t; j < k; j += NT) out[j] = -1;
 }
 
 // ------------------------------------------------------------ exact fallback
@@ -564,10 +567,145 @@ __device__ __forceinline__ void load_values(const float* row, int64_t base, int6
     }
 }
 
+// Selection over up to SMALL_MAX positions with thread t owning positions
+// 16t .. 16t+15 (values in registers, -inf absent).  Its share of the choice is
+// then a 16-bit register mask, and because positions are in output order the
+// ascending output is one block scan of the masks' popcounts: on the common
+// path no bitmap and no atomics besides the histogram's.  The steps are those
+// of select_core: count / min / max, the value-linear histogram and the bin d
+// of the k-th value, positions above d chosen, bin d's positions resolved as
+// candidates (returned through sel_bits).  id_of(j) is the output value of
+// position 16t + j; veto(j) (for chosen positions) may reject the whole choice.
+// Writes out[0, k) ascending with -1 padding and returns true, or returns false
+// (nothing written) when the candidate list overflowed or a veto fired.
+// STATIC_J visits the chosen positions with compile-time j (for id_of / veto
+// that index register arrays, which a runtime j would move to scratch).
+template <bool STATIC_J, typename IdOf, typename Veto>
+__device__ bool select16(Shared<BIG_T>& sh, const float (&v)[VPT], int64_t n_pos, uint32_t k,
+                         int32_t* out, IdOf id_of, Veto veto) {
+    const int t = threadIdx.x;
+    const int words = (int)((n_pos + 31) >> 5);
+    for (int i = t; i < NB; i += BIG_T) sh.hist[i] = 0;
+    if (t < words) {
+        sh.sel_bits[t] = 0;
+        sh.eq_bits[t] = 0;
+    }
+    if (t == 0) {
+        sh.misc[2] = 0;
+        sh.misc[3] = 0;
+    }
+
+    // ---- count / min / max of the valid values
+    float lo = __builtin_huge_valf(), hi = NEG_INF;
+    uint32_t cnt = 0;
+#pragma unroll
+    for (int j = 0; j < VPT; ++j) {
+        const bool ok = v[j] != NEG_INF;
+        cnt += ok ? 1u : 0u;
+        lo = fminf(lo, ok ? v[j] : __builtin_huge_valf());
+        hi = fmaxf(hi, v[j]);
+    }
+    uint32_t n_valid;
+    float vmin, vmax;
+    block_stats<BIG_T>(cnt, lo, hi, sh, &n_valid, &vmin, &vmax);
+
+    uint32_t mask = 0;                   // bit j: position 16t + j chosen
+    if (n_valid <= k) {
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) mask |= v[j] != NEG_INF ? 1u << j : 0u;
+        __syncthreads();                 // block_stats' partials read before the scan reuses them
+    } else {
+        // ---- histogram and the bin d holding the k-th largest value
+        float inv = vmax > vmin ? (float)NB / (vmax - vmin) : 0.0f;
+        if (!(inv < __builtin_huge_valf())) inv = 0.0f;     // range overflowed: one bin
+        uint32_t bin[VPT];
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            const int bb = (int)((v[j] - vmin) * inv);
+            bin[j] = v[j] == NEG_INF ? 0xffffffffu : (uint32_t)(bb < NB - 1 ? bb : NB - 1);
+            if (bin[j] != 0xffffffffu) atomicAdd(&sh.hist[bin[j]], 1u);
+        }
+        __syncthreads();
+        find_digit<BIG_T>(sh, k, NB);
+        const uint32_t d = sh.misc[0];
+        const uint32_t kk = k - sh.misc[1];
+        __syncthreads();
+        // ---- above d: chosen; in d: candidates
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            if (bin[j] != 0xffffffffu && bin[j] > d) {
+                mask |= 1u << j;
+            } else if (bin[j] == d) {
+                const uint32_t slot = atomicAdd(&sh.misc[2], 1u);
+                if (slot < (uint32_t)CAND_CAP) {
+                    sh.ckey[slot] = order_key(v[j]);
+                    sh.cidx[slot] = (uint32_t)(VPT * t + j);
+                }
+            }
+        }
+        __syncthreads();
+        if (!resolve_candidates<BIG_T>(sh, kk, words)) return false;
+        mask |= (sh.sel_bits[t >> 1] >> (16 * (t & 1))) & 0xffffu;
+    }
+
+    // ---- veto, then ranks from a block scan (its barriers also publish the
+    // veto flag), staged in LDS (k <= 4096 entries fit eq_bits), then one
+    // coalesced store with -1 padding
+    if (STATIC_J) {
+        bool vetoed = false;
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) vetoed |= ((mask >> j) & 1u) && veto(j);
+        if (vetoed) sh.misc[3] = 1;
+    } else {
+        for (uint32_t m = mask; m; m &= m - 1)
+            if (veto(__ffs(m) - 1)) sh.misc[3] = 1;
+    }
+    const uint32_t c = (uint32_t)__popc(mask);
+    uint32_t total;
+    uint32_t pos = block_incl_scan<BIG_T>(c, sh, &total) - c;
+    if (sh.misc[3]) return false;
+    int32_t* stage = reinterpret_cast<int32_t*>(sh.eq_bits);
+    if (STATIC_J) {
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) {
+            if ((mask >> j) & 1u) {
+                if (pos < k) stage[pos] = id_of(j);
+                ++pos;
+            }
+        }
+    } else {
+        while (mask) {
+            const int j = __ffs(mask) - 1;
+            mask &= mask - 1;
+            if (pos < k) stage[pos] = id_of(j);
+            ++pos;
+        }
+    }
+    __syncthreads();
+    for (int j = t; j < (int)k; j += BIG_T) out[j] = j < (int)total ? stage[j] : -1;
+    return true;
+}
+
+// Entries 16t .. 16t+15 of a row of n entries as four float4 loads; entries
+// past the end read as -inf (their loads stay in bounds).
+__device__ __forceinline__ void load_run16(const float* row, int64_t n, float (&v)[VPT]) {
+    const float4* v4 = reinterpret_cast<const float4*>(row);
+#pragma unroll
+    for (int r = 0; r < VPT / 4; ++r) {
+        const int64_t e0 = (int64_t)VPT * threadIdx.x + 4 * r;
+        const float4 x = v4[(e0 < n ? e0 : 0) >> 2];
+        v[4 * r] = e0 < n ? x.x : NEG_INF;
+        v[4 * r + 1] = e0 + 1 < n ? x.y : NEG_INF;
+        v[4 * r + 2] = e0 + 2 < n ? x.z : NEG_INF;
+        v[4 * r + 3] = e0 + 3 < n ? x.w : NEG_INF;
+    }
+}
+
 // Rows of up to SMALL_MAX entries (longer rows: the exact fallback).
 __global__ void __launch_bounds__(BIG_T) topk_small_kernel(TopkArgs a) {
     __shared__ Shared<BIG_T> sh;
     const int b = blockIdx.x;
+    const int t = threadIdx.x;
     const int64_t n = row_length(a, b);
     const float* row = a.vals + (int64_t)b * a.stride;
     int32_t* out = a.out + (int64_t)b * a.k;
@@ -576,19 +714,19 @@ __global__ void __launch_bounds__(BIG_T) topk_small_kernel(TopkArgs a) {
         topk_fallback(sh, row, n, a.k, pool, out);
         return;
     }
-    // the pool is needed only to name the chosen entries; its load overlaps
-    // the values' (select_core synchronises before anything reads it)
-    if (pool)
-        for (int i = threadIdx.x; i < a.n_blocks; i += BIG_T) sh.pool[i] = pool[i];
+    // entries 16t .. 16t+15; in pool mode they lie in pool blocks 2t and 2t + 1
     float v[VPT];
-    uint32_t id[VPT];
-    load_values<BIG_T>(row, 0, n, v, id);
-    const int words = (int)((n + 31) >> 5);
-    if (!select_core<BIG_T>(sh, v, id, (uint32_t)a.k, 0, words)) {
-        topk_fallback(sh, row, n, a.k, pool, out);
-        return;
+    load_run16(row, n, v);
+    int32_t pb[2] = {0, 0};
+    if (pool) {
+        pb[0] = 2 * t < a.n_blocks ? pool[2 * t] : 0;
+        pb[1] = 2 * t + 1 < a.n_blocks ? pool[2 * t + 1] : 0;
     }
-    write_bitmap<BIG_T>(sh, words, pool != nullptr, out, a.k);
+    const bool done = select16<false>(
+        sh, v, n, (uint32_t)a.k, out,
+        [&](int j) -> int32_t { return pool ? pb[j >> 3] * BLOCK + (j & 7) : VPT * t + j; },
+        [](int) { return false; });
+    if (!done) topk_fallback(sh, row, n, a.k, pool, out);
 }
 
 // Stage 1 of long rows: exact top-quota of segment g of row b, written densely
@@ -658,7 +796,12 @@ __global__ void __launch_bounds__(SEG_T) topk_seg_kernel(TopkArgs a) {
 }
 
 // Stage 2 of long rows: top-k of the union of the segments' choices, checked.
-// Rows the segment kernel skipped are selected here directly.
+// The dense candidate area lists segment 0's choices, then segment 1's, ...,
+// each in ascending index order, so slot order is output order and the
+// selection runs on slots (select16) with the slots' indices as output.  A full
+// segment whose worst reported entry is chosen may hide winners: that vetoes
+// the choice and the row takes the exact fallback.  Rows the segment kernel
+// skipped are selected here directly.
 __global__ void __launch_bounds__(BIG_T) topk_merge_kernel(TopkArgs a) {
     __shared__ Shared<BIG_T> sh;
     const int b = blockIdx.x;
@@ -673,46 +816,82 @@ __global__ void __launch_bounds__(BIG_T) topk_merge_kernel(TopkArgs a) {
         topk_fallback(sh, row, n, a.k, pool, out);
         return;
     }
-    if (pool)
-        for (int i = t; i < a.n_blocks; i += BIG_T) sh.pool[i] = pool[i];
     float v[VPT];
     uint32_t id[VPT];
-    const uint32_t* meta = a.seg_meta + (int64_t)b * a.n_seg * 2;
-    const int n_seg = (int)((n + SEG - 1) / SEG);
+    // this thread's slots 16t .. 16t+15 span at most two segments (quota >= 256)
+    int g0 = 0, g1 = 0;
+    uint2 m0 = make_uint2(0u, 0u), m1 = make_uint2(0u, 0u);
     if (!two_stage) {
-        load_values<BIG_T>(row, 0, n, v, id);
+        load_run16(row, n, v);
+#pragma unroll
+        for (int j = 0; j < VPT; ++j) id[j] = (uint32_t)(VPT * t + j);
     } else {
-        const float* sv = a.seg_val + (int64_t)b * SMALL_MAX;
-        const uint32_t* si = a.seg_id + (int64_t)b * SMALL_MAX;
+        const float4* sv = reinterpret_cast<const float4*>(a.seg_val + (int64_t)b * SMALL_MAX);
+        const uint4* si = reinterpret_cast<const uint4*>(a.seg_id + (int64_t)b * SMALL_MAX);
+#pragma unroll
+        for (int r = 0; r < VPT / 4; ++r) {
+            const float4 x = sv[4 * t + r];
+            const uint4 y = si[4 * t + r];
+            v[4 * r] = x.x; v[4 * r + 1] = x.y; v[4 * r + 2] = x.z; v[4 * r + 3] = x.w;
+            id[4 * r] = y.x; id[4 * r + 1] = y.y; id[4 * r + 2] = y.z; id[4 * r + 3] = y.w;
+        }
+        // segment of a slot: the quotient of a float reciprocal, exact after
+        // one correction (slots < 2^14, quota <= 4096)
+        const float inv_q = 1.0f / (float)quota;
+        auto seg_of = [&](int e) {
+            int g = (int)((float)e * inv_q);
+            const int r = e - g * quota;
+            return r < 0 ? g - 1 : (r >= quota ? g + 1 : g);
+        };
+        const int n_seg = (int)((n + SEG - 1) / SEG);
+        g0 = seg_of(VPT * t);
+        g1 = seg_of(VPT * t + VPT - 1);
+        const uint32_t* meta = a.seg_meta + (int64_t)b * a.n_seg * 2;
+        if (g0 < n_seg) m0 = *reinterpret_cast<const uint2*>(meta + 2 * g0);
+        if (g1 < n_seg) m1 = *reinterpret_cast<const uint2*>(meta + 2 * g1);
+    }
+    // the pool goes to LDS for the output's lookups; its loads were issued
+    // with the values', and select16 orders these writes before any read
+    int32_t pv[CSA2_MAX_POOL / BIG_T];
+#pragma unroll
+    for (int r = 0; r < CSA2_MAX_POOL / BIG_T; ++r)
+        pv[r] = pool && t + BIG_T * r < a.n_blocks ? pool[t + BIG_T * r] : 0;
+    if (two_stage) {
+        // slots past a segment's reported count hold stale data: absent
+        const int g1_start = g1 * quota;
 #pragma unroll
         for (int j = 0; j < VPT; ++j) {
-            const int e = t + BIG_T * j;           // dense slot, < SMALL_MAX
-            const int g = e / quota, r = e % quota;
-            const bool ok = g < n_seg && (uint32_t)r < (meta[2 * g] & 0x7fffffffu);
-            v[j] = ok ? sv[e] : NEG_INF;
-            id[j] = ok ? si[e] : 0u;
+            const int e = VPT * t + j;
+            const bool hi_seg = e >= g1_start;
+            const uint32_t c = (hi_seg ? m1.x : m0.x) & 0x7fffffffu;
+            const int r = e - (hi_seg ? g1_start : g0 * quota);
+            v[j] = (uint32_t)r < c ? v[j] : NEG_INF;
         }
     }
-    const int words = (int)((n + 31) >> 5);
-    bool good = select_core<BIG_T>(sh, v, id, (uint32_t)a.k, 0, words);
-    if (good && two_stage) {
-        // a full segment whose worst reported entry was chosen may hide winners
-        if (t == 0) sh.misc[3] = 0;
-        __syncthreads();
-        for (int g = t; g < n_seg; g += BIG_T) {
-            const uint32_t m0 = meta[2 * g], worst = meta[2 * g + 1];
-            if ((m0 & 0x80000000u) && ((sh.sel_bits[worst >> 5] >> (worst & 31)) & 1u))
-                sh.misc[3] = 1;
-        }
-        __syncthreads();
-        good = sh.misc[3] == 0;
+    if (pool) {
+#pragma unroll
+        for (int r = 0; r < CSA2_MAX_POOL / BIG_T; ++r)
+            if (t + BIG_T * r < a.n_blocks) sh.pool[t + BIG_T * r] = pv[r];
     }
-    if (!good) {
-        topk_fallback(sh, row, n, a.k, pool, out);
-        return;
-    }
-    write_bitmap<BIG_T>(sh, words, pool != nullptr, out, a.k);
+    const int64_t n_pos = two_stage ? (int64_t)SMALL_MAX : n;
+    const int g1_start = g1 * quota;
+    const bool done = select16<true>(
+        sh, v, n_pos, (uint32_t)a.k, out,
+        [&](int j) -> int32_t {
+            const int32_t i = (int32_t)id[j];
+            return pool ? sh.pool[i >> 3] * BLOCK + (i & 7) : i;
+        },
+        [&](int j) -> bool {
+            if (!two_stage) return false;
+            const uint2 m = VPT * t + j >= g1_start ? m1 : m0;
+            return (m.x & 0x80000000u) && id[j] == m.y;
+        });
+    if (!done) topk_fallback(sh, row, n, a.k, pool, out);
 }
+
+static_assert(CSA2_MAX_POOL % BIG_T == 0, "pool entries per thread");
+static_assert(CSA2_MAX_POOL <= STAGE_WORDS && CSA2_MAX_TOPK <= STAGE_WORDS,
+              "select16 stages up to k outputs in eq_bits");
 
 }  // namespace
 
