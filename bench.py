@@ -152,6 +152,9 @@ class Setup:
         self.ws_ri = K.alloc_workspace(K.OP_INDEX_REINDEX, B)
         self.ws_sel = K.alloc_workspace(K.OP_SELECT_POOL, B, N)
         self.ws_at = K.alloc_workspace(K.OP_DECODE_ATTN, B)
+        # the group's gathered main records: stored by its Full / Reindex layer,
+        # read by its Reuse layers
+        self.kvg = torch.empty((B, G.TOPK, K.RECORD), dtype=torch.uint8, device="cuda")
 
     # A step is three parts: the quantise-on-write of the new token, the Full
     # layer's scan over the whole context (the dominant kernel, timed with HIP
@@ -175,8 +178,9 @@ class Setup:
             elif mode == "I":
                 qi, wi = self.dqi[l]
                 K.index_reindex(c, qi, wi, self.seq, self.ctx, self.pool, self.idx, self.ws_ri)
+            gather = dict(kvg_in=self.kvg) if mode == "R" else dict(kvg_out=self.kvg)
             K.decode_attn(c, l, self.dq[l], self.idx, self.seq, self.ctx, self.out[l],
-                          self.ws_at)
+                          self.ws_at, **gather)
 
     def capture(self):
         """HIP graphs of part_quant and part_rest for every replica."""

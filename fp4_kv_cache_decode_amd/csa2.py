@@ -62,13 +62,17 @@ def lib():
         L.csa2_decode_attn.argtypes = [C.POINTER(csa2_cache), C.POINTER(csa2_window), C.c_int32,
                                        _P, _P, _P, _P, C.c_int32, C.c_int32, C.c_float, _P, _P,
                                        C.c_size_t, _P]
+        L.csa2_decode_attn_ex.argtypes = [C.POINTER(csa2_cache), C.POINTER(csa2_window),
+                                          C.c_int32, _P, _P, _P, _P, C.c_int32, C.c_int32,
+                                          C.c_float, _P, _P, _P, _P, C.c_size_t, _P]
         L.csa2_workspace_bytes.argtypes = [C.c_int32, C.c_int32, C.c_int64, C.c_int32, C.c_int32,
                                            C.c_int32]
         L.csa2_workspace_bytes.restype = C.c_size_t
         L.csa2_status_string.argtypes = [C.c_int]
         L.csa2_status_string.restype = C.c_char_p
         for f in ("csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex",
-                  "csa2_decode_attn", "csa2_index_block_scores", "csa2_index_select_pool"):
+                  "csa2_decode_attn", "csa2_decode_attn_ex", "csa2_index_block_scores",
+                  "csa2_index_select_pool"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -220,7 +224,9 @@ def index_reindex(cache: Cache, q_idx, w, seq, ctx, pool, idx, ws, block: int = 
 
 
 def decode_attn(cache: Cache, layer: int, q, idx, seq, ctx, out, ws, sm_scale=None,
-                stream=None) -> None:
+                stream=None, kvg_in=None, kvg_out=None) -> None:
+    """csa2_decode_attn; with kvg_out / kvg_in ([B][topk][144] uint8) it is
+    csa2_decode_attn_ex, storing / reading the group's gathered main records."""
     B, topk = idx.shape
     _need(q, torch.float32, (B, HEADS, D), "q")
     _need(idx, torch.int32, (B, topk), "idx")
@@ -228,12 +234,23 @@ def decode_attn(cache: Cache, layer: int, q, idx, seq, ctx, out, ws, sm_scale=No
     _need(ctx, torch.int64, (B,), "ctx")
     _need(out, torch.float32, (B, HEADS, D), "out")
     _need(ws, torch.uint8, None, "ws")
+    for name, g in (("kvg_in", kvg_in), ("kvg_out", kvg_out)):
+        if g is not None:
+            _need(g, torch.uint8, (B, topk, RECORD), name)
     if sm_scale is None:
         sm_scale = float(torch.tensor(D ** -0.5, dtype=torch.float32))
-    st = lib().csa2_decode_attn(C.byref(cache.c), C.byref(cache.w), layer, _ptr(q), _ptr(idx),
+    L = lib()
+    if kvg_in is None and kvg_out is None:
+        st = L.csa2_decode_attn(C.byref(cache.c), C.byref(cache.w), layer, _ptr(q), _ptr(idx),
                                 _ptr(seq), _ptr(ctx), B, topk, sm_scale, _ptr(out), _ptr(ws),
                                 ws.numel(), _stream(stream))
-    _check(st, "csa2_decode_attn")
+        _check(st, "csa2_decode_attn")
+        return
+    st = L.csa2_decode_attn_ex(C.byref(cache.c), C.byref(cache.w), layer, _ptr(q), _ptr(idx),
+                               _ptr(seq), _ptr(ctx), B, topk, sm_scale,
+                               _ptr(kvg_in), _ptr(kvg_out), _ptr(out),
+                               _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "csa2_decode_attn_ex")
 
 
 def alloc_workspace(op: int, B: int, max_ctx: int = 0, n_blocks: int = 2048, topk: int = 512,

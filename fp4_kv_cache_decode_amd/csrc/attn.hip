@@ -67,6 +67,8 @@ constexpr int PROW = 72;     // f16 per P row
 
 struct StreamArgs {
     const uint8_t* kv;
+    const uint8_t* kvg_in;   // [B][topk][RECORD] gathered main records, or null
+    uint8_t* kvg_out;        // where to store the gathered main records, or null
     const uint8_t* wk;
     const uint8_t* wv;
     const float* q;
@@ -178,6 +180,8 @@ __device__ __forceinline__ float xor32_f32(float v) {
 
 struct TileArgs {
     const uint8_t* kv;
+    const uint8_t* kvg_in;   // [B][topk][RECORD] gathered main records, or null
+    uint8_t* kvg_out;        // where to store the gathered main records, or null
     const uint8_t* wk;
     const uint8_t* wv;
     const float* q;
@@ -245,12 +249,31 @@ __global__ void __launch_bounds__(AT_THREADS) attn_tile_kernel(TileArgs a) {
         if (is_main) {
             const int j = tile * TILE + e;
             const int32_t pos = (j < a.topk) ? a.idx[(int64_t)b * a.topk + j] : -1;
+            // gathered records sit at known addresses: their loads go out
+            // together with the index load instead of after it
+            const uint8_t* grec =
+                a.kvg_in ? a.kvg_in + ((int64_t)b * a.topk + (j < a.topk ? j : 0)) * RECORD
+                         : nullptr;
+            uint4 kc, vc, sc;
+            if (grec) {
+                kc = *reinterpret_cast<const uint4*>(grec + 16 * q4);
+                vc = *reinterpret_cast<const uint4*>(grec + 64 + 16 * q4);
+                sc = *reinterpret_cast<const uint4*>(grec + 128);
+            }
             ok = seq_ok && pos >= 0 && pos < N;
             if (ok) {
-                const uint8_t* rec = a.kv + ((int64_t)s * a.cap + pos) * RECORD;
-                const uint4 kc = *reinterpret_cast<const uint4*>(rec + 16 * q4);
-                const uint4 vc = *reinterpret_cast<const uint4*>(rec + 64 + 16 * q4);
-                const uint4 sc = *reinterpret_cast<const uint4*>(rec + 128);
+                if (!grec) {
+                    const uint8_t* rec = a.kv + ((int64_t)s * a.cap + pos) * RECORD;
+                    kc = *reinterpret_cast<const uint4*>(rec + 16 * q4);
+                    vc = *reinterpret_cast<const uint4*>(rec + 64 + 16 * q4);
+                    sc = *reinterpret_cast<const uint4*>(rec + 128);
+                }
+                if (a.kvg_out) {
+                    uint8_t* dst = a.kvg_out + ((int64_t)b * a.topk + j) * RECORD;
+                    *reinterpret_cast<uint4*>(dst + 16 * q4) = kc;
+                    *reinterpret_cast<uint4*>(dst + 64 + 16 * q4) = vc;
+                    if (q4 == 0) *reinterpret_cast<uint4*>(dst + 128) = sc;
+                }
                 // K scales are bytes 0..7 of sc, V scales bytes 8..15; this
                 // thread's 32 channels are groups 2*q4 and 2*q4 + 1
                 const uint32_t ks = (q4 < 2 ? sc.x : sc.y) >> (16 * (q4 & 1));
@@ -446,7 +469,10 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
         for (int i = 0; i < 16; ++i) w.r[i] = 0u;
         if (st < a.n_sub_main) {
             const bool ok = seq_ok && pos >= 0 && pos < N;
-            const uint8_t* rec = a.kv + (ok ? ((int64_t)s * a.cap + pos) * RECORD : 0);
+            const int j = SUB * st + c;
+            const uint8_t* rec =
+                a.kvg_in ? a.kvg_in + ((int64_t)b * a.topk + (j < a.topk ? j : 0)) * RECORD
+                         : a.kv + (ok ? ((int64_t)s * a.cap + pos) * RECORD : 0);
             const uint4 kc = *reinterpret_cast<const uint4*>(rec + 16 * g);
             const uint4 sc = *reinterpret_cast<const uint4*>(rec + 128);
             w.r[0] = kc.x; w.r[1] = kc.y; w.r[2] = kc.z; w.r[3] = kc.w;
@@ -529,6 +555,19 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
         // ---- dequantise this step: K into A-operand fragments, V into LDS (V^T)
         half4_t kf[8];
         uint32_t vv[16];                      // f16x2: channels 8g+32k+2i, +1 in vv[4k+i]
+        if (is_main && a.kvg_out && ok_cur) {
+            // this lane's share of the record: K bytes 16g.., V dwords
+            // 64 + 4g + 16k, and (g = 0) the 16 scale bytes
+            uint8_t* dst = a.kvg_out + ((int64_t)b * a.topk + SUB * st + c) * RECORD;
+            *reinterpret_cast<uint4*>(dst + 16 * g) =
+                make_uint4(cur.r[0], cur.r[1], cur.r[2], cur.r[3]);
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                *reinterpret_cast<uint32_t*>(dst + 64 + 4 * g + 16 * k) = cur.r[4 + k];
+            if (g == 0)
+                *reinterpret_cast<uint4*>(dst + 128) =
+                    make_uint4(cur.r[8], cur.r[9], cur.r[10], cur.r[11]);
+        }
         if (is_main) {
             // K scales of groups 2g, 2g+1 (adjacent bytes); V scales of groups
             // 2k + g/2, k = 0..3 (bytes g/2, g/2 + 2, ... of the V scale block)
@@ -776,12 +815,15 @@ int64_t attn_partials(int32_t B, int32_t topk) {
 hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
                        const float* q, const int32_t* idx, const int32_t* seq,
                        const int64_t* ctx, int32_t B, int32_t topk, float sm_scale,
-                       float* out, float* partials, hipStream_t stream) {
+                       const uint8_t* kvg_in, uint8_t* kvg_out, float* out, float* partials,
+                       hipStream_t stream) {
     const AttnPlan p = attn_plan(B, topk);
     if (p.tile) {
         // few queries: one workgroup per 64-entry tile, the shortest dependency chain
         TileArgs a{};
         a.kv = c.kv;
+        a.kvg_in = kvg_in;
+        a.kvg_out = kvg_out;
         a.wk = w.k;
         a.wv = w.v;
         a.q = q;
@@ -808,6 +850,8 @@ hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
     }
     StreamArgs a{};
     a.kv = c.kv;
+    a.kvg_in = kvg_in;
+    a.kvg_out = kvg_out;
     a.wk = w.k;
     a.wv = w.v;
     a.q = q;

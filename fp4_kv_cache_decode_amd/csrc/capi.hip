@@ -220,15 +220,17 @@ csa2_status csa2_index_reindex(const csa2_cache* cache, const float* q_idx, cons
                                       stream));
 }
 
-csa2_status csa2_decode_attn(const csa2_cache* cache, const csa2_window* win, int32_t layer,
-                             const float* q, const int32_t* idx, const int32_t* seq,
-                             const int64_t* ctx, int32_t B, int32_t topk, float sm_scale,
-                             float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+csa2_status csa2_decode_attn_ex(const csa2_cache* cache, const csa2_window* win, int32_t layer,
+                                const float* q, const int32_t* idx, const int32_t* seq,
+                                const int64_t* ctx, int32_t B, int32_t topk, float sm_scale,
+                                const uint8_t* kvg_in, uint8_t* kvg_out, float* out, void* ws,
+                                size_t ws_bytes, hipStream_t stream) {
     csa2_status st = check_cache(cache, true, false);
     if (st != CSA2_OK) return st;
     st = check_window(win, cache);
     if (st != CSA2_OK) return st;
     if (!q || !idx || !seq || !ctx || !out) return CSA2_ERR_INVALID_ARG;
+    if (kvg_in && kvg_out) return CSA2_ERR_INVALID_ARG;
     if (layer < 0 || layer >= win->n_layers || B < 0 || !isfinite(sm_scale))
         return CSA2_ERR_INVALID_ARG;
     if (topk < 1 || topk > CSA2_MAX_TOPK || B > 65535) return CSA2_ERR_UNSUPPORTED;
@@ -236,7 +238,15 @@ csa2_status csa2_decode_attn(const csa2_cache* cache, const csa2_window* win, in
     const size_t need = attn_bytes(B, topk);
     if (need > 0 && (!ws || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
     return launched(csa2::launch_attn(*cache, *win, layer, q, idx, seq, ctx, B, topk, sm_scale,
-                                      out, static_cast<float*>(ws), stream));
+                                      kvg_in, kvg_out, out, static_cast<float*>(ws), stream));
+}
+
+csa2_status csa2_decode_attn(const csa2_cache* cache, const csa2_window* win, int32_t layer,
+                             const float* q, const int32_t* idx, const int32_t* seq,
+                             const int64_t* ctx, int32_t B, int32_t topk, float sm_scale,
+                             float* out, void* ws, size_t ws_bytes, hipStream_t stream) {
+    return csa2_decode_attn_ex(cache, win, layer, q, idx, seq, ctx, B, topk, sm_scale, nullptr,
+                               nullptr, out, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -40,10 +40,13 @@ hipError_t launch_topk(const float* vals, int64_t stride, const int64_t* ctx,
 size_t topk_workspace_bytes(int32_t B, int64_t max_n);
 
 // Split-K gather/dequant attention for one layer plus the cross-split merge.
+// kvg_in (optional): main records read from [B][topk][RECORD] instead of the
+// cache; kvg_out (optional): the main records read are also stored there.
 hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
                        const float* q, const int32_t* idx, const int32_t* seq,
                        const int64_t* ctx, int32_t B, int32_t topk, float sm_scale,
-                       float* out, float* partials, hipStream_t stream);
+                       const uint8_t* kvg_in, uint8_t* kvg_out, float* out, float* partials,
+                       hipStream_t stream);
 
 // Partial records an attention call writes (0 when no query is split).
 int64_t attn_partials(int32_t B, int32_t topk);

@@ -220,6 +220,30 @@ csa2_status csa2_decode_attn(const csa2_cache* cache, const csa2_window* win, in
                              const int64_t* ctx, int32_t B, int32_t topk, float sm_scale,
                              float* out, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * csa2_decode_attn_ex - csa2_decode_attn that keeps the gathered main KV for
+ * the layers that reuse it.
+ * Passage: Reuse layers take both the KV and the top-k indices of their group's
+ * Full or Reindex layer ([P4] mode list; [P5] "CSA2 and the attention
+ * redesign").  The main KV is shared by every layer, so the records gathered
+ * for one layer of a group are the records of all its layers.
+ *   kvg_out   NULL, or a [B][topk][144] device buffer: the call also stores the
+ *             record it reads for entry j of query b (valid entries only) at
+ *             kvg_out[b][j].  Other bytes are left untouched.
+ *   kvg_in    NULL, or a buffer that a kvg_out call with the same cache, idx,
+ *             seq, ctx, B and topk filled: main rows are read from kvg_in[b][j]
+ *             (contiguous, at addresses that do not wait for idx) instead of
+ *             the cache.  idx still decides which entries are valid.
+ *   At most one of kvg_in / kvg_out may be non-NULL (else CSA2_ERR_INVALID_ARG);
+ *   with both NULL this is csa2_decode_attn.  The other arguments and the
+ *   results are those of csa2_decode_attn, bit for bit.
+ */
+csa2_status csa2_decode_attn_ex(const csa2_cache* cache, const csa2_window* win, int32_t layer,
+                                const float* q, const int32_t* idx, const int32_t* seq,
+                                const int64_t* ctx, int32_t B, int32_t topk, float sm_scale,
+                                const uint8_t* kvg_in, uint8_t* kvg_out, float* out, void* ws,
+                                size_t ws_bytes, hipStream_t stream);
+
 /* Workspace bytes an operation needs (0 for unknown op or invalid sizes). */
 size_t csa2_workspace_bytes(int32_t op, int32_t B, int64_t max_ctx, int32_t n_blocks,
                             int32_t block, int32_t topk);

@@ -141,3 +141,12 @@ def test_attn_error_paths(L):
     assert call(sm=float("nan")) == 1
     assert call(wsb=ws - 4) == 3
     assert call(B=0) == 0
+    # the gathered-KV variant: the same checks, and at most one gathered buffer
+    fx = L.csa2_decode_attn_ex
+    call_ex = lambda gin, gout, **kw: fx(C.byref(c), C.byref(w), kw.get("layer", 1), FAKE, FAKE,
+                                         FAKE, FAKE, kw.get("B", 2), 512, 0.088, gin, gout, FAKE,
+                                         FAKE, ws, None)
+    assert call_ex(FAKE, FAKE) == 1
+    assert call_ex(FAKE, None, layer=2) == 1
+    assert call_ex(None, FAKE, B=0) == 0
+    assert call_ex(FAKE, None, B=0) == 0

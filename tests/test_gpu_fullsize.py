@@ -13,7 +13,8 @@ benchmark times.
 Stages are isolated as in the smaller parity tests: Reindex receives the
 oracle's pool and attention the oracle's index sets, so that an exempt near tie
 cannot cascade; the GPU-only chain is compared end to end where its index sets
-equal the oracle's.
+equal the oracle's.  Attention runs as the benchmark runs it: a group's Full or
+Reindex layer stores the gathered main records, its Reuse layers read them.
 """
 import sys
 import time
@@ -84,6 +85,7 @@ def test_decode_step_full_size(K, name):
     ws_ri = K.alloc_workspace(K.OP_INDEX_REINDEX, B)
     ws_sel = K.alloc_workspace(K.OP_SELECT_POOL, B, N)
     ws_at = K.alloc_workspace(K.OP_DECODE_ATTN, B)
+    kvg = torch.empty((B, G.TOPK, K.RECORD), dtype=torch.uint8, device="cuda")
 
     opool = oidx = None
     gpu_chain_equal = True
@@ -117,10 +119,12 @@ def test_decode_step_full_size(K, name):
                 n_exempt += check_index_set(gidx[b], oidx[b], lambda t: scs[b][t], kp[b])
             gpu_chain_equal &= np.array_equal(gidx, oidx)
             _say(f"  layer {l} Reindex: exempt diffs so far {n_exempt}")
-        # attention of every layer on the group's (oracle) index set; Reuse
-        # layers pass the same idx again
+        # attention of every layer on the group's (oracle) index set, as the
+        # benchmark runs it: the group's first layer stores the gathered
+        # records, its Reuse layers read them with the same idx
         q = G.attn_queries(seed, l, B)
-        K.decode_attn(gc, l, dev(q), dev(oidx), dseq, dctx, out_t, ws_at)
+        gather = dict(kvg_in=kvg) if mode == "R" else dict(kvg_out=kvg)
+        K.decode_attn(gc, l, dev(q), dev(oidx), dseq, dctx, out_t, ws_at, **gather)
         torch.cuda.synchronize()
         want = oc.decode_attn(l, q, oidx, seq, ctx)
         err = float(np.max(np.abs(out_t.cpu().numpy() - want)))

@@ -422,3 +422,44 @@ def test_attention_workspace_reuse_across_shapes(K):
         torch.cuda.synchronize()
         want = oc.decode_attn(layer, q, idx, seq, ctx)
         assert np.max(np.abs(out.cpu().numpy() - want)) <= 1e-4, (B, topk, layer)
+
+
+@pytest.mark.parametrize("B", [3, 96])
+def test_reuse_gathered_records_bit_exact(K, B):
+    """csa2_decode_attn_ex: the group's first layer stores the gathered main
+    records (kvg_out), its Reuse layers read them (kvg_in).  Both give the plain
+    call's output bit for bit (tile kernel at B = 3, split stream kernel at
+    B = 96), and the stored records are the cache's bytes."""
+    _say(f"reuse via gathered records B={B}")
+    N, L = 3000, 4
+    oc = O.Cache(3, N, L)
+    gc = K.Cache(3, N, L)
+    fill_both(23, 3, N, L, oc, gc)
+    seq = (np.arange(B) % 3).astype(np.int32)
+    ctx = np.array([N, N - 100, 700], np.int64)[seq]
+    qi, wi = G.index_queries(23, 0, 3)
+    _, idx3, _, _ = oc.index_full(qi, wi, np.arange(3, dtype=np.int32), ctx[:3])
+    idx = idx3[seq].copy()
+    idx[1, 500:] = -1                       # padding inside the list
+    didx, dseq, dctx = dev(idx), dev(seq), dev(ctx)
+    ws = K.alloc_workspace(K.OP_DECODE_ATTN, B)
+    g = torch.zeros((B, 512, 144), dtype=torch.uint8, device="cuda")
+    plain = torch.empty((B, 16, 128), dtype=torch.float32, device="cuda")
+    out = torch.empty_like(plain)
+    for layer in range(L):
+        q = dev(G.attn_queries(23, layer, B))
+        K.decode_attn(gc, layer, q, didx, dseq, dctx, plain, ws)
+        if layer == 0:
+            K.decode_attn(gc, layer, q, didx, dseq, dctx, out, ws, kvg_out=g)
+        else:
+            K.decode_attn(gc, layer, q, didx, dseq, dctx, out, ws, kvg_in=g)
+        torch.cuda.synchronize()
+        assert torch.equal(out, plain), layer
+        want = oc.decode_attn(layer, G.attn_queries(23, layer, B), idx, seq, ctx)
+        assert float(np.max(np.abs(out.cpu().numpy() - want))) <= 1e-4
+    # the stored records are the cache's records of the valid entries
+    gh, kv = g.cpu().numpy(), oc.kv
+    valid = (idx >= 0) & (idx < ctx[:, None])
+    bb, jj = np.nonzero(valid)
+    assert np.array_equal(gh[bb, jj], kv[seq[bb], idx[bb, jj]])
+    assert not gh[~valid].any()             # invalid entries left untouched
