@@ -826,12 +826,19 @@ __global__ void __launch_bounds__(BIG_T) topk_merge_kernel(TopkArgs a) {
 #pragma unroll
         for (int j = 0; j < VPT; ++j) id[j] = (uint32_t)(VPT * t + j);
     } else {
+        // slots past the last segment's area are never loaded (absent)
         const float4* sv = reinterpret_cast<const float4*>(a.seg_val + (int64_t)b * SMALL_MAX);
         const uint4* si = reinterpret_cast<const uint4*>(a.seg_id + (int64_t)b * SMALL_MAX);
+        const int n_slots = (int)((n + SEG - 1) / SEG) * quota;   // <= SMALL_MAX
 #pragma unroll
         for (int r = 0; r < VPT / 4; ++r) {
-            const float4 x = sv[4 * t + r];
-            const uint4 y = si[4 * t + r];
+            const bool in = VPT * t + 4 * r < n_slots;
+            float4 x = make_float4(NEG_INF, NEG_INF, NEG_INF, NEG_INF);
+            uint4 y = make_uint4(0u, 0u, 0u, 0u);
+            if (in) {
+                x = sv[4 * t + r];
+                y = si[4 * t + r];
+            }
             v[4 * r] = x.x; v[4 * r + 1] = x.y; v[4 * r + 2] = x.z; v[4 * r + 3] = x.w;
             id[4 * r] = y.x; id[4 * r + 1] = y.y; id[4 * r + 2] = y.z; id[4 * r + 3] = y.w;
         }
