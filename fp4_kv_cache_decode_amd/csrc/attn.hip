@@ -28,19 +28,26 @@
 // step's records are in flight while a step is computed.
 //
 // Precision: dequantised values are exact in f16 (an E2M1 value times an E4M3
-// scale has at most 5 significant bits, an E4M3 value has 4).  The fp32 query
+// scale has at most 6 significant bits, an E4M3 value has 4).  The fp32 query
 // and the fp32 softmax weights are split into f16 hi + lo parts and issued as
 // two MFMAs, so products are exact and accumulation is fp32.
 //
 // A workgroup (4 waves) owns a range of a query's steps; the waves' (m, l, O)
 // are combined in LDS.  With one workgroup per query (large batches) it writes
-// the output directly; otherwise each split writes (m, l, O) partials and a
-// merge kernel combines them (the same algebra an unsplit softmax uses).
+// the output directly; otherwise each split writes (m, l, O) partials and the
+// merge kernel combines them (the same algebra an unsplit softmax uses), one
+// workgroup per (head, query).
 //
-// FP4 dequantisation: the f16 encodings of the E2M1 magnitudes {0, .5, 1, 1.5,
-// 2, 3, 4, 6} differ only in their high byte, so v_perm_b32 with an 8-byte table
-// turns four code nibbles into four f16 high bytes in one instruction; a packed
-// f16 multiply by the group's E4M3 scale is exact (at most 6 significant bits).
+// Gathered records: a Reuse layer attends over the main rows its group's first
+// layer gathered (the main KV is shared by every layer).  With kvg_out a call
+// also stores each valid main record it read at [b][j] of a compact buffer;
+// with kvg_in a call reads record [b][j] from that buffer, at an address that
+// does not wait for the index load, and the index only decides validity.  The
+// bytes are the same, so the results are bit-identical.
+//
+// Dequantisation (both kernels): gfx950's v_cvt_scalef32_pk_f16_fp4 / _fp8 turn
+// two codes into two exact f16 values per instruction; the E4M3 group scale is
+// then one packed f16 multiply, exact (at most 6 significant bits).
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
@@ -105,42 +112,6 @@ struct StreamShared {
 };
 
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
-
-// f16 high bytes of the E2M1 magnitudes 0..3 and 4..7 (a v_perm_b32 table).
-constexpr uint32_t E2M1_HB_LO = 0x3E3C3800u;
-constexpr uint32_t E2M1_HB_HI = 0x46444240u;
-
-// f16 value of a signed E4M3 scale code (exact).
-__device__ __forceinline__ half2_t scale_h2(uint32_t code) {
-    const float s = e4m3_value_pos(code & 0x7f) * ((code & 0x80) ? -1.0f : 1.0f);
-    const _Float16 h = (_Float16)s;
-    return half2_t{h, h};
-}
-
-// 8 FP4 codes (one dword; channel 2j in the low nibble of byte j) -> 4 f16x2
-// words (channels 2j, 2j+1 in word j), times the group scale.
-__device__ __forceinline__ void fp4x8_to_f16x2(uint32_t w, half2_t scale, uint32_t* o) {
-    // high bytes of channels 0,2,4,6 and 1,3,5,7; sign bit = nibble bit 3
-    const uint32_t he = __builtin_amdgcn_perm(E2M1_HB_HI, E2M1_HB_LO, w & 0x07070707u) |
-                        ((w << 4) & 0x80808080u);
-    const uint32_t ho = __builtin_amdgcn_perm(E2M1_HB_HI, E2M1_HB_LO, (w >> 4) & 0x07070707u) |
-                        (w & 0x80808080u);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        // bytes: 0x00, even high byte j, 0x00, odd high byte j (selector 12 = 0x00)
-        const uint32_t sel = 0x0Cu | ((uint32_t)j << 8) | (0x0Cu << 16) | ((uint32_t)(4 + j) << 24);
-        const uint32_t x = __builtin_amdgcn_perm(ho, he, sel);
-        const half2_t v = __builtin_bit_cast(half2_t, x) * scale;
-        o[j] = __builtin_bit_cast(uint32_t, v);
-    }
-}
-
-// 4 E4M3 bytes -> 4 f16 (exact) packed in two dwords.
-__device__ __forceinline__ void fp8x4_to_f16x4(uint32_t w, uint32_t* o) {
-    const float2 a = e4m3x2_to_f32<false>(w), b = e4m3x2_to_f32<true>(w);
-    o[0] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)a.x, (_Float16)a.y});
-    o[1] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)b.x, (_Float16)b.y});
-}
 
 // The gfx950 scaled converters.  Their fp32 scale operand applies only its
 // power of two (E8M0 semantics), so it is 1 here and the E4M3 group scale is
@@ -280,18 +251,20 @@ __global__ void __launch_bounds__(AT_THREADS) attn_tile_kernel(TileArgs a) {
                 }
                 // K scales are bytes 0..7 of sc, V scales bytes 8..15; this
                 // thread's 32 channels are groups 2*q4 and 2*q4 + 1
-                const uint32_t ks = (q4 < 2 ? sc.x : sc.y) >> (16 * (q4 & 1));
-                const uint32_t vs = (q4 < 2 ? sc.z : sc.w) >> (16 * (q4 & 1));
-                const half2_t k0 = scale_h2(ks & 0xff), k1 = scale_h2((ks >> 8) & 0xff);
-                const half2_t v0 = scale_h2(vs & 0xff), v1 = scale_h2((vs >> 8) & 0xff);
-                fp4x8_to_f16x2(kc.x, k0, kw + 0);
-                fp4x8_to_f16x2(kc.y, k0, kw + 4);
-                fp4x8_to_f16x2(kc.z, k1, kw + 8);
-                fp4x8_to_f16x2(kc.w, k1, kw + 12);
-                fp4x8_to_f16x2(vc.x, v0, vw + 0);
-                fp4x8_to_f16x2(vc.y, v0, vw + 4);
-                fp4x8_to_f16x2(vc.z, v1, vw + 8);
-                fp4x8_to_f16x2(vc.w, v1, vw + 12);
+                const half2_t ks2 =
+                    fp8x2_h2<false>((q4 < 2 ? sc.x : sc.y) >> (16 * (q4 & 1)));
+                const half2_t vs2 =
+                    fp8x2_h2<false>((q4 < 2 ? sc.z : sc.w) >> (16 * (q4 & 1)));
+                const half2_t k0 = half2_t{ks2.x, ks2.x}, k1 = half2_t{ks2.y, ks2.y};
+                const half2_t v0 = half2_t{vs2.x, vs2.x}, v1 = half2_t{vs2.y, vs2.y};
+                fp4x8_scaled(kc.x, k0, kw + 0);
+                fp4x8_scaled(kc.y, k0, kw + 4);
+                fp4x8_scaled(kc.z, k1, kw + 8);
+                fp4x8_scaled(kc.w, k1, kw + 12);
+                fp4x8_scaled(vc.x, v0, vw + 0);
+                fp4x8_scaled(vc.y, v0, vw + 4);
+                fp4x8_scaled(vc.z, v1, vw + 8);
+                fp4x8_scaled(vc.w, v1, vw + 12);
             }
         } else {
             const int64_t u0 = N > WINDOW ? N - WINDOW : 0;
@@ -307,12 +280,10 @@ __global__ void __launch_bounds__(AT_THREADS) attn_tile_kernel(TileArgs a) {
                 const uint32_t vr[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
 #pragma unroll
                 for (int i = 0; i < 8; ++i) {
-                    const float2 a0 = e4m3x2_to_f32<false>(kr[i]), a1 = e4m3x2_to_f32<true>(kr[i]);
-                    const float2 b0 = e4m3x2_to_f32<false>(vr[i]), b1 = e4m3x2_to_f32<true>(vr[i]);
-                    kw[2 * i] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)a0.x, (_Float16)a0.y});
-                    kw[2 * i + 1] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)a1.x, (_Float16)a1.y});
-                    vw[2 * i] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)b0.x, (_Float16)b0.y});
-                    vw[2 * i + 1] = __builtin_bit_cast(uint32_t, half2_t{(_Float16)b1.x, (_Float16)b1.y});
+                    kw[2 * i] = __builtin_bit_cast(uint32_t, fp8x2_h2<false>(kr[i]));
+                    kw[2 * i + 1] = __builtin_bit_cast(uint32_t, fp8x2_h2<true>(kr[i]));
+                    vw[2 * i] = __builtin_bit_cast(uint32_t, fp8x2_h2<false>(vr[i]));
+                    vw[2 * i + 1] = __builtin_bit_cast(uint32_t, fp8x2_h2<true>(vr[i]));
                 }
             }
         }

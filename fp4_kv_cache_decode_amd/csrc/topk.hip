@@ -121,16 +121,8 @@ __device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
     return v;
 }
 
-// The four 16-lane rows reduced inside the row by DPP, then combined from
-// lanes 0, 16, 32, 48 with v_readlane; the result is wave-uniform.
-__device__ __forceinline__ uint32_t wave_sum_u32(uint32_t v) {
-    v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, DPP_XOR1, 0xf, 0xf, false);
-    v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, DPP_XOR2, 0xf, 0xf, false);
-    v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, DPP_ROR4, 0xf, 0xf, false);
-    v += (uint32_t)__builtin_amdgcn_mov_dpp((int)v, DPP_ROR8, 0xf, 0xf, false);
-    return (uint32_t)__builtin_amdgcn_readlane((int)v, 0) + (uint32_t)__builtin_amdgcn_readlane((int)v, 16) +
-           (uint32_t)__builtin_amdgcn_readlane((int)v, 32) + (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
-}
+// Min / max over the wave: the four 16-lane rows reduced inside the row by
+// DPP, then combined from lanes 0, 16, 32, 48 with v_readlane (wave-uniform).
 __device__ __forceinline__ float rows_min(float v) {
     auto rl = [](float x, int l) { return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), l)); };
     v = fminf(v, dpp_f32<DPP_XOR1>(v));
@@ -189,10 +181,11 @@ __device__ uint32_t block_incl_scan(uint32_t v, Shared<NT>& sh, uint32_t* total)
 }
 
 // Block-wide count, min and max in one LDS round: each wave reduces its own
-// values, then lanes 0 .. NT/64 - 1 of every wave read the waves' partials and
-// a 16-lane DPP reduction leaves the block's result in every lane.  The partial
-// arrays are next written after at least one more barrier (every caller's next
-// phase ends in one before any wave_u / wave_f write).
+// values (cnt is already the wave's count), then lanes 0 .. NT/64 - 1 of every
+// wave read the waves' partials and a 16-lane DPP reduction leaves the block's
+// result in every lane.  The partial arrays are next written after at least
+// one more barrier (every caller's next phase ends in one before any wave_u /
+// wave_f write).
 template <int NT>
 __device__ void block_stats(uint32_t cnt, float lo, float hi, Shared<NT>& sh, uint32_t* total,
                             float* mn, float* mx) {
@@ -200,7 +193,6 @@ __device__ void block_stats(uint32_t cnt, float lo, float hi, Shared<NT>& sh, ui
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     lo = rows_min(lo);
     hi = rows_max(hi);
-    cnt = wave_sum_u32(cnt);
     if (lane == 0) {
         sh.wave_f[0][wave] = lo;
         sh.wave_f[1][wave] = hi;
@@ -276,12 +268,12 @@ __device__ bool select_core(Shared<NT>& sh, const float (&v)[VPT], const uint32_
     }
     if (t == 0) sh.misc[2] = 0;
     float lo = __builtin_huge_valf(), hi = NEG_INF;
-    uint32_t cnt = 0;
+    uint32_t cnt = 0;                    // the wave's valid values (wave-uniform)
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
         const bool ok = v[j] != NEG_INF;
-        cnt += ok ? 1u : 0u;
-        lo = ok ? fminf(lo, v[j]) : lo;
+        cnt += (uint32_t)__builtin_popcountll(__ballot(ok));
+        lo = fminf(lo, ok ? v[j] : __builtin_huge_valf());
         hi = fmaxf(hi, v[j]);               // -inf never raises the max
     }
     uint32_t n_valid;
@@ -597,13 +589,13 @@ __device__ bool select16(Shared<BIG_T>& sh, const float (&v)[VPT], int64_t n_pos
 
     // ---- count / min / max of the valid values
     float lo = __builtin_huge_valf(), hi = NEG_INF;
-    uint32_t cnt = 0;
+    uint32_t cnt = 0;                    // the wave's valid values (wave-uniform)
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
         const bool ok = v[j] != NEG_INF;
-        cnt += ok ? 1u : 0u;
+        cnt += (uint32_t)__builtin_popcountll(__ballot(ok));
         lo = fminf(lo, ok ? v[j] : __builtin_huge_valf());
-        hi = fmaxf(hi, v[j]);
+        hi = fmaxf(hi, v[j]);               // -inf never raises the max
     }
     uint32_t n_valid;
     float vmin, vmax;
