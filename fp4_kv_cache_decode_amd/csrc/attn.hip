@@ -306,19 +306,23 @@ __global__ void __launch_bounds__(AT_THREADS) attn_tile_kernel(TileArgs a) {
 
     __syncthreads();
 
-    // ---- S = Q K^T for entries 16*wave .. +15
-    float4_t sacc = {0.f, 0.f, 0.f, 0.f};
+    // ---- S = Q K^T for entries 16*wave .. +15 (hi and lo parts of q in two
+    // independent accumulator chains)
+    float4_t sacc;
     {
+        float4_t shi = {0.f, 0.f, 0.f, 0.f}, slo = {0.f, 0.f, 0.f, 0.f};
         const int ent = 16 * wave + (lane & 15), g = lane >> 4;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
             const half4_t kf = *reinterpret_cast<const half4_t*>(&sh.K[ent * KROW + 16 * ks + 4 * g]);
-            sacc = __builtin_amdgcn_mfma_f32_16x16x16f16(qhi[ks], kf, sacc, 0, 0, 0);
-            sacc = __builtin_amdgcn_mfma_f32_16x16x16f16(qlo[ks], kf, sacc, 0, 0, 0);
+            shi = __builtin_amdgcn_mfma_f32_16x16x16f16(qhi[ks], kf, shi, 0, 0, 0);
+            slo = __builtin_amdgcn_mfma_f32_16x16x16f16(qlo[ks], kf, slo, 0, 0, 0);
         }
+        sacc = shi + slo;
     }
-    // lane holds S[head 4*(lane/16) + r][entry 16*wave + lane%16]
-    const float lscale = a.sm_scale * (is_main ? 1.0f : a.wk_scale);
+    // lane holds S[head 4*(lane/16) + r][entry 16*wave + lane%16]; logits in
+    // log2 units (log2(e) folded into the scale), so exp2 is one v_exp_f32
+    const float lscale = a.sm_scale * LOG2E * (is_main ? 1.0f : a.wk_scale);
     const bool ent_ok = sh.valid[16 * wave + (lane & 15)];
     float sv[4];
 #pragma unroll
@@ -345,7 +349,8 @@ __global__ void __launch_bounds__(AT_THREADS) attn_tile_kernel(TileArgs a) {
     for (int r = 0; r < 4; ++r) {
         const int h = 4 * (lane >> 4) + r;
         m_tile[r] = fmaxf(fmaxf(sh.red[0][h], sh.red[1][h]), fmaxf(sh.red[2][h], sh.red[3][h]));
-        p[r] = (m_tile[r] == NEG_INF || sv[r] == NEG_INF) ? 0.0f : expf(sv[r] - m_tile[r]);
+        p[r] = (m_tile[r] == NEG_INF || sv[r] == NEG_INF) ? 0.0f
+                                                        : __builtin_amdgcn_exp2f(sv[r] - m_tile[r]);
         float v = p[r];
         v += dpp_f32<DPP_XOR1>(v);
         v += dpp_f32<DPP_XOR2>(v);
@@ -396,7 +401,7 @@ __global__ void __launch_bounds__(AT_THREADS) attn_tile_kernel(TileArgs a) {
     }
     if (wave == 0 && (lane & 15) == 0) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) part[4 * (lane >> 4) + r] = m_tile[r];
+        for (int r = 0; r < 4; ++r) part[4 * (lane >> 4) + r] = m_tile[r] * LN2;   // natural log
     }
 }
 
