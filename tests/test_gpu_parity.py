@@ -463,3 +463,30 @@ def test_reuse_gathered_records_bit_exact(K, B):
     bb, jj = np.nonzero(valid)
     assert np.array_equal(gh[bb, jj], kv[seq[bb], idx[bb, jj]])
     assert not gh[~valid].any()             # invalid entries left untouched
+
+
+@pytest.mark.parametrize("wv_scale", [50.0, 300.0])
+@pytest.mark.parametrize("B", [3, 96])
+def test_decode_attn_window_scales(K, B, wv_scale):
+    """Per-tensor window scales away from 1 on both kernels.  The stream kernel
+    (B = 96) lets its softmax reference lag by up to 2^8 only while weight times
+    window V scale stays inside f16 (scale <= 128): 50 takes that path, 300 the
+    exact-max path."""
+    _say(f"decode_attn window scales B={B} wv_scale={wv_scale}")
+    N, L = 2000, 2
+    oc = O.Cache(3, N, L, wk_scale=0.02, wv_scale=wv_scale)
+    gc = K.Cache(3, N, L, wk_scale=0.02, wv_scale=wv_scale)
+    fill_both(61, 3, N, L, oc, gc)
+    seq = (np.arange(B) % 3).astype(np.int32)
+    ctx = np.array([N, N - 7, 900], np.int64)[seq]
+    qi, wi = G.index_queries(61, 0, 3)
+    _, idx3, _, _ = oc.index_full(qi, wi, np.arange(3, dtype=np.int32), ctx[:3])
+    idx = idx3[seq]
+    q = G.attn_queries(61, 1, B)
+    out = torch.empty((B, 16, 128), dtype=torch.float32, device="cuda")
+    K.decode_attn(gc, 1, dev(q), dev(idx), dev(seq), dev(ctx), out, K.alloc_workspace(K.OP_DECODE_ATTN, B))
+    torch.cuda.synchronize()
+    want = oc.decode_attn(1, q, idx, seq, ctx)
+    err = float(np.max(np.abs(out.cpu().numpy() - want)))
+    _say(f"  max-abs err {err:.3g}")
+    assert err <= 1e-4 * max(1.0, float(np.max(np.abs(want))))
