@@ -405,7 +405,13 @@ hipError_t launch_score_pool(const csa2_cache& c, const float* q_idx, const floa
     a.out_stride = (int64_t)n_blocks * BLOCK;
     a.n_seq = c.n_seq;
     a.n_blocks = n_blocks;
-    a.keys_per_wg = STEP * WAVES;           // one step per wave: latency, not bandwidth
+    // few queries: one step per wave (latency); many queries: longer runs per
+    // workgroup, so that dispatch does not dominate (about 8 workgroups per CU)
+    const int64_t items_all = (int64_t)B * n_blocks * BLOCK;
+    int64_t kpw = items_all / (256 * 8);
+    kpw = kpw < STEP * WAVES ? STEP * WAVES : (kpw + STEP * WAVES - 1) / (STEP * WAVES) * (STEP * WAVES);
+    const int64_t row = ((int64_t)n_blocks * BLOCK + STEP * WAVES - 1) / (STEP * WAVES) * (STEP * WAVES);
+    a.keys_per_wg = (int32_t)(kpw > row ? row : kpw);
     a.scale = c.idxk_scale;
     const int64_t items = (int64_t)n_blocks * BLOCK;
     dim3 grid((unsigned)((items + a.keys_per_wg - 1) / a.keys_per_wg), (unsigned)B);
