@@ -25,7 +25,8 @@
 // few instructions per value: a single-barrier block reduction, no atomics on
 // the chosen path, one coalesced store.
 //
-// Rows of up to 16,384 entries: one workgroup, one read of the row.
+// Rows of up to 16,384 entries: one workgroup, one read of the row; up to
+// 32,768: the same with 32 values per thread.
 // Longer rows (up to 131,072): a segment kernel takes the exact top-q of each
 // 4,096-entry segment (q >= 4x a segment's expected share of the top-k) and
 // writes it densely in ascending index order; a merge kernel selects the top-k
@@ -46,9 +47,10 @@ constexpr int VPT = 16;                  // values per thread
 constexpr int BIG_T = 1024;              // threads: small-row and merge kernels
 constexpr int SEG_T = 256;               // threads: segment kernel
 constexpr int SMALL_MAX = BIG_T * VPT;   // 16,384
+constexpr int RUN2_MAX = 2 * SMALL_MAX;  // 32,768: one workgroup at 32 values per thread
 constexpr int SEG = SEG_T * VPT;         // 4,096
 constexpr int FAST_MAX_N = 131072;
-constexpr int STAGE_WORDS = CSA2_MAX_POOL > SMALL_MAX / 32 ? CSA2_MAX_POOL : SMALL_MAX / 32;
+constexpr int STAGE_WORDS = CSA2_MAX_POOL > RUN2_MAX / 32 ? CSA2_MAX_POOL : RUN2_MAX / 32;
 constexpr int CAND_CAP = 4096;
 constexpr int RANK_MAX = 256;            // candidate sets ranked directly
 constexpr int UNROLL = 8;
@@ -75,7 +77,7 @@ struct TopkArgs {
 template <int NT>
 struct Shared {
     uint32_t hist[4096];
-    uint32_t sel_bits[NT == BIG_T ? SMALL_MAX / 32 : SEG / 32];
+    uint32_t sel_bits[NT == BIG_T ? RUN2_MAX / 32 : SEG / 32];
     uint32_t eq_bits[NT == BIG_T ? STAGE_WORDS : SEG / 32];   // also the output staging
     uint32_t ckey[CAND_CAP];
     uint32_t cidx[CAND_CAP];
@@ -559,22 +561,23 @@ __device__ __forceinline__ void load_values(const float* row, int64_t base, int6
     }
 }
 
-// Selection over up to SMALL_MAX positions with thread t owning positions
-// 16t .. 16t+15 (values in registers, -inf absent).  Its share of the choice is
-// then a 16-bit register mask, and because positions are in output order the
+// Selection over up to V * 1,024 positions with thread t owning positions
+// Vt .. Vt+V-1 (V = 16 or 32; values in registers, -inf absent).  Its share of
+// the choice is then a V-bit register mask, and because positions are in output order the
 // ascending output is one block scan of the masks' popcounts: on the common
 // path no bitmap and no atomics besides the histogram's.  The steps are those
 // of select_core: count / min / max, the value-linear histogram and the bin d
 // of the k-th value, positions above d chosen, bin d's positions resolved as
 // candidates (returned through sel_bits).  id_of(j) is the output value of
-// position 16t + j; veto(j) (for chosen positions) may reject the whole choice.
+// position Vt + j; veto(j) (for chosen positions) may reject the whole choice.
 // Writes out[0, k) ascending with -1 padding and returns true, or returns false
 // (nothing written) when the candidate list overflowed or a veto fired.
 // STATIC_J visits the chosen positions with compile-time j (for id_of / veto
 // that index register arrays, which a runtime j would move to scratch).
-template <bool STATIC_J, typename IdOf, typename Veto>
-__device__ bool select16(Shared<BIG_T>& sh, const float (&v)[VPT], int64_t n_pos, uint32_t k,
-                         int32_t* out, IdOf id_of, Veto veto) {
+template <int V, bool STATIC_J, typename IdOf, typename Veto>
+__device__ bool select_run(Shared<BIG_T>& sh, const float (&v)[V], int64_t n_pos, uint32_t k,
+                           int32_t* out, IdOf id_of, Veto veto) {
+    static_assert(V == 16 || V == 32, "a thread's choice is one 32-bit mask word or half of one");
     const int t = threadIdx.x;
     const int words = (int)((n_pos + 31) >> 5);
     for (int i = t; i < NB; i += BIG_T) sh.hist[i] = 0;
@@ -591,7 +594,7 @@ __device__ bool select16(Shared<BIG_T>& sh, const float (&v)[VPT], int64_t n_pos
     float lo = __builtin_huge_valf(), hi = NEG_INF;
     uint32_t cnt = 0;                    // the wave's valid values (wave-uniform)
 #pragma unroll
-    for (int j = 0; j < VPT; ++j) {
+    for (int j = 0; j < V; ++j) {
         const bool ok = v[j] != NEG_INF;
         cnt += (uint32_t)__builtin_popcountll(__ballot(ok));
         lo = fminf(lo, ok ? v[j] : __builtin_huge_valf());
@@ -601,18 +604,18 @@ __device__ bool select16(Shared<BIG_T>& sh, const float (&v)[VPT], int64_t n_pos
     float vmin, vmax;
     block_stats<BIG_T>(cnt, lo, hi, sh, &n_valid, &vmin, &vmax);
 
-    uint32_t mask = 0;                   // bit j: position 16t + j chosen
+    uint32_t mask = 0;                   // bit j: position Vt + j chosen
     if (n_valid <= k) {
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) mask |= v[j] != NEG_INF ? 1u << j : 0u;
+        for (int j = 0; j < V; ++j) mask |= v[j] != NEG_INF ? 1u << j : 0u;
         __syncthreads();                 // block_stats' partials read before the scan reuses them
     } else {
         // ---- histogram and the bin d holding the k-th largest value
         float inv = vmax > vmin ? (float)NB / (vmax - vmin) : 0.0f;
         if (!(inv < __builtin_huge_valf())) inv = 0.0f;     // range overflowed: one bin
-        uint32_t bin[VPT];
+        uint32_t bin[V];
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
+        for (int j = 0; j < V; ++j) {
             const int bb = (int)((v[j] - vmin) * inv);
             bin[j] = v[j] == NEG_INF ? 0xffffffffu : (uint32_t)(bb < NB - 1 ? bb : NB - 1);
             if (bin[j] != 0xffffffffu) atomicAdd(&sh.hist[bin[j]], 1u);
@@ -624,20 +627,21 @@ __device__ bool select16(Shared<BIG_T>& sh, const float (&v)[VPT], int64_t n_pos
         __syncthreads();
         // ---- above d: chosen; in d: candidates
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
+        for (int j = 0; j < V; ++j) {
             if (bin[j] != 0xffffffffu && bin[j] > d) {
                 mask |= 1u << j;
             } else if (bin[j] == d) {
                 const uint32_t slot = atomicAdd(&sh.misc[2], 1u);
                 if (slot < (uint32_t)CAND_CAP) {
                     sh.ckey[slot] = order_key(v[j]);
-                    sh.cidx[slot] = (uint32_t)(VPT * t + j);
+                    sh.cidx[slot] = (uint32_t)(V * t + j);
                 }
             }
         }
         __syncthreads();
         if (!resolve_candidates<BIG_T>(sh, kk, words)) return false;
-        mask |= (sh.sel_bits[t >> 1] >> (16 * (t & 1))) & 0xffffu;
+        const uint32_t bit0 = (uint32_t)(V * t);
+        mask |= V == 32 ? sh.sel_bits[t] : (sh.sel_bits[bit0 >> 5] >> (bit0 & 31)) & 0xffffu;
     }
 
     // ---- veto, then ranks from a block scan (its barriers also publish the
@@ -646,7 +650,7 @@ __device__ bool select16(Shared<BIG_T>& sh, const float (&v)[VPT], int64_t n_pos
     if (STATIC_J) {
         bool vetoed = false;
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) vetoed |= ((mask >> j) & 1u) && veto(j);
+        for (int j = 0; j < V; ++j) vetoed |= ((mask >> j) & 1u) && veto(j);
         if (vetoed) sh.misc[3] = 1;
     } else {
         for (uint32_t m = mask; m; m &= m - 1)
@@ -659,7 +663,7 @@ __device__ bool select16(Shared<BIG_T>& sh, const float (&v)[VPT], int64_t n_pos
     int32_t* stage = reinterpret_cast<int32_t*>(sh.eq_bits);
     if (STATIC_J) {
 #pragma unroll
-        for (int j = 0; j < VPT; ++j) {
+        for (int j = 0; j < V; ++j) {
             if ((mask >> j) & 1u) {
                 if (pos < k) stage[pos] = id_of(j);
                 ++pos;
@@ -678,13 +682,14 @@ __device__ bool select16(Shared<BIG_T>& sh, const float (&v)[VPT], int64_t n_pos
     return true;
 }
 
-// Entries 16t .. 16t+15 of a row of n entries as four float4 loads; entries
-// past the end read as -inf (their loads stay in bounds).
-__device__ __forceinline__ void load_run16(const float* row, int64_t n, float (&v)[VPT]) {
+// Entries Vt .. Vt+V-1 of a row of n entries as float4 loads; entries past the
+// end read as -inf (their loads stay in bounds).
+template <int V>
+__device__ __forceinline__ void load_run(const float* row, int64_t n, float (&v)[V]) {
     const float4* v4 = reinterpret_cast<const float4*>(row);
 #pragma unroll
-    for (int r = 0; r < VPT / 4; ++r) {
-        const int64_t e0 = (int64_t)VPT * threadIdx.x + 4 * r;
+    for (int r = 0; r < V / 4; ++r) {
+        const int64_t e0 = (int64_t)V * threadIdx.x + 4 * r;
         const float4 x = v4[(e0 < n ? e0 : 0) >> 2];
         v[4 * r] = e0 < n ? x.x : NEG_INF;
         v[4 * r + 1] = e0 + 1 < n ? x.y : NEG_INF;
@@ -708,15 +713,44 @@ __global__ void __launch_bounds__(BIG_T) topk_small_kernel(TopkArgs a) {
     }
     // entries 16t .. 16t+15; in pool mode they lie in pool blocks 2t and 2t + 1
     float v[VPT];
-    load_run16(row, n, v);
+    load_run<VPT>(row, n, v);
     int32_t pb[2] = {0, 0};
     if (pool) {
         pb[0] = 2 * t < a.n_blocks ? pool[2 * t] : 0;
         pb[1] = 2 * t + 1 < a.n_blocks ? pool[2 * t + 1] : 0;
     }
-    const bool done = select16<false>(
+    const bool done = select_run<VPT, false>(
         sh, v, n, (uint32_t)a.k, out,
         [&](int j) -> int32_t { return pool ? pb[j >> 3] * BLOCK + (j & 7) : VPT * t + j; },
+        [](int) { return false; });
+    if (!done) topk_fallback(sh, row, n, a.k, pool, out);
+}
+
+// Rows of up to RUN2_MAX entries in one workgroup, 32 values per thread (rows
+// just past SMALL_MAX, e.g. the block maxima of 131,073..262,144 positions,
+// need no segment pass).  Entries 32t .. 32t+31 lie in pool blocks 4t .. 4t+3.
+__global__ void __launch_bounds__(BIG_T) topk_run32_kernel(TopkArgs a) {
+    __shared__ Shared<BIG_T> sh;
+    const int b = blockIdx.x;
+    const int t = threadIdx.x;
+    const int64_t n = row_length(a, b);
+    const float* row = a.vals + (int64_t)b * a.stride;
+    int32_t* out = a.out + (int64_t)b * a.k;
+    const int32_t* pool = a.pool ? a.pool + (int64_t)b * a.n_blocks : nullptr;
+    if (n > RUN2_MAX) {
+        topk_fallback(sh, row, n, a.k, pool, out);
+        return;
+    }
+    float v[2 * VPT];
+    load_run<2 * VPT>(row, n, v);
+    int32_t pb[4] = {0, 0, 0, 0};
+    if (pool) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pb[i] = 4 * t + i < a.n_blocks ? pool[4 * t + i] : 0;
+    }
+    const bool done = select_run<2 * VPT, true>(
+        sh, v, n, (uint32_t)a.k, out,
+        [&](int j) -> int32_t { return pool ? pb[j >> 3] * BLOCK + (j & 7) : 2 * VPT * t + j; },
         [](int) { return false; });
     if (!done) topk_fallback(sh, row, n, a.k, pool, out);
 }
@@ -790,7 +824,7 @@ __global__ void __launch_bounds__(SEG_T) topk_seg_kernel(TopkArgs a) {
 // Stage 2 of long rows: top-k of the union of the segments' choices, checked.
 // The dense candidate area lists segment 0's choices, then segment 1's, ...,
 // each in ascending index order, so slot order is output order and the
-// selection runs on slots (select16) with the slots' indices as output.  A full
+// selection runs on slots (select_run) with the slots' indices as output.  A full
 // segment whose worst reported entry is chosen may hide winners: that vetoes
 // the choice and the row takes the exact fallback.  Rows the segment kernel
 // skipped are selected here directly.
@@ -814,7 +848,7 @@ __global__ void __launch_bounds__(BIG_T) topk_merge_kernel(TopkArgs a) {
     int g0 = 0, g1 = 0;
     uint2 m0 = make_uint2(0u, 0u), m1 = make_uint2(0u, 0u);
     if (!two_stage) {
-        load_run16(row, n, v);
+        load_run<VPT>(row, n, v);
 #pragma unroll
         for (int j = 0; j < VPT; ++j) id[j] = (uint32_t)(VPT * t + j);
     } else {
@@ -850,7 +884,7 @@ __global__ void __launch_bounds__(BIG_T) topk_merge_kernel(TopkArgs a) {
         if (g1 < n_seg) m1 = *reinterpret_cast<const uint2*>(meta + 2 * g1);
     }
     // the pool goes to LDS for the output's lookups; its loads were issued
-    // with the values', and select16 orders these writes before any read
+    // with the values', and select_run orders these writes before any read
     int32_t pv[CSA2_MAX_POOL / BIG_T];
 #pragma unroll
     for (int r = 0; r < CSA2_MAX_POOL / BIG_T; ++r)
@@ -874,7 +908,7 @@ __global__ void __launch_bounds__(BIG_T) topk_merge_kernel(TopkArgs a) {
     }
     const int64_t n_pos = two_stage ? (int64_t)SMALL_MAX : n;
     const int g1_start = g1 * quota;
-    const bool done = select16<true>(
+    const bool done = select_run<VPT, true>(
         sh, v, n_pos, (uint32_t)a.k, out,
         [&](int j) -> int32_t {
             const int32_t i = (int32_t)id[j];
@@ -890,12 +924,12 @@ __global__ void __launch_bounds__(BIG_T) topk_merge_kernel(TopkArgs a) {
 
 static_assert(CSA2_MAX_POOL % BIG_T == 0, "pool entries per thread");
 static_assert(CSA2_MAX_POOL <= STAGE_WORDS && CSA2_MAX_TOPK <= STAGE_WORDS,
-              "select16 stages up to k outputs in eq_bits");
+              "select_run stages up to k outputs in eq_bits");
 
 }  // namespace
 
 size_t topk_workspace_bytes(int32_t B, int64_t max_n) {
-    if (max_n <= SMALL_MAX || max_n > FAST_MAX_N) return 0;
+    if (max_n <= RUN2_MAX || max_n > FAST_MAX_N) return 0;
     const int64_t n_seg = (max_n + SEG - 1) / SEG;
     return (size_t)B * SMALL_MAX * (sizeof(float) + sizeof(uint32_t)) +
            (size_t)B * (size_t)n_seg * 2 * sizeof(uint32_t);
@@ -918,6 +952,10 @@ hipError_t launch_topk(const float* vals, int64_t stride, const int64_t* ctx,
     const int64_t max_n = ctx ? (max_ctx + BLOCK - 1) / BLOCK : n_fixed;
     if (max_n <= SMALL_MAX || max_n > FAST_MAX_N) {
         hipLaunchKernelGGL(topk_small_kernel, dim3(B), dim3(BIG_T), 0, stream, a);
+        return hipGetLastError();
+    }
+    if (max_n <= RUN2_MAX) {
+        hipLaunchKernelGGL(topk_run32_kernel, dim3(B), dim3(BIG_T), 0, stream, a);
         return hipGetLastError();
     }
     const int64_t n_seg = (max_n + SEG - 1) / SEG;

@@ -193,7 +193,7 @@ csa2_status csa2_index_block_scores(const csa2_cache* cache, const float* q_idx,
  * (ties to the lower block), ascending, -1 padded.  n_blocks in 1..4096.  M must
  * be 16-byte aligned with m_stride a multiple of 4; -inf entries count as absent.
  *   ws        csa2_workspace_bytes(CSA2_OP_SELECT_POOL, B, max_ctx, n_blocks, 8, 1)
- *             bytes (zero for rows of up to 16,384 blocks; ws may then be NULL).
+ *             bytes (zero for rows of up to 32,768 blocks; ws may then be NULL).
  */
 csa2_status csa2_index_select_pool(const float* M, int64_t m_stride, const int64_t* ctx,
                                    int32_t B, int64_t max_ctx, int32_t n_blocks, int32_t* pool,
