@@ -61,6 +61,10 @@ def test_workspace_sizes(L):
     assert K.workspace_bytes(K.OP_INDEX_FULL, 4, 1 << 20, 8192, 8, 512) == 0      # pool too big
     assert K.workspace_bytes(K.OP_DECODE_ATTN, 4, 0, 0, 0, 4096) == 0             # topk too big
     assert K.workspace_bytes(99, 4, 0, 0, 0, 512) == 0
+    # block selection: one workgroup per row up to 32,768 blocks, segments beyond
+    assert K.workspace_bytes(K.OP_SELECT_POOL, 4, 8 * 32768, 2048, 8, 1) == 0
+    assert K.workspace_bytes(K.OP_SELECT_POOL, 4, 8 * 32768 + 1, 2048, 8, 1) > 0
+    assert K.workspace_bytes(K.OP_SELECT_POOL, 4, 8 * 131072, 2048, 8, 1) > 0
 
 
 FAKE = C.c_void_p(0x10000)   # never dereferenced: validation fails first
