@@ -142,10 +142,6 @@ constexpr float RESCALE_SLACK = 8.0f;
 constexpr float RESCALE_VSC_MAX = 128.0f;
 constexpr float LN2 = 0.6931471805599453f;
 
-__device__ __forceinline__ float xor32_f32(float v) {
-    const int lane = __lane_id();
-    return __int_as_float(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, __float_as_int(v)));
-}
 
 // ---------------------------------------------------------------------------
 // Tile kernel (small batches, latency): one workgroup per (query, 64-entry
@@ -636,8 +632,7 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
             sv[r] = ok ? sacc[r] * lscale : NEG_INF;
             tmax = fmaxf(tmax, sv[r]);
         }
-        tmax = fmaxf(tmax, swz_xor16(tmax));
-        tmax = fmaxf(tmax, xor32_f32(tmax));
+        tmax = max_xor32(max_xor16(tmax));
         // The reference max moves only when a logit exceeds it by more than
         // `slack` (log2 units), so O is rescaled rarely.  Any reference gives
         // the same softmax; weights stay below 2^slack, and p * vsc must stay
@@ -679,8 +674,7 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
     }
 
     // ---- combine the 4 waves: l over the 4 lanes of a head, then LDS
-    l_run += swz_xor16(l_run);
-    l_run += xor32_f32(l_run);
+    l_run = add_xor32(add_xor16(l_run));
     __syncthreads();                       // every wave is done with its V^T tile
     if (g == 0) {
         sh.mg.m[wave][c] = m_run;

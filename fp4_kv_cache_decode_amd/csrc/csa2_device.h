@@ -93,27 +93,29 @@ constexpr int DPP_ROR2 = 0x122;     // row_ror:2
 constexpr int DPP_ROR4 = 0x124;     // row_ror:4
 constexpr int DPP_ROR8 = 0x128;     // row_ror:8
 
-__device__ __forceinline__ float swz_xor16(float v) {
-    // ds_swizzle bit mode: and_mask 0x1f, xor_mask 0x10 (lanes i <-> i^16 in 32)
-    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401f));
+// Lanes l and l ^ 16 (or l ^ 32) combined without an LDS round trip: gfx950's
+// v_permlane16_swap / v_permlane32_swap of v with itself leave v[l & ~16] in
+// one result and v[l | 16] in the other (resp. 32), so their max or sum is the
+// pair's.
+__device__ __forceinline__ float max_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-
-__device__ __forceinline__ float wave_max(float v) {
-    v = fmaxf(v, dpp_f32<DPP_XOR1>(v));
-    v = fmaxf(v, dpp_f32<DPP_XOR2>(v));
-    v = fmaxf(v, dpp_f32<DPP_ROR4>(v));
-    v = fmaxf(v, dpp_f32<DPP_ROR8>(v));
-    v = fmaxf(v, swz_xor16(v));
-    return fmaxf(v, __shfl_xor(v, 32));
+__device__ __forceinline__ float max_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-
-__device__ __forceinline__ float wave_min(float v) {
-    v = fminf(v, dpp_f32<DPP_XOR1>(v));
-    v = fminf(v, dpp_f32<DPP_XOR2>(v));
-    v = fminf(v, dpp_f32<DPP_ROR4>(v));
-    v = fminf(v, dpp_f32<DPP_ROR8>(v));
-    v = fminf(v, swz_xor16(v));
-    return fminf(v, __shfl_xor(v, 32));
+__device__ __forceinline__ float add_xor16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float add_xor32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                    false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 // Order-preserving map of a finite float to uint32 (larger float -> larger
