@@ -497,7 +497,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU only (--gpus {args.gpus} requested); "
+        print(f"bench.py measures one GPU only (--gpus {args.gpus} requested); "
               "the decode path needs no collectives and shards by sequence, so run one "
               "process per GPU", file=sys.stderr)
         sys.exit(2)

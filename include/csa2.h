@@ -75,7 +75,7 @@ extern "C" {
 typedef enum csa2_status {
     CSA2_OK = 0,
     CSA2_ERR_INVALID_ARG = 1,  /* null pointer, negative size, out-of-range value */
-    CSA2_ERR_UNSUPPORTED = 2,  /* a size this build does not implement */
+    CSA2_ERR_UNSUPPORTED = 2,  /* a size the library does not implement */
     CSA2_ERR_WORKSPACE = 3,    /* ws null or ws_bytes below csa2_workspace_bytes */
     CSA2_ERR_LAUNCH = 4        /* a kernel launch failed (hipGetLastError) */
 } csa2_status;
