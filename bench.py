@@ -80,7 +80,7 @@ def counter_traffic(workload: str):
 class Setup:
     """Device caches (replicas), per-layer inputs and output buffers."""
 
-    def __init__(self, wl, seed, replicas, want_oracle):
+    def __init__(self, wl, seed, replicas, want_oracle, page_tokens=0):
         import torch
 
         import fp4_kv_cache_decode_amd.csa2 as K
@@ -89,7 +89,15 @@ class Setup:
         B, N, L = wl.B, wl.N, len(wl.layers)
         dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
         self.dev = dev
-        self.caches = [K.Cache(wl.n_seq, wl.cap, L, wl.w_cap) for _ in range(replicas)]
+        paging = {}
+        if page_tokens:
+            # every replica: the same fragmented layout over its own physical pool
+            table, n_pages = G.page_table(seed, wl.n_seq, wl.cap, page_tokens,
+                                          [wl.cap] * wl.n_seq)
+            paging = dict(page_tokens=page_tokens, n_pages=n_pages,
+                          page_table=torch.from_numpy(table))
+        self.caches = [K.Cache(wl.n_seq, wl.cap, L, wl.w_cap, **paging)
+                       for _ in range(replicas)]
         self.oc = None
         if want_oracle:
             import oracle as O
@@ -486,6 +494,9 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--replicas", type=int, default=2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--page-tokens", type=int, default=0,
+                    help="decode row on a paged cache: tokens per page (power of two >= 64), "
+                         "pages scattered over a shuffled physical pool; 0 = contiguous")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from Python instead of replaying HIP graphs")
     ap.add_argument("--copy-probe", action="store_true",
@@ -522,7 +533,7 @@ def main():
     B, N = wl.B, wl.N
     want_cpu = not args.no_cpu_baseline
     log(f"[bench] workload {wl.name}: B={B} N={N} layers={''.join(wl.layers)}")
-    S = Setup(wl, args.seed, args.replicas, want_cpu)
+    S = Setup(wl, args.seed, args.replicas, want_cpu, args.page_tokens)
 
     copy_gbs = copy_bandwidth()
     log(f"[bench] device copy {copy_gbs:.0f} GB/s")
@@ -550,8 +561,11 @@ def main():
     # roofline of the dominant kernel: the Full layer's indexer scan
     n_keys = B * N
     alg_bytes = n_keys * 64 + B * (-(-N // 8)) * 4 + B * (4 * 64 + 4) * 4
+    if args.page_tokens:
+        alg_bytes += B * (-(-N // args.page_tokens)) * 4      # page-table entries
     achieved = alg_bytes / (score_ms * 1e-3) / 1e9
-    traffic = counter_traffic(wl.name)
+    # the committed counters were taken on the contiguous cache
+    traffic = None if args.page_tokens else counter_traffic(wl.name)
 
     cpu = None
     if want_cpu:
@@ -584,7 +598,9 @@ def main():
         "config": {"workload": wl.name, "batch": B, "ctx": N, "layers": "".join(wl.layers),
                    "topk": G.TOPK, "window": G.WINDOW, "pool_blocks": G.N_BLOCKS,
                    "block": G.BLOCK, "replicas": args.replicas, "seed": args.seed,
-                   "launch": "eager" if args.eager else "hip-graph"},
+                   "launch": "eager" if args.eager else "hip-graph",
+                   "cache": (f"paged, {args.page_tokens}-token pages over a shuffled pool"
+                             if args.page_tokens else "contiguous")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
                      "traffic": traffic,

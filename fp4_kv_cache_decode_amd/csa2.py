@@ -28,7 +28,8 @@ class Csa2Error(RuntimeError):
 
 class csa2_cache(C.Structure):
     _fields_ = [("kv", C.c_void_p), ("idxk", C.c_void_p), ("idxk_scale", C.c_float),
-                ("n_seq", C.c_int32), ("cap", C.c_int64)]
+                ("n_seq", C.c_int32), ("cap", C.c_int64), ("page_table", C.c_void_p),
+                ("page_tokens", C.c_int32), ("n_pages", C.c_int32)]
 
 
 class csa2_window(C.Structure):
@@ -122,17 +123,39 @@ class Cache:
     """Device storage for the compressed cache and the per-layer window stores.
 
     Allocation goes through torch; the library only receives the pointers.
+    With page_tokens > 0 the global store is paged: kv and idxk hold n_pages
+    physical pages of page_tokens rows, and page_table[s][j] (int32, on the
+    device) names the page that holds positions j*page_tokens.. of sequence s.
+    The default table gives sequence s the pages s*cap/page_tokens + j.
     """
 
     def __init__(self, n_seq: int, cap: int, n_layers: int = 1, w_cap: int = WINDOW,
                  idxk_scale: float = 1.0, wk_scale: float = 1.0, wv_scale: float = 1.0,
-                 device="cuda"):
+                 device="cuda", page_tokens: int = 0, n_pages: int | None = None,
+                 page_table=None):
         self.n_seq, self.cap, self.n_layers, self.w_cap = n_seq, cap, n_layers, w_cap
-        self.kv = torch.zeros((n_seq, cap, RECORD), dtype=torch.uint8, device=device)
-        self.idxk = torch.zeros((n_seq, cap, IDX_DIM), dtype=torch.uint8, device=device)
+        self.page_tokens = page_tokens
+        if page_tokens:
+            if cap % page_tokens:
+                raise ValueError("cap must be a multiple of page_tokens")
+            per_seq = cap // page_tokens
+            self.n_pages = n_seq * per_seq if n_pages is None else n_pages
+            rows = (self.n_pages, page_tokens)
+            if page_table is None:
+                page_table = torch.arange(n_seq * per_seq, dtype=torch.int32).view(n_seq, per_seq)
+            page_table = torch.as_tensor(page_table, dtype=torch.int32)
+            if tuple(page_table.shape) != (n_seq, per_seq):
+                raise ValueError(f"page_table: expected shape {(n_seq, per_seq)}")
+            self.page_table = page_table.to(device).contiguous()
+        else:
+            self.n_pages, rows, self.page_table = 0, (n_seq, cap), None
+        self.kv = torch.zeros((*rows, RECORD), dtype=torch.uint8, device=device)
+        self.idxk = torch.zeros((*rows, IDX_DIM), dtype=torch.uint8, device=device)
         self.wk = torch.zeros((n_layers, n_seq, w_cap, D), dtype=torch.uint8, device=device)
         self.wv = torch.zeros_like(self.wk)
-        self.c = csa2_cache(self.kv.data_ptr(), self.idxk.data_ptr(), idxk_scale, n_seq, cap)
+        pt = self.page_table.data_ptr() if page_tokens else None
+        self.c = csa2_cache(self.kv.data_ptr(), self.idxk.data_ptr(), idxk_scale, n_seq, cap,
+                            pt, page_tokens, self.n_pages)
         self.w = csa2_window(self.wk.data_ptr(), self.wv.data_ptr(), wk_scale, wv_scale,
                              n_layers, n_seq, w_cap)
 

@@ -85,6 +85,7 @@ struct StreamArgs {
     float* part;             // [B][n_split][ATTN_PART_FLOATS] when n_split > 1
     float* out;              // [B][16][128] when n_split == 1
     int64_t cap;
+    PageMap pm;              // page table of a paged cache (table null otherwise)
     int32_t n_seq;
     int32_t w_cap;
     int32_t layer;
@@ -161,6 +162,7 @@ struct TileArgs {
     const int64_t* ctx;
     float* part;
     int64_t cap;
+    PageMap pm;              // page table of a paged cache (table null otherwise)
     int32_t n_seq;
     int32_t w_cap;
     int32_t layer;
@@ -182,6 +184,7 @@ struct TileShared {
     int valid[TILE];
 };
 
+template <bool PAGED>
 __global__ void __launch_bounds__(AT_THREADS) attn_tile_kernel(TileArgs a) {
     __shared__ TileShared sh;
     const int tile = blockIdx.x;
@@ -234,7 +237,7 @@ __global__ void __launch_bounds__(AT_THREADS) attn_tile_kernel(TileArgs a) {
             ok = seq_ok && pos >= 0 && pos < N;
             if (ok) {
                 if (!grec) {
-                    const uint8_t* rec = a.kv + ((int64_t)s * a.cap + pos) * RECORD;
+                    const uint8_t* rec = a.kv + cache_row<PAGED>(a.pm, a.cap, s, pos) * RECORD;
                     kc = *reinterpret_cast<const uint4*>(rec + 16 * q4);
                     vc = *reinterpret_cast<const uint4*>(rec + 64 + 16 * q4);
                     sc = *reinterpret_cast<const uint4*>(rec + 128);
@@ -414,6 +417,7 @@ struct Raw {
 };
 
 // 4 workgroups (16 waves) per CU: at most 128 VGPRs
+template <bool PAGED>
 __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a) {
     __shared__ StreamShared sh;
     const int split = blockIdx.x;
@@ -448,7 +452,7 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
             const int j = SUB * st + c;
             const uint8_t* rec =
                 a.kvg_in ? a.kvg_in + ((int64_t)b * a.topk + (j < a.topk ? j : 0)) * RECORD
-                         : a.kv + (ok ? ((int64_t)s * a.cap + pos) * RECORD : 0);
+                         : a.kv + (ok ? cache_row<PAGED>(a.pm, a.cap, s, pos) * RECORD : 0);
             const uint4 kc = *reinterpret_cast<const uint4*>(rec + 16 * g);
             const uint4 sc = *reinterpret_cast<const uint4*>(rec + 128);
             w.r[0] = kc.x; w.r[1] = kc.y; w.r[2] = kc.z; w.r[3] = kc.w;
@@ -811,6 +815,7 @@ hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
         a.ctx = ctx;
         a.part = partials;
         a.cap = c.cap;
+        a.pm = page_map(c);
         a.n_seq = c.n_seq;
         a.w_cap = w.w_cap;
         a.layer = layer;
@@ -820,7 +825,12 @@ hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
         a.wk_scale = w.k_scale;
         a.wv_scale = w.v_scale;
         a.sm_scale = sm_scale;
-        hipLaunchKernelGGL(attn_tile_kernel, dim3(a.n_tiles, B), dim3(AT_THREADS), 0, stream, a);
+        if (c.page_table)
+            hipLaunchKernelGGL(attn_tile_kernel<true>, dim3(a.n_tiles, B), dim3(AT_THREADS), 0,
+                               stream, a);
+        else
+            hipLaunchKernelGGL(attn_tile_kernel<false>, dim3(a.n_tiles, B), dim3(AT_THREADS), 0,
+                               stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(attn_merge_kernel, dim3(HEADS, B), dim3(D), 0, stream, partials,
@@ -840,6 +850,7 @@ hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
     a.part = partials;
     a.out = out;
     a.cap = c.cap;
+    a.pm = page_map(c);
     a.n_seq = c.n_seq;
     a.w_cap = w.w_cap;
     a.layer = layer;
@@ -850,7 +861,12 @@ hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
     a.n_sub_main = (topk + SUB - 1) / SUB;
     a.n_sub = a.n_sub_main + WINDOW / SUB;
     a.n_split = p.n_split;
-    hipLaunchKernelGGL(attn_stream_kernel, dim3(a.n_split, B), dim3(AT_THREADS), 0, stream, a);
+    if (c.page_table)
+        hipLaunchKernelGGL(attn_stream_kernel<true>, dim3(a.n_split, B), dim3(AT_THREADS), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL(attn_stream_kernel<false>, dim3(a.n_split, B), dim3(AT_THREADS), 0,
+                           stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_split == 1) return e;
     hipLaunchKernelGGL(attn_merge_kernel, dim3(HEADS, B), dim3(D), 0, stream, partials,

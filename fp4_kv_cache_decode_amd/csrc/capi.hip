@@ -56,6 +56,11 @@ csa2_status check_cache(const csa2_cache* c, bool need_kv, bool need_idxk) {
     if ((need_kv && !c->kv) || (need_idxk && !c->idxk)) return CSA2_ERR_INVALID_ARG;
     if (c->n_seq <= 0 || c->cap <= 0) return CSA2_ERR_INVALID_ARG;
     if (need_idxk && !good_scale(c->idxk_scale)) return CSA2_ERR_INVALID_ARG;
+    if (c->page_table) {
+        const int32_t p = c->page_tokens;
+        if (p < 64 || p > 65536 || (p & (p - 1))) return CSA2_ERR_UNSUPPORTED;
+        if (c->n_pages <= 0 || c->cap % p) return CSA2_ERR_INVALID_ARG;
+    }
     return CSA2_OK;
 }
 

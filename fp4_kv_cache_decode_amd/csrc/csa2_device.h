@@ -129,4 +129,26 @@ __device__ __forceinline__ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) {
     return v < lo ? lo : (v > hi ? hi : v);
 }
 
+// ---------------------------------------------------------------- cache rows
+// Row of kv / idxk that holds position t of sequence s.  A contiguous cache
+// keeps sequence s in rows s*cap .. s*cap + cap - 1.  A paged cache keeps t in
+// row t mod 2^shift of the physical page its table names for page t >> shift;
+// table entries outside [0, n_pages) are clamped into it, so a bad or unused
+// entry cannot move an access outside the buffers.
+struct PageMap {
+    const int32_t* table;   // [n_seq][per_seq] physical page ids (paged caches)
+    int64_t per_seq;        // pages per sequence: cap >> shift
+    int32_t shift;          // log2 of the tokens per page
+    int32_t n_pages;
+};
+
+template <bool PAGED>
+__device__ __forceinline__ int64_t cache_row(const PageMap& m, int64_t cap, int32_t s,
+                                             int64_t t) {
+    if (!PAGED) return (int64_t)s * cap + t;
+    int32_t pg = m.table[(int64_t)s * m.per_seq + (t >> m.shift)];
+    pg = pg < 0 ? 0 : (pg >= m.n_pages ? m.n_pages - 1 : pg);
+    return ((int64_t)pg << m.shift) + (t & (((int64_t)1 << m.shift) - 1));
+}
+
 }  // namespace csa2

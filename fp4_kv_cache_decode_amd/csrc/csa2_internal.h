@@ -6,8 +6,23 @@
 #include <stdint.h>
 
 #include "../../include/csa2.h"
+#include "csa2_device.h"
 
 namespace csa2 {
+
+// Device-side view of a cache descriptor's page table (unused when the cache
+// is contiguous; the descriptor has been validated by the caller).
+inline PageMap page_map(const csa2_cache& c) {
+    PageMap m{};
+    if (c.page_table) {
+        m.table = c.page_table;
+        m.shift = 0;
+        while ((1 << m.shift) < c.page_tokens) ++m.shift;
+        m.per_seq = c.cap >> m.shift;
+        m.n_pages = c.n_pages;
+    }
+    return m;
+}
 
 // Quantise-on-write of n rows into the cache (and window stores).
 hipError_t launch_quantize(const csa2_cache& c, const csa2_window* w, const float* k,

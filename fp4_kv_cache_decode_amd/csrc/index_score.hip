@@ -46,6 +46,7 @@ struct ScoreArgs {
     int64_t cap;
     int64_t max_ctx;
     int64_t out_stride;
+    PageMap pm;              // page table of a paged cache (table null otherwise)
     int32_t n_seq;
     int32_t n_blocks;        // pool mode
     int32_t keys_per_wg;
@@ -58,8 +59,11 @@ struct Raw {
 
 // Lanes whose key is not visible load key 0 of the sequence (always in bounds)
 // and have their score masked later: no branch, no register clearing.
-__device__ __forceinline__ void load_key(Raw& r, const uint8_t* keys, int64_t t, bool ok) {
-    const uint4* p = reinterpret_cast<const uint4*>(keys + (ok ? t : 0) * IDX_DIM);
+template <bool PAGED>
+__device__ __forceinline__ void load_key(Raw& r, const ScoreArgs& a, const uint8_t* idxk,
+                                         int32_t s, int64_t t, bool ok) {
+    const uint4* p =
+        reinterpret_cast<const uint4*>(idxk + cache_row<PAGED>(a.pm, a.cap, s, ok ? t : 0) * IDX_DIM);
     r.d[0] = p[0];
     r.d[1] = p[1];
     r.d[2] = p[2];
@@ -103,7 +107,7 @@ __device__ __forceinline__ float key_score(const Raw& r, const float* __restrict
 // provably unclobbered and can be scalar loads.  `zero` is 0 at run time; adding
 // zero * step to the query address makes it loop-variant, so the compiler
 // reloads one head at a time (64 SGPRs) instead of hoisting all 256 floats.
-template <bool POOL>
+template <bool POOL, bool PAGED>
 __global__ void __launch_bounds__(SC_THREADS)
 score_kernel(ScoreArgs a, const float* __restrict__ q_all, const uint8_t* __restrict__ idxk,
              float* __restrict__ out_all, int64_t zero) {
@@ -119,7 +123,6 @@ score_kernel(ScoreArgs a, const float* __restrict__ q_all, const uint8_t* __rest
     if (wg0 >= n_items) return;
     const int64_t wg_end = wg0 + a.keys_per_wg < n_items ? wg0 + a.keys_per_wg : n_items;
 
-    const uint8_t* keys = idxk + (int64_t)s * a.cap * IDX_DIM;
     const float* q = q_all + (int64_t)b * IDX_HEADS * IDX_DIM;
     float wh[4];
 #pragma unroll
@@ -161,17 +164,17 @@ score_kernel(ScoreArgs a, const float* __restrict__ q_all, const uint8_t* __rest
     Raw A, B;
     int64_t tA = 0, tB = 0;
     bool okA = k0 < wg_end && locate(k0 + lane, tA);
-    load_key(A, keys, tA, okA);
+    load_key<PAGED>(A, a, idxk, s, tA, okA);
     for (; k0 < wg_end; k0 += 2 * stride) {
         const int64_t k1 = k0 + stride;
         const bool okB = k1 < wg_end && locate(k1 + lane, tB);
-        load_key(B, keys, tB, okB);
+        load_key<PAGED>(B, a, idxk, s, tB, okB);
         __builtin_amdgcn_sched_barrier(0);
         finish(A, k0, okA);
         if (k1 >= wg_end) break;
         const int64_t k2 = k1 + stride;
         okA = k2 < wg_end && locate(k2 + lane, tA);
-        load_key(A, keys, tA, okA);
+        load_key<PAGED>(A, a, idxk, s, tA, okA);
         __builtin_amdgcn_sched_barrier(0);
         finish(B, k1, okB);
     }
@@ -241,6 +244,7 @@ __device__ __forceinline__ void wait_vm() {
 constexpr int SCAN_WAVES = 16;
 constexpr int SCAN_THREADS = SCAN_WAVES * 64;
 
+template <bool PAGED>
 __global__ void __launch_bounds__(SCAN_THREADS)
 scan_kernel(ScoreArgs a, const float* __restrict__ q_all, const uint8_t* __restrict__ idxk,
             float* __restrict__ out_all, int64_t zero) {
@@ -287,10 +291,13 @@ scan_kernel(ScoreArgs a, const float* __restrict__ q_all, const uint8_t* __restr
         return t < n_steps ? t : -1;
     };
     // issue step t into `slot`; a step that reaches past N loads key N - 1 in
-    // place of the missing keys (in bounds; their scores are masked)
+    // place of the missing keys (in bounds; their scores are masked).  A step
+    // is 64 aligned keys, so in a paged cache it lies inside one page; the page
+    // id is a uniform (scalar-cache) load, and neighbouring steps share it.
     auto issue = [&](int t, int slot) {
         const int64_t kb = wg0 + (int64_t)t * STEP;
-        const uint8_t* g = keys + kb * IDX_DIM;
+        const uint8_t* g =
+            PAGED ? idxk + cache_row<true>(a.pm, a.cap, s, kb) * IDX_DIM : keys + kb * IDX_DIM;
         const uint32_t l = lds0 + (uint32_t)(slot * SCAN_STEP_BYTES);
         if (kb + STEP <= N) {
 #pragma unroll
@@ -378,13 +385,18 @@ hipError_t launch_score_blocks(const csa2_cache& c, const float* q_idx, const fl
     a.cap = c.cap;
     a.max_ctx = max_ctx;
     a.out_stride = m_stride;
+    a.pm = page_map(c);
     a.n_seq = c.n_seq;
     a.keys_per_wg = keys_per_wg;
     a.scale = c.idxk_scale;
     dim3 grid((unsigned)((max_ctx + keys_per_wg - 1) / keys_per_wg), (unsigned)B);
     if (grid.x == 0) return hipSuccess;
-    hipLaunchKernelGGL(scan_kernel, grid, dim3(SCAN_THREADS), 0, stream, a, q_idx, c.idxk, M,
-                       (int64_t)0);
+    if (c.page_table)
+        hipLaunchKernelGGL(scan_kernel<true>, grid, dim3(SCAN_THREADS), 0, stream, a, q_idx,
+                           c.idxk, M, (int64_t)0);
+    else
+        hipLaunchKernelGGL(scan_kernel<false>, grid, dim3(SCAN_THREADS), 0, stream, a, q_idx,
+                           c.idxk, M, (int64_t)0);
     return hipGetLastError();
 }
 
@@ -403,6 +415,7 @@ hipError_t launch_score_pool(const csa2_cache& c, const float* q_idx, const floa
     a.cap = c.cap;
     a.max_ctx = c.cap;
     a.out_stride = (int64_t)n_blocks * BLOCK;
+    a.pm = page_map(c);
     a.n_seq = c.n_seq;
     a.n_blocks = n_blocks;
     // few queries: one step per wave (latency); many queries: longer runs per
@@ -415,8 +428,12 @@ hipError_t launch_score_pool(const csa2_cache& c, const float* q_idx, const floa
     a.scale = c.idxk_scale;
     const int64_t items = (int64_t)n_blocks * BLOCK;
     dim3 grid((unsigned)((items + a.keys_per_wg - 1) / a.keys_per_wg), (unsigned)B);
-    hipLaunchKernelGGL(score_kernel<true>, grid, dim3(SC_THREADS), 0, stream, a, q_idx, c.idxk,
-                       S, (int64_t)0);
+    if (c.page_table)
+        hipLaunchKernelGGL((score_kernel<true, true>), grid, dim3(SC_THREADS), 0, stream, a,
+                           q_idx, c.idxk, S, (int64_t)0);
+    else
+        hipLaunchKernelGGL((score_kernel<true, false>), grid, dim3(SC_THREADS), 0, stream, a,
+                           q_idx, c.idxk, S, (int64_t)0);
     return hipGetLastError();
 }
 

@@ -35,6 +35,7 @@ struct QuantArgs {
     const int64_t* pos;
     int64_t n;
     int64_t cap;
+    PageMap pm;              // page table of a paged cache (table null otherwise)
     int32_t n_seq;
     int32_t w_cap;
     float idxk_scale;
@@ -70,7 +71,7 @@ __device__ __forceinline__ bool row_target(const QuantArgs& a, int64_t row, int6
     int32_t s = a.seq[row];
     int64_t p = a.pos[row];
     if (s < 0 || s >= a.n_seq || p < 0 || p >= a.cap) return false;
-    dst = (int64_t)s * a.cap + p;
+    dst = a.pm.table ? cache_row<true>(a.pm, a.cap, s, p) : cache_row<false>(a.pm, a.cap, s, p);
     return true;
 }
 
@@ -152,6 +153,7 @@ hipError_t launch_quantize(const csa2_cache& c, const csa2_window* w, const floa
     a.pos = pos;
     a.n = n;
     a.cap = c.cap;
+    a.pm = page_map(c);
     a.n_seq = c.n_seq;
     a.idxk_scale = c.idxk_scale;
     int parts = idx_k ? 2 : 1;

@@ -45,7 +45,7 @@ OUTLIER_GAIN = 8.0
 CHUNK = 65536    # rows per generator chunk
 
 # tensor ids for stream keys
-_K, _V, _IDXK, _WINK, _WINV, _Q, _QIDX, _W, _OUTL = range(9)
+_K, _V, _IDXK, _WINK, _WINV, _Q, _QIDX, _W, _OUTL, _PAGES = range(10)
 
 
 def _rng(seed: int, *key: int) -> np.random.Generator:
@@ -116,6 +116,24 @@ def index_queries(seed: int, layer: int, n: int, stream: int = 0):
     q = _rng(seed, _QIDX, layer, stream).standard_normal((n, HI, DI), dtype=np.float32)
     w = _rng(seed, _W, layer, stream).random((n, HI), dtype=np.float32)
     return q, w
+
+
+def page_table(seed: int, n_seq: int, cap: int, page_tokens: int, n_used, spare: int = 3):
+    """A fragmented page layout for a paged cache: sequence s owns its first
+    ceil(n_used[s] / page_tokens) logical pages, scattered over a shuffled pool
+    of physical pages that also holds `spare` pages nobody owns; its remaining
+    logical pages are -1.  Returns (table [n_seq][cap // page_tokens] int32,
+    n_pages)."""
+    per = cap // page_tokens
+    need = [-(-int(n) // page_tokens) for n in n_used]
+    n_pages = sum(need) + spare
+    perm = _rng(seed, _PAGES, n_seq, page_tokens).permutation(n_pages).astype(np.int32)
+    table = np.full((n_seq, per), -1, np.int32)
+    at = 0
+    for s in range(n_seq):
+        table[s, :need[s]] = perm[at:at + need[s]]
+        at += need[s]
+    return table, n_pages
 
 
 # ---------------------------------------------------------------------------

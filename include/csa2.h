@@ -32,7 +32,8 @@
  *  - Inputs must be finite.  Index outputs are ascending and padded with -1.
  *
  * Data layout in HBM (the cache descriptor)
- *  - kv   [n_seq][cap][144] bytes, one record per token:
+ *  - kv   [n_seq][cap][144] bytes (paged: [n_pages][page_tokens][144], below),
+ *         one record per token:
  *         [0,64)   K codes, FP4 E2M1, channel 2j in the low nibble of byte j,
  *                  channel 2j+1 in the high nibble;
  *         [64,128) V codes, same packing;
@@ -41,9 +42,22 @@
  *    (FP4 E2M1 main KV with one E4M3 scale per 16 channels, quantised after
  *    RoPE: [P1] "CSA2 and FP4 KV caching", [P4] "FP4 and SWA Bounded Replay";
  *    0.5 byte per element: [P3] section 3 step 3.)
- *  - idxk [n_seq][cap][64] bytes, E4M3FN indexer keys; key value = code value
- *    times idxk_scale.  Main KV and indexer keys are shared by every layer of
- *    the decoder ([P1] "CSA2 and FP4 KV caching"; [P4] mode list).
+ *  - idxk [n_seq][cap][64] bytes (paged: [n_pages][page_tokens][64]), E4M3FN
+ *    indexer keys; key value = code value times idxk_scale.  Main KV and
+ *    indexer keys are shared by every layer of the decoder ([P1] "CSA2 and FP4
+ *    KV caching"; [P4] mode list).
+ *  - Paged caches.  The global store is the long-lived part of the cache: it is
+ *    kept while the sliding-window KV is not persisted and is rebuilt by
+ *    replaying the last 128 tokens ([P4] "FP4 and SWA Bounded Replay").  A
+ *    serving layer therefore allocates it in pages.  With a page table, the
+ *    record and indexer key of position t of sequence s live in row
+ *    t % page_tokens of physical page page_table[s][t / page_tokens] of kv and
+ *    idxk.  page_tokens is a power of two in [64, 65536] (a 64-key scan step
+ *    never straddles two pages), cap is a multiple of it, and the table is
+ *    [n_seq][cap / page_tokens] int32 on the device.  Entries of pages that
+ *    hold no visible position are never used for data and may be -1; any entry
+ *    outside [0, n_pages) is clamped into it, so that no access leaves kv/idxk.
+ *    Results are bit-identical to a contiguous cache holding the same bytes.
  *  - window k/v [n_layers][n_seq][w_cap][128] bytes, E4M3FN, one store per
  *    layer; position u lives in slot u % w_cap; value = code times k_scale /
  *    v_scale.  (FP8 sliding-window KV: [P4] "FP4 and SWA Bounded Replay";
@@ -74,19 +88,25 @@ extern "C" {
 
 typedef enum csa2_status {
     CSA2_OK = 0,
-    CSA2_ERR_INVALID_ARG = 1,  /* null pointer, negative size, out-of-range value */
-    CSA2_ERR_UNSUPPORTED = 2,  /* a size the library does not implement */
+    CSA2_ERR_INVALID_ARG = 1,  /* null pointer, negative size, out-of-range value,
+                                  cap not a multiple of page_tokens */
+    CSA2_ERR_UNSUPPORTED = 2,  /* a size the library does not implement
+                                  (including page_tokens) */
     CSA2_ERR_WORKSPACE = 3,    /* ws null or ws_bytes below csa2_workspace_bytes */
     CSA2_ERR_LAUNCH = 4        /* a kernel launch failed (hipGetLastError) */
 } csa2_status;
 
-/* The shared compressed store: main-KV records and indexer keys. */
+/* The shared compressed store: main-KV records and indexer keys.  A zeroed
+ * tail (page_table NULL) describes a contiguous cache. */
 typedef struct csa2_cache {
-    uint8_t* kv;        /* device [n_seq][cap][144] */
-    uint8_t* idxk;      /* device [n_seq][cap][64]  */
+    uint8_t* kv;        /* device [n_seq][cap][144], or [n_pages][page_tokens][144] */
+    uint8_t* idxk;      /* device [n_seq][cap][64],  or [n_pages][page_tokens][64]  */
     float idxk_scale;   /* per-tensor scale of the indexer keys (> 0) */
     int32_t n_seq;
     int64_t cap;        /* positions per sequence */
+    const int32_t* page_table;  /* NULL, or device [n_seq][cap / page_tokens] page ids */
+    int32_t page_tokens;        /* paged only: tokens per page, power of two in [64, 65536] */
+    int32_t n_pages;            /* paged only: physical pages behind kv and idxk (> 0) */
 } csa2_cache;
 
 /* Per-layer FP8 sliding-window stores, all layers in one allocation. */

@@ -31,8 +31,9 @@ def rows_for(seed, s, p0, p1, n_layers, N, wlo=None):
 def fill_both(seed, n_seq, N, n_layers, ocache, gcache=None, chunk=1 << 18, wlo=None,
               workers=1):
     """Write positions [0,N) of every sequence into the oracle cache and (if
-    given) the device cache through csa2_quantize_kv.  With workers > 1 the
-    rows of up to `workers` chunks are generated in parallel threads."""
+    given) the device cache, or each of a tuple of device caches, through
+    csa2_quantize_kv.  With workers > 1 the rows of up to `workers` chunks are
+    generated in parallel threads."""
     import torch
     from fp4_kv_cache_decode_amd import csa2
     for s in range(n_seq):
@@ -55,13 +56,13 @@ def _write_rows(s, p0, p1, rows, ocache, gcache, torch, csa2):
         if wk is not None:
             ocache.quantize(k[w0 - p0:], v[w0 - p0:], None, wk, wv, seq[w0 - p0:],
                             pos[w0 - p0:])
-    if gcache is not None:
-        dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
-        csa2.quantize_kv(gcache, dev(k), dev(v), dev(seq), dev(pos), idx_k=dev(ik))
+    gcaches = () if gcache is None else (gcache if isinstance(gcache, tuple) else (gcache,))
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    for gc in gcaches:
+        csa2.quantize_kv(gc, dev(k), dev(v), dev(seq), dev(pos), idx_k=dev(ik))
         if wk is not None:
-            csa2.quantize_kv(gcache, dev(k[w0 - p0:]), dev(v[w0 - p0:]),
-                             dev(seq[w0 - p0:]), dev(pos[w0 - p0:]), win_k=dev(wk),
-                             win_v=dev(wv))
+            csa2.quantize_kv(gc, dev(k[w0 - p0:]), dev(v[w0 - p0:]), dev(seq[w0 - p0:]),
+                             dev(pos[w0 - p0:]), win_k=dev(wk), win_v=dev(wv))
 
 
 def check_index_set(got, want, scores, kth, rel=REL_EXEMPT, exact=False):
@@ -90,3 +91,15 @@ def block_scores(pos_scores, N, block=8):
     pad = np.full(nb * block, -np.inf)
     pad[:N] = pos_scores
     return pad.reshape(nb, block).max(1)
+
+
+def shuffled_pages(seed, n_seq, cap, page_tokens, n_used, spare=3):
+    """(table, n_pages) of a shuffled physical pool with `spare` unowned pages
+    and -1 entries past each sequence's n_used positions."""
+    return G.page_table(seed, n_seq, cap, page_tokens, n_used, spare)
+
+
+def unpage(phys, table, page_tokens, n):
+    """Logical rows [n_seq][n][...] of a paged store [n_pages][page_tokens][...]."""
+    t = np.arange(n)
+    return phys[table[:, t // page_tokens], t % page_tokens]

@@ -154,3 +154,37 @@ def test_attn_error_paths(L):
     assert call_ex(FAKE, None, layer=2) == 1
     assert call_ex(None, FAKE, B=0) == 0
     assert call_ex(FAKE, None, B=0) == 0
+
+
+def test_paged_cache_validation(L):
+    """A page table needs a power-of-two page of 64..65,536 tokens that divides
+    cap and at least one physical page; every entry point checks it."""
+    from fp4_kv_cache_decode_amd import csa2 as K
+
+    def paged(P, n_pages=8, cap=1024):
+        return K.csa2_cache(FAKE.value, FAKE.value, 1.0, 1, cap, FAKE.value, P, n_pages)
+
+    q = L.csa2_quantize_kv
+    quant = lambda c: q(C.byref(c), None, FAKE, FAKE, None, None, None, FAKE, FAKE, 0, None)
+    assert quant(paged(64)) == 0
+    assert quant(paged(1024)) == 0
+    for bad in (0, 32, 96, 1 << 17):
+        assert quant(paged(bad)) == 2, bad
+    assert quant(paged(256, cap=1000)) == 1     # cap not a multiple of the page
+    assert quant(paged(256, n_pages=0)) == 1
+    # a null table means contiguous: the page fields are not looked at
+    assert quant(K.csa2_cache(FAKE.value, FAKE.value, 1.0, 1, 1000, None, 96, 0)) == 0
+    w = _win(K)
+    ws = K.workspace_bytes(K.OP_DECODE_ATTN, 2, 0, 0, 0, 512)
+    attn = lambda c: L.csa2_decode_attn(C.byref(c), C.byref(w), 0, FAKE, FAKE, FAKE, FAKE, 0,
+                                        512, 0.088, FAKE, FAKE, ws, None)
+    assert attn(paged(128)) == 0
+    assert attn(paged(100)) == 2
+    full = lambda c: L.csa2_index_full(C.byref(c), FAKE, FAKE, FAKE, FAKE, 0, 1024, 64, 8, 32,
+                                       None, FAKE, FAKE, 1 << 20, None)
+    assert full(paged(128)) == 0
+    assert full(paged(256, n_pages=-1)) == 1
+    ri = lambda c: L.csa2_index_reindex(C.byref(c), FAKE, FAKE, FAKE, FAKE, 0, FAKE, 64, 8, 32,
+                                        FAKE, FAKE, 1 << 20, None)
+    assert ri(paged(64)) == 0
+    assert ri(paged(48)) == 2

@@ -5,7 +5,9 @@ benchmark times.
   [Full + 3 Reuse] + 4 x [Reindex + 3 Reuse]; group_64k_b32: 32 x 65,536,
   Full + 3 Reuse; hier_256k_b8: 8 x 262,144, Full + Reindex + 3 Reuse.  Every
   output of the step is checked: block maxima, pool, the Full and Reindex index
-  sets, and every layer's attention output.
+  sets, and every layer's attention output.  decoder20_1m_b4 also runs every
+  call on a paged copy of the cache (256-token pages over a shuffled pool), which
+  must give the contiguous cache's outputs bit for bit.
 * prefill_8k_over_128k: 8,192 causal queries over a 131,072-position prefix
   plus the chunk itself (seq = 0 for all, ctx_i = 131,073 + i).  The GPU runs all
   8,192 queries in one call per stage; the oracle checks a strided sample.
@@ -24,7 +26,7 @@ import pytest
 
 import oracle as O
 from fp4_kv_cache_decode_amd import datagen as G
-from parity import ATTN_TOL, REL_EXEMPT, block_scores, check_index_set, fill_both
+from parity import ATTN_TOL, REL_EXEMPT, block_scores, check_index_set, fill_both, shuffled_pages
 
 pytestmark = [pytest.mark.gpu, pytest.mark.timeout(1200)]
 
@@ -67,7 +69,14 @@ def test_decode_step_full_size(K, name):
     t0 = time.time()
     oc = O.Cache(wl.n_seq, wl.cap, L, wl.w_cap)
     gc = K.Cache(wl.n_seq, wl.cap, L, wl.w_cap)
-    fill_both(seed, wl.n_seq, N, L, oc, gc, chunk=G.CHUNK, workers=16)
+    gp = None
+    if name == "decoder20_1m_b4":
+        P = 256
+        table, n_pages = shuffled_pages(seed, wl.n_seq, wl.cap, P, [N] * wl.n_seq)
+        gp = K.Cache(wl.n_seq, wl.cap, L, wl.w_cap, page_tokens=P, n_pages=n_pages,
+                     page_table=torch.from_numpy(table))
+    fill_both(seed, wl.n_seq, N, L, oc, gc if gp is None else (gc, gp), chunk=G.CHUNK,
+              workers=16)
     torch.cuda.synchronize()
     _say(f"  caches built in {time.time() - t0:.1f}s")
     # the stored bytes are identical (quantise-on-write parity at full size)
@@ -86,6 +95,17 @@ def test_decode_step_full_size(K, name):
     ws_sel = K.alloc_workspace(K.OP_SELECT_POOL, B, N)
     ws_at = K.alloc_workspace(K.OP_DECODE_ATTN, B)
     kvg = torch.empty((B, G.TOPK, K.RECORD), dtype=torch.uint8, device="cuda")
+    kvg_p = torch.empty_like(kvg)
+
+    def paged_same(fn, *outs):
+        """Run fn(cache) on the paged copy into fresh buffers shaped like outs,
+        then require the contiguous results bit for bit."""
+        if gp is None:
+            return
+        got = fn(gp)
+        torch.cuda.synchronize()
+        for g, o in zip(got, outs):
+            assert torch.equal(g, o)
 
     opool = oidx = None
     gpu_chain_equal = True
@@ -100,6 +120,16 @@ def test_decode_step_full_size(K, name):
             K.index_select_pool(M, dctx, N, gpool_t, ws_sel)
             K.index_reindex(gc, dev(qi), dev(wi), dseq, dctx, gpool_t, gidx_t, ws_ri)
             torch.cuda.synchronize()
+
+            def full_chain(c):
+                Mx, px, ix = M.clone(), torch.empty_like(gpool_t), torch.empty_like(gidx_t)
+                for b in range(B):                    # every block the scan must write
+                    Mx[b, :-(-int(ctx[b]) // 8)] = float("nan")
+                K.index_block_scores(c, dev(qi), dev(wi), dseq, dctx, N, Mx)
+                K.index_select_pool(Mx, dctx, N, px, ws_sel)
+                K.index_reindex(c, dev(qi), dev(wi), dseq, dctx, px, ix, ws_ri)
+                return Mx, px, ix
+            paged_same(full_chain, M, gpool_t, gidx_t)
             opool, oidx, kb, kp = oc.index_full(qi, wi, seq, ctx)
             gM, gpool, gidx = M.cpu().numpy(), gpool_t.cpu().numpy(), gidx_t.cpu().numpy()
             for b in range(B):
@@ -113,6 +143,12 @@ def test_decode_step_full_size(K, name):
             # Reindex on the oracle's pool (isolated) ...
             K.index_reindex(gc, dev(qi), dev(wi), dseq, dctx, dev(opool), gidx_t, ws_ri)
             torch.cuda.synchronize()
+
+            def reindex(c):
+                ix = torch.empty_like(gidx_t)
+                K.index_reindex(c, dev(qi), dev(wi), dseq, dctx, dev(opool), ix, ws_ri)
+                return (ix,)
+            paged_same(reindex, gidx_t)
             oidx, kp = oc.index_reindex(qi, wi, seq, ctx, opool)
             gidx = gidx_t.cpu().numpy()
             for b in range(B):
@@ -126,12 +162,21 @@ def test_decode_step_full_size(K, name):
         gather = dict(kvg_in=kvg) if mode == "R" else dict(kvg_out=kvg)
         K.decode_attn(gc, l, dev(q), dev(oidx), dseq, dctx, out_t, ws_at, **gather)
         torch.cuda.synchronize()
+
+        def attend(c):
+            ox = torch.empty_like(out_t)
+            g = dict(kvg_in=kvg_p) if mode == "R" else dict(kvg_out=kvg_p)
+            K.decode_attn(c, l, dev(q), dev(oidx), dseq, dctx, ox, ws_at, **g)
+            return (ox,)
+        paged_same(attend, out_t)
         want = oc.decode_attn(l, q, oidx, seq, ctx)
         err = float(np.max(np.abs(out_t.cpu().numpy() - want)))
         assert err <= ATTN_TOL, (l, err)
         if mode != "R":
             _say(f"  layer {l} attention max-abs err {err:.3g}")
     _say(f"  GPU index sets equal the oracle's in every layer: {gpu_chain_equal}")
+    if gp is not None:
+        _say("  paged cache (256-token pages): every output bit-identical")
 
 
 def test_prefill_chunk_8k_over_128k(K):
