@@ -26,3 +26,22 @@ def test_streams_are_distinct_and_shaped():
     q, w = G.index_queries(0, 0, 5)
     assert q.shape == (5, G.HI, G.DI) and w.shape == (5, G.HI)
     assert np.all((w >= 0) & (w < 1))
+
+
+def test_page_table_layout():
+    """A fragmented page layout: each sequence owns exactly the pages its rows
+    need, no physical page is owned twice, the spare pages are owned by nobody,
+    the rest of each row is -1, and the draw is seeded."""
+    table, n_pages = G.page_table(3, 3, 1024, 64, [1000, 64, 1], spare=5)
+    assert table.shape == (3, 16) and table.dtype == np.int32
+    assert n_pages == 16 + 1 + 1 + 5
+    need = [16, 1, 1]
+    for s in range(3):
+        assert (table[s, :need[s]] >= 0).all() and (table[s, need[s]:] == -1).all()
+    owned = table[table >= 0]
+    assert owned.size == 18 and np.unique(owned).size == 18
+    assert owned.max() < n_pages
+    again, _ = G.page_table(3, 3, 1024, 64, [1000, 64, 1], spare=5)
+    assert np.array_equal(table, again)
+    other, _ = G.page_table(4, 3, 1024, 64, [1000, 64, 1], spare=5)
+    assert not np.array_equal(table, other)
