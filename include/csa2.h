@@ -134,7 +134,8 @@ enum {
  * quantised after RoPE; sliding-window KV kept in FP8 ([P4] "FP4 and SWA
  * Bounded Replay"; [P1] "CSA2 and FP4 KV caching").
  *   k, v      [n][128] fp32, post-RoPE main K and V rows -> record at
- *             kv[seq[i]][pos[i]].  Per 16-channel group: scale code =
+ *             kv[seq[i]][pos[i]] (for a paged cache, the row the page table
+ *             gives for that position).  Per 16-channel group: scale code =
  *             E4M3(fp32(amax)/6) rounded to nearest even and saturated at 448;
  *             each nibble = nearest E2M1 value of x/scale (ties to even,
  *             saturating at 6, sign of x kept); a zero scale gives zero codes.
@@ -143,7 +144,9 @@ enum {
  *             pos[i] % w_cap of every layer's window store, E4M3(x/scale).
  *   win       may be NULL when win_k/win_v are NULL.
  *   seq, pos  [n] device; pos must lie in [0, cap).  Rows with seq or pos out of
- *             range are skipped.  Rows are written in parallel: duplicate
+ *             range are skipped.  A paged cache must own a page for every pos
+ *             written (an entry outside [0, n_pages) is clamped, so the row
+ *             lands in some other page).  Rows are written in parallel: duplicate
  *             (seq, pos) pairs, or window rows of one call that share a slot
  *             (same seq, equal pos % w_cap), race.
  */
