@@ -267,11 +267,14 @@ __global__ void __launch_bounds__(AT_THREADS) attn_tile_kernel(TileArgs a) {
             }
         } else {
             const int64_t u0 = N > WINDOW ? N - WINDOW : 0;
-            const int64_t u = u0 + (int64_t)(tile - a.n_main) * TILE + e;
-            ok = seq_ok && u < N;
+            const int off = (tile - a.n_main) * TILE + e;               // < 128 <= w_cap
+            ok = seq_ok && u0 + off < N;
             if (ok) {
+                // (u0 + off) mod w_cap from the uniform u0 mod w_cap: one subtract
+                int32_t w = (int32_t)(u0 % a.w_cap) + off;
+                w = w >= a.w_cap ? w - a.w_cap : w;
                 const int64_t slot =
-                    (((int64_t)a.layer * a.n_seq + s) * a.w_cap + u % a.w_cap) * D + 32 * q4;
+                    (((int64_t)a.layer * a.n_seq + s) * a.w_cap + w) * D + 32 * q4;
                 const uint4* kp = reinterpret_cast<const uint4*>(a.wk + slot);
                 const uint4* vp = reinterpret_cast<const uint4*>(a.wv + slot);
                 const uint4 k0 = kp[0], k1 = kp[1], v0 = vp[0], v1 = vp[1];

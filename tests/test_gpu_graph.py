@@ -1,8 +1,9 @@
 """HIP-graph capture of a decode step: replays match eager launches exactly.
 
-The step (quantise-on-write, Full indexer, Reindex, attention) is captured once
-and replayed several times with eager work and synchronisations in between;
-every replay must reproduce the eager results bit for bit.
+The step (quantise-on-write, Full indexer, Reindex, attention with the group's
+gathered records) is captured once and replayed several times with eager work
+and synchronisations in between; every replay must reproduce the eager results
+bit for bit.  The same holds for a paged cache (shuffled 128-token pages).
 """
 import numpy as np
 import pytest
@@ -14,12 +15,19 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 
-def test_graph_replay_matches_eager():
+@pytest.mark.parametrize("page_tokens", [0, 128])
+def test_graph_replay_matches_eager(page_tokens):
     if not torch.cuda.is_available():
         pytest.skip("no GPU")
     from fp4_kv_cache_decode_amd import csa2 as K
     B, N, L = 3, 40000, 3
-    gc = K.Cache(B, N, L)
+    if page_tokens:
+        cap = -(-N // page_tokens) * page_tokens
+        table, n_pages = G.page_table(23, B, cap, page_tokens, [N] * B)
+        gc = K.Cache(B, cap, L, page_tokens=page_tokens, n_pages=n_pages,
+                     page_table=torch.from_numpy(table))
+    else:
+        gc = K.Cache(B, N, L)
     fill_both(23, B, N, L, None, gc)
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     seq, ctx = dev(np.arange(B, dtype=np.int32)), dev(np.array([N, N - 7, 20000], np.int64))
@@ -37,6 +45,7 @@ def test_graph_replay_matches_eager():
     ws_sel = K.alloc_workspace(K.OP_SELECT_POOL, B, N)
     ws_ri = K.alloc_workspace(K.OP_INDEX_REINDEX, B)
     ws_at = K.alloc_workspace(K.OP_DECODE_ATTN, B)
+    kvg = torch.zeros((B, 512, K.RECORD), dtype=torch.uint8, device="cuda")
 
     def step():
         K.quantize_kv(gc, new["k"], new["v"], seq, new["pos"], idx_k=new["ik"], win_k=new["wk"],
@@ -46,22 +55,22 @@ def test_graph_replay_matches_eager():
         K.index_reindex(gc, q0, w0, seq, ctx, pool, idx, ws_ri)
         K.decode_attn(gc, 0, qa[0], idx, seq, ctx, out[0], ws_at)
         K.index_reindex(gc, q1, w1, seq, ctx, pool, idx, ws_ri)
-        for l in (1, 2):
-            K.decode_attn(gc, l, qa[l], idx, seq, ctx, out[l], ws_at)
+        K.decode_attn(gc, 1, qa[1], idx, seq, ctx, out[1], ws_at, kvg_out=kvg)
+        K.decode_attn(gc, 2, qa[2], idx, seq, ctx, out[2], ws_at, kvg_in=kvg)
 
     step()
     torch.cuda.synchronize()
-    want = [t.clone() for t in (pool, idx, out, gc.kv[:, N - 8:], gc.wk)]
+    want = [t.clone() for t in (pool, idx, out, gc.kv, gc.wk, kvg)]
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=torch.cuda.Stream()):
         step()
     for rep in range(4):
-        for t in (pool, idx, out):
-            t.fill_(-7)
+        for t in (pool, idx, out, kvg):
+            t.fill_(-7 if t.dtype != torch.uint8 else 7)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        got = (pool, idx, out, gc.kv[:, N - 8:], gc.wk)
+        got = (pool, idx, out, gc.kv, gc.wk, kvg)
         for a, b in zip(got, want):
             assert torch.equal(a, b), f"replay {rep} differs"
         step()                                  # eager work between replays

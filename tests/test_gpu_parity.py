@@ -490,3 +490,37 @@ def test_decode_attn_window_scales(K, B, wv_scale):
     err = float(np.max(np.abs(out.cpu().numpy() - want)))
     _say(f"  max-abs err {err:.3g}")
     assert err <= 1e-4 * max(1.0, float(np.max(np.abs(want))))
+
+
+@pytest.mark.parametrize("B", [3, 96])
+def test_maximum_pool_and_topk(K, B):
+    """The largest sizes the library takes: a 4,096-block pool (32,768 positions
+    scored per query, selected by the 32-per-thread top-k) and top-2,048
+    positions, then attention over 2,048 + 128 entries on the tile kernel (B = 3)
+    and the split stream kernel (B = 96)."""
+    _say(f"maximum pool / topk B={B}")
+    N, n_seq, L = 50000, 3, 2
+    oc = O.Cache(n_seq, N, L)
+    gc = K.Cache(n_seq, N, L)
+    fill_both(83, n_seq, N, L, oc, gc)
+    seq = (np.arange(B) % n_seq).astype(np.int32)
+    ctx = np.array([N, N - 3, 33001], np.int64)[seq]
+    q, w = G.index_queries(83, 0, B)
+    gpool, gidx = _run_full(K, gc, q, w, seq, ctx, N, n_blocks=4096, topk=2048)
+    rows = range(B) if B <= 3 else (0, 1, 2, 50, 95)
+    sub = np.array(list(rows))
+    nd = _check_full(oc, q[sub], w[sub], seq[sub], ctx[sub], gpool[sub], gidx[sub], 4096, 2048)
+    _say(f"  exempt differences: {nd}")
+    # attention over the oracle's top-2,048 sets of the checked rows (the rest: the GPU's)
+    _, oidx, _, _ = oc.index_full(q[sub], w[sub], seq[sub], ctx[sub], n_blocks=4096, topk=2048)
+    idx = gidx.copy()
+    idx[sub] = oidx
+    qa = G.attn_queries(83, 1, B)
+    out = torch.empty((B, 16, 128), dtype=torch.float32, device="cuda")
+    K.decode_attn(gc, 1, dev(qa), dev(idx), dev(seq), dev(ctx), out,
+                  K.alloc_workspace(K.OP_DECODE_ATTN, B, topk=2048))
+    torch.cuda.synchronize()
+    want = oc.decode_attn(1, qa[sub], oidx, seq[sub], ctx[sub])
+    err = float(np.max(np.abs(out.cpu().numpy()[sub] - want)))
+    _say(f"  attention max-abs err {err:.3g}")
+    assert err <= 1e-4
