@@ -48,6 +48,7 @@ struct ScoreArgs {
     int64_t out_stride;
     PageMap pm;              // page table of a paged cache (table null otherwise)
     int32_t n_seq;
+    int32_t n_queries;       // B (rows of q_idx / out)
     int32_t n_blocks;        // pool mode
     int32_t keys_per_wg;
     float scale;
@@ -70,11 +71,8 @@ __device__ __forceinline__ void load_key(Raw& r, const ScoreArgs& a, const uint8
     r.d[3] = p[3];
 }
 
-// Score of one key (64 E4M3 codes) against the workgroup's query; wh already
-// carries the key scale (w_h * max(0, s*d) = (w_h * s) * max(0, d) for s > 0).
-__device__ __forceinline__ float key_score(const Raw& r, const float* __restrict__ q,
-                                           const float (&wh)[4]) {
-    float kf[64];
+// One key's 64 E4M3 codes as fp32 (exact).
+__device__ __forceinline__ void key_f32(const Raw& r, float (&kf)[64]) {
     const uint32_t dw[16] = {r.d[0].x, r.d[0].y, r.d[0].z, r.d[0].w, r.d[1].x, r.d[1].y,
                              r.d[1].z, r.d[1].w, r.d[2].x, r.d[2].y, r.d[2].z, r.d[2].w,
                              r.d[3].x, r.d[3].y, r.d[3].z, r.d[3].w};
@@ -87,6 +85,12 @@ __device__ __forceinline__ float key_score(const Raw& r, const float* __restrict
         kf[4 * i + 2] = hi.x;
         kf[4 * i + 3] = hi.y;
     }
+}
+
+// Score of one key against one query; wh already carries the key scale
+// (w_h * max(0, s*d) = (w_h * s) * max(0, d) for s > 0).
+__device__ __forceinline__ float key_dot(const float (&kf)[64], const float* __restrict__ q,
+                                         const float (&wh)[4]) {
     // two accumulator chains per head (a single 64-long chain measured slower)
     float s = 0.0f;
 #pragma unroll
@@ -101,6 +105,13 @@ __device__ __forceinline__ float key_score(const Raw& r, const float* __restrict
         s = fmaf(wh[h], fmaxf(a0 + a1, 0.0f), s);
     }
     return s + 0.0f;
+}
+
+__device__ __forceinline__ float key_score(const Raw& r, const float* __restrict__ q,
+                                           const float (&wh)[4]) {
+    float kf[64];
+    key_f32(r, kf);
+    return key_dot(kf, q, wh);
 }
 
 // q, keys and out are distinct buffers (restrict), so the query loads are
@@ -243,34 +254,36 @@ __device__ __forceinline__ void wait_vm() {
 // memory latency exposed).
 constexpr int SCAN_WAVES = 16;
 constexpr int SCAN_THREADS = SCAN_WAVES * 64;
+constexpr int SCAN_GROUP = 4;            // queries per key pass in large batches
+constexpr int32_t SCAN_GROUP_MIN_B = 1024;
 
-template <bool PAGED>
-__global__ void __launch_bounds__(SCAN_THREADS)
-scan_kernel(ScoreArgs a, const float* __restrict__ q_all, const uint8_t* __restrict__ idxk,
-            float* __restrict__ out_all, int64_t zero) {
-    __shared__ __attribute__((aligned(16))) uint8_t ring[SCAN_WAVES][SCAN_STAGES][SCAN_STEP_BYTES];
-    __shared__ int next_step;
-    const int b = blockIdx.y;
+// Scores one key stream, sequence s keys [wg0, min(wg0 + keys_per_wg, N)),
+// against NQ queries: rows bq[], visible lengths nq[] (N is the largest).  The
+// caller has zeroed next_step and synchronised; every wave calls this with the
+// same (uniform) arguments.
+template <bool PAGED, int NQ>
+__device__ __forceinline__ void scan_stream(const ScoreArgs& a, const float* __restrict__ q_all,
+                                            const uint8_t* __restrict__ idxk,
+                                            float* __restrict__ out_all, int64_t zero,
+                                            uint8_t* my_ring, int* next_step, int32_t s,
+                                            const int (&bq)[NQ], const int64_t (&nq)[NQ],
+                                            int64_t N) {
     const int lane = threadIdx.x & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-    const int64_t N = clamp64(a.ctx[b], 0, a.max_ctx);
-    const int32_t s = a.seq[b];
-    if (s < 0 || s >= a.n_seq) return;
     const int64_t wg0 = (int64_t)blockIdx.x * a.keys_per_wg;
-    if (wg0 >= N) return;
     const int64_t wg_end = wg0 + a.keys_per_wg < N ? wg0 + a.keys_per_wg : N;
     const int n_steps = (int)((wg_end - wg0 + STEP - 1) / STEP);
-    if (threadIdx.x == 0) next_step = 0;
-    __syncthreads();
 
     const uint8_t* keys = idxk + (int64_t)s * a.cap * IDX_DIM;
-    const float* q = q_all + (int64_t)b * IDX_HEADS * IDX_DIM;
-    float wh[4];
+    const float* q[NQ];
+    float wh[NQ][4];
+    float* out[NQ];
 #pragma unroll
-    for (int h = 0; h < 4; ++h) wh[h] = a.w[(int64_t)b * IDX_HEADS + h] * a.scale;
-    float* out = out_all + (int64_t)b * a.out_stride;
-
-    uint8_t* const my_ring = &ring[wave][0][0];
+    for (int j = 0; j < NQ; ++j) {
+        q[j] = q_all + (int64_t)bq[j] * IDX_HEADS * IDX_DIM;
+#pragma unroll
+        for (int h = 0; h < 4; ++h) wh[j][h] = a.w[(int64_t)bq[j] * IDX_HEADS + h] * a.scale;
+        out[j] = out_all + (int64_t)bq[j] * a.out_stride;
+    }
     const uint32_t lds0 = (uint32_t)(uintptr_t)my_ring;
 
     // load side: lane l fills position l & 3 of key l >> 2 of each 1 KB group
@@ -286,7 +299,7 @@ scan_kernel(ScoreArgs a, const float* __restrict__ q_all, const uint8_t* __restr
     // next step of the workgroup for this wave, or -1 when none is left
     auto grab = [&]() -> int {
         int t = 0;
-        if (lane == 0) t = atomicAdd(&next_step, 1);
+        if (lane == 0) t = atomicAdd(next_step, 1);
         t = __builtin_amdgcn_readfirstlane(t);
         return t < n_steps ? t : -1;
     };
@@ -341,19 +354,91 @@ scan_kernel(ScoreArgs a, const float* __restrict__ q_all, const uint8_t* __restr
 #pragma unroll
         for (int m = 0; m < 4; ++m)
             r.d[m] = *reinterpret_cast<const uint4*>(rd[m] + slot * SCAN_STEP_BYTES);
-        float sc = key_score(r, q + zero * k0, wh);
-        const bool whole = k0 + STEP <= N;    // uniform
-        if (!whole) sc = k0 + lane < N ? sc : NEG_INF;
-        float mx = fmaxf(sc, dpp_f32<DPP_XOR1>(sc));
-        mx = fmaxf(mx, dpp_f32<DPP_XOR2>(mx));
-        mx = fmaxf(mx, __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(mx), 0x101f)));
-        // lanes 8m..8m+7 hold block k0/8 + m; a block is visible iff its first key is
-        float* ob = out + (k0 >> 3);
-        if ((lane & 7) == 0 && (whole || k0 + lane < N)) ob[lane >> 3] = mx;
+        // the key is converted once and scored against every query of the stream
+        float kf[64];
+        key_f32(r, kf);
+#pragma unroll
+        for (int j = 0; j < NQ; ++j) {
+            float sc = key_dot(kf, q[j] + zero * k0, wh[j]);
+            const bool whole = k0 + STEP <= nq[j];    // uniform
+            if (!whole) sc = k0 + lane < nq[j] ? sc : NEG_INF;
+            float mx = fmaxf(sc, dpp_f32<DPP_XOR1>(sc));
+            mx = fmaxf(mx, dpp_f32<DPP_XOR2>(mx));
+            mx = fmaxf(mx,
+                       __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(mx), 0x101f)));
+            // lanes 8m..8m+7 hold block k0/8 + m; a block is visible iff its first key is
+            float* ob = out[j] + (k0 >> 3);
+            if ((lane & 7) == 0 && (whole || k0 + lane < nq[j])) ob[lane >> 3] = mx;
+        }
         return true;
     };
     static_assert(SCAN_STAGES == 2, "the slot rotation below is written out for 2 slots");
     while (step(0) && step(1)) {
+    }
+}
+
+// QPW = 1: one query per workgroup row (decode batches).  QPW > 1: the
+// workgroup row serves queries QPW*y .. QPW*y + QPW - 1 (chunked prefill, where
+// a chunk's queries read one sequence): when they share the sequence, each key
+// is loaded and converted once and scored against all of them; otherwise they
+// are scanned one after another.
+template <bool PAGED, int QPW>
+__global__ void __launch_bounds__(SCAN_THREADS)
+scan_kernel(ScoreArgs a, const float* __restrict__ q_all, const uint8_t* __restrict__ idxk,
+            float* __restrict__ out_all, int64_t zero) {
+    __shared__ __attribute__((aligned(16))) uint8_t ring[SCAN_WAVES][SCAN_STAGES][SCAN_STEP_BYTES];
+    __shared__ int next_step;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    uint8_t* const my_ring = &ring[wave][0][0];
+    const int64_t wg0 = (int64_t)blockIdx.x * a.keys_per_wg;
+    auto start = [&]() {
+        if (threadIdx.x == 0) next_step = 0;
+        __syncthreads();
+    };
+    if (QPW == 1) {
+        const int bq[1] = {(int)blockIdx.y};
+        const int64_t nq[1] = {clamp64(a.ctx[bq[0]], 0, a.max_ctx)};
+        const int32_t s = a.seq[bq[0]];
+        if (s < 0 || s >= a.n_seq || wg0 >= nq[0]) return;
+        start();
+        scan_stream<PAGED, 1>(a, q_all, idxk, out_all, zero, my_ring, &next_step, s, bq, nq,
+                              nq[0]);
+        return;
+    }
+    // the group's queries; rows past the batch get length 0 (never written)
+    // and borrow the first row's query and weights
+    const int b0 = (int)blockIdx.y * QPW;
+    int bq[QPW];
+    int64_t nq[QPW];
+    int32_t sq[QPW];
+    bool shared = true;
+    int64_t N = 0;
+#pragma unroll
+    for (int j = 0; j < QPW; ++j) {
+        const bool in = b0 + j < a.n_queries;
+        bq[j] = in ? b0 + j : b0;
+        sq[j] = a.seq[bq[j]];
+        const bool ok = in && sq[j] >= 0 && sq[j] < a.n_seq;
+        nq[j] = ok ? clamp64(a.ctx[bq[j]], 0, a.max_ctx) : 0;
+        shared &= !ok || sq[j] == sq[0];
+        N = nq[j] > N ? nq[j] : N;
+    }
+    shared &= sq[0] >= 0 && sq[0] < a.n_seq;
+    if (shared) {
+        if (wg0 >= N) return;
+        start();
+        scan_stream<PAGED, QPW>(a, q_all, idxk, out_all, zero, my_ring, &next_step, sq[0], bq,
+                                nq, N);
+        return;
+    }
+    for (int j = 0; j < QPW; ++j) {
+        if (wg0 >= nq[j]) continue;       // also an absent or invalid row (length 0)
+        const int bj[1] = {bq[j]};
+        const int64_t nj[1] = {nq[j]};
+        start();
+        scan_stream<PAGED, 1>(a, q_all, idxk, out_all, zero, my_ring, &next_step, sq[j], bj, nj,
+                              nj[0]);
+        __syncthreads();                  // every wave is done with the ring and the counter
     }
 }
 
@@ -374,7 +459,10 @@ hipError_t launch_score_blocks(const csa2_cache& c, const float* q_idx, const fl
                                const int32_t* seq, const int64_t* ctx, int32_t B,
                                int64_t max_ctx, int64_t m_stride, float* M,
                                hipStream_t stream) {
-    const int32_t keys_per_wg = scan_keys_per_wg(B, max_ctx);
+    // batches of prefill size score four queries per key pass
+    const int qpw = B >= SCAN_GROUP_MIN_B ? SCAN_GROUP : 1;
+    const int32_t rows = (B + qpw - 1) / qpw;
+    const int32_t keys_per_wg = scan_keys_per_wg(rows, max_ctx);
     ScoreArgs a{};
     a.idxk = c.idxk;
     a.q_idx = q_idx;
@@ -387,16 +475,26 @@ hipError_t launch_score_blocks(const csa2_cache& c, const float* q_idx, const fl
     a.out_stride = m_stride;
     a.pm = page_map(c);
     a.n_seq = c.n_seq;
+    a.n_queries = B;
     a.keys_per_wg = keys_per_wg;
     a.scale = c.idxk_scale;
-    dim3 grid((unsigned)((max_ctx + keys_per_wg - 1) / keys_per_wg), (unsigned)B);
+    dim3 grid((unsigned)((max_ctx + keys_per_wg - 1) / keys_per_wg), (unsigned)rows);
     if (grid.x == 0) return hipSuccess;
-    if (c.page_table)
-        hipLaunchKernelGGL(scan_kernel<true>, grid, dim3(SCAN_THREADS), 0, stream, a, q_idx,
-                           c.idxk, M, (int64_t)0);
-    else
-        hipLaunchKernelGGL(scan_kernel<false>, grid, dim3(SCAN_THREADS), 0, stream, a, q_idx,
-                           c.idxk, M, (int64_t)0);
+    const dim3 blk(SCAN_THREADS);
+    const int64_t z = 0;
+    if (qpw == 1) {
+        if (c.page_table)
+            hipLaunchKernelGGL((scan_kernel<true, 1>), grid, blk, 0, stream, a, q_idx, c.idxk, M, z);
+        else
+            hipLaunchKernelGGL((scan_kernel<false, 1>), grid, blk, 0, stream, a, q_idx, c.idxk, M, z);
+    } else {
+        if (c.page_table)
+            hipLaunchKernelGGL((scan_kernel<true, SCAN_GROUP>), grid, blk, 0, stream, a, q_idx,
+                               c.idxk, M, z);
+        else
+            hipLaunchKernelGGL((scan_kernel<false, SCAN_GROUP>), grid, blk, 0, stream, a, q_idx,
+                               c.idxk, M, z);
+    }
     return hipGetLastError();
 }
 

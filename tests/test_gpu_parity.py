@@ -524,3 +524,49 @@ def test_maximum_pool_and_topk(K, B):
     err = float(np.max(np.abs(out.cpu().numpy()[sub] - want)))
     _say(f"  attention max-abs err {err:.3g}")
     assert err <= 1e-4
+
+
+def test_block_scores_query_groups(K):
+    """Batches of 1,024+ queries score four queries per key pass when they read
+    one sequence (chunked prefill) and one after another otherwise.  Groups of
+    one sequence, mixed groups, a partial last group, ragged and empty contexts
+    and an out-of-range sequence: block maxima against the oracle on a sample,
+    unwritten entries untouched, and bit for bit equal to the same queries
+    scored in batches small enough for one query per workgroup row."""
+    _say("block scores, grouped queries")
+    N, n_seq, B = 5000, 3, 1030
+    oc, gc = _setup(K, 97, n_seq, N)
+    rng = np.random.default_rng(97)
+    seq = np.zeros(B, np.int32)
+    seq[512:1024] = np.arange(512, 1024) % n_seq          # mixed groups
+    seq[1024:] = 2                                          # partial last group (1028, 1029)
+    seq[700] = -1                                           # out of range: row untouched
+    ctx = rng.integers(1, N + 1, B).astype(np.int64)
+    ctx[:256] = N - np.arange(256) // 2                     # groups of (nearly) equal length
+    ctx[300] = 0                                            # nothing visible
+    ctx[1029] = N
+    q, w = G.index_queries(97, 0, B)
+    stride = K.block_stride(N)
+    M = torch.full((B, stride), float("nan"), dtype=torch.float32, device="cuda")
+    K.index_block_scores(gc, dev(q), dev(w), dev(seq), dev(ctx), N, M)
+    torch.cuda.synchronize()
+    Mg = M.cpu().numpy()
+    # the same queries in small batches (one query per workgroup row)
+    Ms = torch.full((B, stride), float("nan"), dtype=torch.float32, device="cuda")
+    for b0 in range(0, B, 300):
+        b1 = min(B, b0 + 300)
+        K.index_block_scores(gc, dev(q[b0:b1]), dev(w[b0:b1]), dev(seq[b0:b1]), dev(ctx[b0:b1]),
+                             N, Ms[b0:b1])
+    torch.cuda.synchronize()
+    valid = seq >= 0
+    assert np.array_equal(Mg[valid], Ms.cpu().numpy()[valid], equal_nan=True)
+    nb = -(-ctx // 8)
+    for b in range(B):
+        if valid[b]:
+            assert np.isnan(Mg[b, nb[b]:]).all(), b
+            assert not np.isnan(Mg[b, :nb[b]]).any(), b
+    sample = [0, 1, 2, 3, 255, 256, 300, 511, 512, 513, 514, 515, 777, 1023, 1024, 1028, 1029]
+    for b in sample:
+        sc = oc.scores(int(seq[b]), q[b], w[b], int(ctx[b]))
+        want = block_scores(sc, int(ctx[b]))
+        np.testing.assert_allclose(Mg[b, :want.size], want, rtol=2e-6, atol=1e-6)
