@@ -118,10 +118,14 @@ __device__ __forceinline__ float key_score(const Raw& r, const float* __restrict
 // provably unclobbered and can be scalar loads.  `zero` is 0 at run time; adding
 // zero * step to the query address makes it loop-variant, so the compiler
 // reloads one head at a time (64 SGPRs) instead of hoisting all 256 floats.
-template <bool POOL, bool PAGED>
+// STAGE (pool mode, several steps per wave): the workgroup's slice of the
+// block list is copied to LDS first, so that a step's key loads wait on an LDS
+// read of their block instead of a global load.
+template <bool POOL, bool PAGED, bool STAGE>
 __global__ void __launch_bounds__(SC_THREADS)
 score_kernel(ScoreArgs a, const float* __restrict__ q_all, const uint8_t* __restrict__ idxk,
              float* __restrict__ out_all, int64_t zero) {
+    __shared__ int32_t pslice[STAGE ? CSA2_MAX_POOL : 1];
     const int b = blockIdx.y;
     const int lane = threadIdx.x & 63;
     // wave index is uniform per wave; say so, so that k0 and the query address are SGPRs
@@ -140,11 +144,17 @@ score_kernel(ScoreArgs a, const float* __restrict__ q_all, const uint8_t* __rest
     for (int h = 0; h < 4; ++h) wh[h] = a.w[(int64_t)b * IDX_HEADS + h] * a.scale;
     float* out = out_all + (int64_t)b * a.out_stride;
     const int32_t* pool = POOL ? a.pool + (int64_t)b * a.n_blocks : nullptr;
+    const int64_t blk0 = wg0 >> 3;          // wg0 is a multiple of 256
+    if (STAGE) {
+        const int cnt = (int)(((wg_end + 7) >> 3) - blk0);
+        for (int i = threadIdx.x; i < cnt; i += SC_THREADS) pslice[i] = pool[blk0 + i];
+        __syncthreads();
+    }
 
     // position of item i (pool mode maps through the block list); ok = visible
     auto locate = [&](int64_t i, int64_t& t) -> bool {
         if (POOL) {
-            const int32_t pb = i < n_items ? pool[i >> 3] : -1;
+            const int32_t pb = i < n_items ? (STAGE ? pslice[(i >> 3) - blk0] : pool[i >> 3]) : -1;
             t = (int64_t)pb * BLOCK + (i & 7);
             return pb >= 0 && t < N;
         }
@@ -526,12 +536,24 @@ hipError_t launch_score_pool(const csa2_cache& c, const float* q_idx, const floa
     a.scale = c.idxk_scale;
     const int64_t items = (int64_t)n_blocks * BLOCK;
     dim3 grid((unsigned)((items + a.keys_per_wg - 1) / a.keys_per_wg), (unsigned)B);
-    if (c.page_table)
-        hipLaunchKernelGGL((score_kernel<true, true>), grid, dim3(SC_THREADS), 0, stream, a,
-                           q_idx, c.idxk, S, (int64_t)0);
-    else
-        hipLaunchKernelGGL((score_kernel<true, false>), grid, dim3(SC_THREADS), 0, stream, a,
-                           q_idx, c.idxk, S, (int64_t)0);
+    const bool stage = a.keys_per_wg > STEP * WAVES;      // several steps per wave
+    const dim3 blk(SC_THREADS);
+    const int64_t z = 0;
+    if (c.page_table) {
+        if (stage)
+            hipLaunchKernelGGL((score_kernel<true, true, true>), grid, blk, 0, stream, a, q_idx,
+                               c.idxk, S, z);
+        else
+            hipLaunchKernelGGL((score_kernel<true, true, false>), grid, blk, 0, stream, a, q_idx,
+                               c.idxk, S, z);
+    } else {
+        if (stage)
+            hipLaunchKernelGGL((score_kernel<true, false, true>), grid, blk, 0, stream, a, q_idx,
+                               c.idxk, S, z);
+        else
+            hipLaunchKernelGGL((score_kernel<true, false, false>), grid, blk, 0, stream, a, q_idx,
+                               c.idxk, S, z);
+    }
     return hipGetLastError();
 }
 
