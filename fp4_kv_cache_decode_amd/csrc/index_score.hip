@@ -236,17 +236,30 @@ constexpr int SCAN_STEP_BYTES = STEP * IDX_DIM;   // 4096
 __device__ __forceinline__ int chunk_rot(int j) { return ((j >> 1) ^ (j >> 3)) & 3; }
 
 // m0 is named as clobbered: it carries the LDS address of the copy, and no
-// other code of these kernels keeps a value in m0.
+// other code of these kernels keeps a value in m0.  NT marks the load
+// non-temporal: a decode scan reads each key once per step, and a long
+// context's keys outgrow the caches anyway (measured at the decode shape:
+// 48-52 us instead of 56-58 us for 4 x 1 Mi keys).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
+template <bool NT>
 __device__ __forceinline__ void dma_1k(uint32_t voff, const uint8_t* sbase, uint32_t lds_addr) {
-    asm volatile(
-        "s_mov_b32 m0, %2\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %0, %1"
-        :
-        : "v"(voff), "s"(sbase), "s"(lds_addr)
-        : "memory", "m0");
+    if (NT)
+        asm volatile(
+            "s_mov_b32 m0, %2\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %0, %1 nt"
+            :
+            : "v"(voff), "s"(sbase), "s"(lds_addr)
+            : "memory", "m0");
+    else
+        asm volatile(
+            "s_mov_b32 m0, %2\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %0, %1"
+            :
+            : "v"(voff), "s"(sbase), "s"(lds_addr)
+            : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -270,8 +283,8 @@ constexpr int32_t SCAN_GROUP_MIN_B = 1024;
 // Scores one key stream, sequence s keys [wg0, min(wg0 + keys_per_wg, N)),
 // against NQ queries: rows bq[], visible lengths nq[] (N is the largest).  The
 // caller has zeroed next_step and synchronised; every wave calls this with the
-// same (uniform) arguments.
-template <bool PAGED, int NQ>
+// same (uniform) arguments.  NT: non-temporal key loads (keys read once).
+template <bool PAGED, int NQ, bool NT>
 __device__ __forceinline__ void scan_stream(const ScoreArgs& a, const float* __restrict__ q_all,
                                             const uint8_t* __restrict__ idxk,
                                             float* __restrict__ out_all, int64_t zero,
@@ -324,13 +337,13 @@ __device__ __forceinline__ void scan_stream(const ScoreArgs& a, const float* __r
         const uint32_t l = lds0 + (uint32_t)(slot * SCAN_STEP_BYTES);
         if (kb + STEP <= N) {
 #pragma unroll
-            for (int c = 0; c < 4; ++c) dma_1k(dma_off, g + 1024 * c, l + 1024 * c);
+            for (int c = 0; c < 4; ++c) dma_1k<NT>(dma_off, g + 1024 * c, l + 1024 * c);
         } else {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
                 int64_t j = kb + 16 * c + kl;
                 j = j < N ? j : N - 1;
-                dma_1k((uint32_t)((j - kb) * IDX_DIM + 16 * chunk_here), g, l + 1024 * c);
+                dma_1k<NT>((uint32_t)((j - kb) * IDX_DIM + 16 * chunk_here), g, l + 1024 * c);
             }
         }
     };
@@ -387,11 +400,12 @@ __device__ __forceinline__ void scan_stream(const ScoreArgs& a, const float* __r
     }
 }
 
-// QPW = 1: one query per workgroup row (decode batches).  QPW > 1: the
-// workgroup row serves queries QPW*y .. QPW*y + QPW - 1 (chunked prefill, where
-// a chunk's queries read one sequence): when they share the sequence, each key
-// is loaded and converted once and scored against all of them; otherwise they
-// are scanned one after another.
+// QPW = 1: one query per workgroup row (decode batches; keys are read once, so
+// their loads are non-temporal).  QPW > 1: the workgroup row serves queries
+// QPW*y .. QPW*y + QPW - 1 (chunked prefill, where a chunk's queries read one
+// sequence and the keys are re-read from L2 by every row): when they share the
+// sequence, each key is loaded and converted once and scored against all of
+// them; otherwise they are scanned one after another.
 template <bool PAGED, int QPW>
 __global__ void __launch_bounds__(SCAN_THREADS)
 scan_kernel(ScoreArgs a, const float* __restrict__ q_all, const uint8_t* __restrict__ idxk,
@@ -411,7 +425,7 @@ scan_kernel(ScoreArgs a, const float* __restrict__ q_all, const uint8_t* __restr
         const int32_t s = a.seq[bq[0]];
         if (s < 0 || s >= a.n_seq || wg0 >= nq[0]) return;
         start();
-        scan_stream<PAGED, 1>(a, q_all, idxk, out_all, zero, my_ring, &next_step, s, bq, nq,
+        scan_stream<PAGED, 1, QPW == 1>(a, q_all, idxk, out_all, zero, my_ring, &next_step, s, bq, nq,
                               nq[0]);
         return;
     }
@@ -437,7 +451,7 @@ scan_kernel(ScoreArgs a, const float* __restrict__ q_all, const uint8_t* __restr
     if (shared) {
         if (wg0 >= N) return;
         start();
-        scan_stream<PAGED, QPW>(a, q_all, idxk, out_all, zero, my_ring, &next_step, sq[0], bq,
+        scan_stream<PAGED, QPW, false>(a, q_all, idxk, out_all, zero, my_ring, &next_step, sq[0], bq,
                                 nq, N);
         return;
     }
@@ -446,7 +460,7 @@ scan_kernel(ScoreArgs a, const float* __restrict__ q_all, const uint8_t* __restr
         const int bj[1] = {bq[j]};
         const int64_t nj[1] = {nq[j]};
         start();
-        scan_stream<PAGED, 1>(a, q_all, idxk, out_all, zero, my_ring, &next_step, sq[j], bj, nj,
+        scan_stream<PAGED, 1, false>(a, q_all, idxk, out_all, zero, my_ring, &next_step, sq[j], bj, nj,
                               nj[0]);
         __syncthreads();                  // every wave is done with the ring and the counter
     }
