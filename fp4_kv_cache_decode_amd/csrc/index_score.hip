@@ -8,10 +8,11 @@
 //     score_t = sum_h w_h * max(0, q_h . khat_t),  khat_t = E4M3(code_t) * scale,
 // with 4 heads of 64 dims, and a block's score as the max over its 8 positions.
 //
-// Design (gfx950, wave64): one key per lane, 64 keys (4 KB) per wave step.  The
-// query is the same for the whole workgroup, so it is read as scalar (SGPR)
-// operands of v_fma_f32 straight from the scalar cache, one head (64 floats) at
-// a time: no lane holds a copy of it and no cross-lane reduction is needed.
+// Design (gfx950, wave64): one key per lane, 64 keys (4 KB) per wave step.  A
+// workgroup's query (or its four queries, in prefill-sized batches) is the same
+// for every lane, so it is read as scalar (SGPR) operands of v_fma_f32 straight
+// from the scalar cache, one head (64 floats) at a time: no lane holds a copy
+// of it and no cross-lane reduction is needed.
 // FP8->fp32 uses the packed converter (2 values per instruction); the dot
 // products are plain fp32 FMAs (the 1e-5 relative score budget rules out f16
 // query math).  Block maxima come from DPP/swizzle max over the 8 lanes of a
@@ -21,8 +22,9 @@
 //  - score_kernel<true> scores a Reindex (or the Full layer's second) pass over
 //    the pool's 2,048 runs of 8 positions: latency bound, each lane holding its
 //    key plus the next one in flight in registers;
-//  - scan_kernel scores the whole context of a Full layer: HBM bound, keys
-//    streamed through a per-wave LDS ring (below).
+//  - scan_kernel scores the whole context of a Full layer, keys streamed
+//    through a per-wave LDS ring (below): HBM bound in decode; in a chunked
+//    prefill it scores four queries per key pass and is bound by fp32 VALU.
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
