@@ -229,3 +229,37 @@ def test_prefill_chunk_8k_over_128k(K):
     err = float(np.max(np.abs(got - want)))
     _say(f"  attention max-abs err over the sample {err:.3g}")
     assert err <= ATTN_TOL
+
+
+def test_gather_row_full_size(K):
+    """The gather row's launch configuration: 1,024 queries, each on its own
+    65,536-position sequence (one workgroup per query, no split), a random
+    top-512 set per query plus the window.  Every sequence holds the same rows
+    (as in the benchmark), so the oracle needs one sequence; a strided sample of
+    queries is checked, in all four layers."""
+    B, N, L = 1024, 65536, 4
+    seed = 0
+    _say(f"gather row: B={B} N={N} L={L}")
+    oc = O.Cache(1, N, L)
+    gc = K.Cache(B, N, L)
+    fill_both(seed, 1, N, L, oc, gc, chunk=G.CHUNK)
+    gc.kv[1:].copy_(gc.kv[0:1].expand(B - 1, -1, -1))
+    gc.wk[:, 1:].copy_(gc.wk[:, 0:1].expand(-1, B - 1, -1, -1))
+    gc.wv[:, 1:].copy_(gc.wv[:, 0:1].expand(-1, B - 1, -1, -1))
+    rng = np.random.default_rng(seed)
+    idx = np.sort(np.argpartition(rng.random((B, N), dtype=np.float32), G.TOPK, axis=1)
+                  [:, :G.TOPK], axis=1).astype(np.int32)
+    seq, ctx = np.arange(B, dtype=np.int32), np.full(B, N, np.int64)
+    sample = np.r_[0, 1, np.arange(37, B, 97), B - 1]
+    ws = K.alloc_workspace(K.OP_DECODE_ATTN, B)
+    assert ws.numel() == 1                     # one workgroup per query: no partials
+    out = torch.empty((B, G.H, G.D), dtype=torch.float32, device="cuda")
+    for l in range(L):
+        q = G.attn_queries(seed, l, B)
+        K.decode_attn(gc, l, dev(q), dev(idx), dev(seq), dev(ctx), out, ws)
+        torch.cuda.synchronize()
+        want = oc.decode_attn(l, q[sample], idx[sample], np.zeros(sample.size, np.int32),
+                              ctx[sample])
+        err = float(np.max(np.abs(out.cpu().numpy()[sample] - want)))
+        _say(f"  layer {l}: {sample.size} sampled queries, max-abs err {err:.3g}")
+        assert err <= ATTN_TOL
