@@ -1,0 +1,32 @@
+"""Host-side behaviour of bench.py (no GPU): the one-GPU guard and the source
+hash that ties committed counters to the scan code."""
+import os
+import subprocess
+import sys
+
+from conftest import ROOT
+
+sys.path.insert(0, ROOT)
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
+
+
+def test_code_hash_ignores_comments_and_blank_lines():
+    import bench
+    code = "int f(int x) {\n    return x + 1;  // add one\n}\n"
+    same = "// a header\n\nint f(int x) {\n    return x + 1;\n\n}   \n"
+    other = "int f(int x) {\n    return x + 2;\n}\n"
+    assert bench.code_hash(code) == bench.code_hash(same)
+    assert bench.code_hash(code) != bench.code_hash(other)
+    assert len(bench.code_hash(code)) == 16
+
+
+def test_counter_traffic_needs_matching_workload():
+    import bench
+    assert bench.counter_traffic("no_such_workload") is None
