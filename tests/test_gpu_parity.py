@@ -570,3 +570,47 @@ def test_block_scores_query_groups(K):
         sc = oc.scores(int(seq[b]), q[b], w[b], int(ctx[b]))
         want = block_scores(sc, int(ctx[b]))
         np.testing.assert_allclose(Mg[b, :want.size], want, rtol=2e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("B", [3, 96])
+def test_empty_and_one_token_contexts(K, B):
+    """Queries that see no position (ctx = 0) or one: the Full indexer and a
+    Reindex layer return empty (all -1) or one-entry sets, and attention gives
+    zeros for an empty context, on the tile kernel (B = 3) and the split stream
+    kernel (B = 96)."""
+    _say(f"empty and one-token contexts B={B}")
+    N, n_seq, L = 3000, 3, 2
+    oc, gc = _setup(K, 53, n_seq, N, n_layers=L)
+    seq = (np.arange(B) % n_seq).astype(np.int32)
+    ctx = np.array([0, 1, N], np.int64)[np.arange(B) % 3]
+    q, w = G.index_queries(53, 0, B)
+    gpool, gidx = _run_full(K, gc, q, w, seq, ctx, N)
+    _check_full(oc, q, w, seq, ctx, gpool, gidx, 2048, 512)
+    empty = ctx == 0
+    assert (gpool[empty] == -1).all() and (gidx[empty] == -1).all()
+    one = ctx == 1
+    assert (gidx[one, 0] == 0).all() and (gidx[one, 1:] == -1).all()
+    opool, _, _, _ = oc.index_full(q, w, seq, ctx)
+    q1, w1 = G.index_queries(53, 1, B)
+    idx = torch.empty((B, 512), dtype=torch.int32, device="cuda")
+    K.index_reindex(gc, dev(q1), dev(w1), dev(seq), dev(ctx), dev(opool), idx,
+                    K.alloc_workspace(K.OP_INDEX_REINDEX, B))
+    torch.cuda.synchronize()
+    ridx = idx.cpu().numpy()
+    assert (ridx[empty] == -1).all()
+    oidx, kp = oc.index_reindex(q1, w1, seq, ctx, opool)
+    for b in range(B):
+        sc = oc.scores(int(seq[b]), q1[b], w1[b], int(ctx[b]))
+        check_index_set(ridx[b], oidx[b], lambda t: sc[t], kp[b])
+    # attention on the Full sets; a one-token context's window is slot 0 of
+    # the ring, which both sides read the same way
+    qa = G.attn_queries(53, 1, B)
+    out = torch.full((B, 16, 128), float("nan"), dtype=torch.float32, device="cuda")
+    K.decode_attn(gc, 1, dev(qa), dev(gidx), dev(seq), dev(ctx), out,
+                  K.alloc_workspace(K.OP_DECODE_ATTN, B))
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert (got[empty] == 0.0).all()
+    some = ~empty
+    want = oc.decode_attn(1, qa[some], gidx[some], seq[some], ctx[some])
+    assert float(np.max(np.abs(got[some] - want))) <= 1e-4
