@@ -8,11 +8,14 @@
 // "How the architecture shrinks the KV cache").
 //
 // Select core (one workgroup of 1,024 threads, 16 values per thread in registers):
-//   1. min / max / count of the valid values (block reduction);
-//   2. an LDS histogram over 2,048 bins linear in value between min and max
-//      (a monotone map, so ranks survive; linear bins keep LDS atomics spread
-//      even when every value shares one exponent) and the bin d holding the
-//      k-th largest value;
+//   1. min / max / count of the valid values and the smallest per-thread
+//      maximum (block reduction); when at least k threads hold a valid value,
+//      that minimum is a floor the k-th largest value cannot fall below;
+//   2. an LDS histogram over 2,048 bins linear in value between the floor and
+//      max (a monotone map, so ranks survive; linear bins keep LDS atomics
+//      spread even when every value shares one exponent; values below the floor
+//      stay out, which for 16 values per thread skips most atomics) and the bin
+//      d holding the k-th largest value;
 //   3. values in bins above d are chosen; bin d's values go to an LDS candidate
 //      list.  Up to 256 candidates are ranked directly in (value desc, index
 //      asc) order; larger lists take an 11/11/10-bit radix on the exact order
@@ -82,7 +85,7 @@ struct Shared {
     uint32_t ckey[CAND_CAP];
     uint32_t cidx[CAND_CAP];
     uint32_t wave_u[NT / 64];
-    float wave_f[2][NT / 64];
+    float wave_f[3][NT / 64];
     uint32_t misc[8];        // [0,1] digit search, [2] candidates, [3] flag, [4] valid count
     int32_t pool[NT == BIG_T ? CSA2_MAX_POOL : 1];   // the row's pool (pool mode), in LDS
 };
@@ -182,28 +185,37 @@ __device__ uint32_t block_incl_scan(uint32_t v, Shared<NT>& sh, uint32_t* total)
     return v + before;
 }
 
-// Block-wide count, min and max in one LDS round: each wave reduces its own
-// values (cnt is already the wave's count), then lanes 0 .. NT/64 - 1 of every
-// wave read the waves' partials and a 16-lane DPP reduction leaves the block's
-// result in every lane.  The partial arrays are next written after at least
-// one more barrier (every caller's next phase ends in one before any wave_u /
-// wave_f write).
+// Block-wide statistics in one LDS round: count, min and max of the valid
+// values, and the smallest per-thread maximum with the number of threads that
+// hold a valid value (each such thread has at least one value >= that
+// minimum, so it bounds the k-th largest value from below whenever at least k
+// threads hold one).  Each wave reduces its own values (cnt is already the
+// wave's count), then lanes 0 .. NT/64 - 1 of every wave read the waves'
+// partials and a 16-lane DPP reduction leaves the block's result in every lane.
+// The partial arrays are next written after at least one more barrier (every
+// caller's next phase ends in one before any wave_u / wave_f write).
 template <int NT>
 __device__ void block_stats(uint32_t cnt, float lo, float hi, Shared<NT>& sh, uint32_t* total,
-                            float* mn, float* mx) {
+                            float* mn, float* mx, float* tmax_min, uint32_t* n_thr) {
     static_assert(NT / 64 <= 16, "one 16-lane row holds every wave's partial");
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // this thread's maximum if it holds a valid value (-inf never raises hi)
+    float fl = hi != NEG_INF ? hi : __builtin_huge_valf();
+    const uint32_t thr = (uint32_t)__builtin_popcountll(__ballot(hi != NEG_INF));
     lo = rows_min(lo);
     hi = rows_max(hi);
+    fl = rows_min(fl);
     if (lane == 0) {
         sh.wave_f[0][wave] = lo;
         sh.wave_f[1][wave] = hi;
-        sh.wave_u[wave] = cnt;
+        sh.wave_f[2][wave] = fl;
+        sh.wave_u[wave] = cnt | (thr << 16);   // counts < 2^16 (at most 32,768 values)
     }
     __syncthreads();
     const bool mine = lane < NT / 64;
     float a = mine ? sh.wave_f[0][lane] : __builtin_huge_valf();
     float c = mine ? sh.wave_f[1][lane] : NEG_INF;
+    float e = mine ? sh.wave_f[2][lane] : __builtin_huge_valf();
     uint32_t n = mine ? sh.wave_u[lane] : 0u;
     a = fminf(a, dpp_f32<DPP_XOR1>(a));
     a = fminf(a, dpp_f32<DPP_XOR2>(a));
@@ -213,13 +225,29 @@ __device__ void block_stats(uint32_t cnt, float lo, float hi, Shared<NT>& sh, ui
     c = fmaxf(c, dpp_f32<DPP_XOR2>(c));
     c = fmaxf(c, dpp_f32<DPP_ROR4>(c));
     c = fmaxf(c, dpp_f32<DPP_ROR8>(c));
+    e = fminf(e, dpp_f32<DPP_XOR1>(e));
+    e = fminf(e, dpp_f32<DPP_XOR2>(e));
+    e = fminf(e, dpp_f32<DPP_ROR4>(e));
+    e = fminf(e, dpp_f32<DPP_ROR8>(e));
     n += (uint32_t)__builtin_amdgcn_mov_dpp((int)n, DPP_XOR1, 0xf, 0xf, false);
     n += (uint32_t)__builtin_amdgcn_mov_dpp((int)n, DPP_XOR2, 0xf, 0xf, false);
     n += (uint32_t)__builtin_amdgcn_mov_dpp((int)n, DPP_ROR4, 0xf, 0xf, false);
     n += (uint32_t)__builtin_amdgcn_mov_dpp((int)n, DPP_ROR8, 0xf, 0xf, false);
     *mn = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(a)));
     *mx = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(c)));
-    *total = (uint32_t)__builtin_amdgcn_readfirstlane((int)n);
+    *tmax_min = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(e)));
+    n = (uint32_t)__builtin_amdgcn_readfirstlane((int)n);
+    *total = n & 0xffffu;
+    *n_thr = n >> 16;
+}
+
+// Histogram floor: values below it cannot be among the k largest.  With at
+// least k threads holding a valid value, every one of them holds a value >= the
+// smallest thread maximum, so the k-th largest value is >= that minimum;
+// otherwise the floor is the smallest valid value.
+__device__ __forceinline__ float hist_floor(uint32_t k, float vmin, float tmax_min,
+                                            uint32_t n_thr) {
+    return n_thr >= k ? tmax_min : vmin;
 }
 
 // Digit d of hist[0..nbins) with count(> d) < kk <= count(>= d); returns d and
@@ -278,9 +306,9 @@ __device__ bool select_core(Shared<NT>& sh, const float (&v)[VPT], const uint32_
         lo = fminf(lo, ok ? v[j] : __builtin_huge_valf());
         hi = fmaxf(hi, v[j]);               // -inf never raises the max
     }
-    uint32_t n_valid;
-    float vmin, vmax;
-    block_stats<NT>(cnt, lo, hi, sh, &n_valid, &vmin, &vmax);
+    uint32_t n_valid, n_thr;
+    float vmin, vmax, tmax_min;
+    block_stats<NT>(cnt, lo, hi, sh, &n_valid, &vmin, &vmax, &tmax_min, &n_thr);
     if (t == 0) sh.misc[4] = n_valid;
     if (n_valid <= k) {
 #pragma unroll
@@ -291,13 +319,15 @@ __device__ bool select_core(Shared<NT>& sh, const float (&v)[VPT], const uint32_
         __syncthreads();
         return true;
     }
-    float inv = vmax > vmin ? (float)NB / (vmax - vmin) : 0.0f;
+    // bins linear in value over [floor, max]; values below the floor are absent
+    const float floor_ = hist_floor(k, vmin, tmax_min, n_thr);
+    float inv = vmax > floor_ ? (float)NB / (vmax - floor_) : 0.0f;
     if (!(inv < __builtin_huge_valf())) inv = 0.0f;     // range overflowed: one bin
     uint32_t bin[VPT];
 #pragma unroll
     for (int j = 0; j < VPT; ++j) {
-        const int bb = (int)((v[j] - vmin) * inv);
-        bin[j] = v[j] == NEG_INF ? 0xffffffffu : (uint32_t)(bb < NB - 1 ? bb : NB - 1);
+        const int bb = (int)((v[j] - floor_) * inv);
+        bin[j] = !(v[j] >= floor_) ? 0xffffffffu : (uint32_t)(bb < NB - 1 ? bb : NB - 1);
         if (bin[j] != 0xffffffffu) atomicAdd(&sh.hist[bin[j]], 1u);
     }
     __syncthreads();
@@ -600,9 +630,9 @@ __device__ bool select_run(Shared<BIG_T>& sh, const float (&v)[V], int64_t n_pos
         lo = fminf(lo, ok ? v[j] : __builtin_huge_valf());
         hi = fmaxf(hi, v[j]);               // -inf never raises the max
     }
-    uint32_t n_valid;
-    float vmin, vmax;
-    block_stats<BIG_T>(cnt, lo, hi, sh, &n_valid, &vmin, &vmax);
+    uint32_t n_valid, n_thr;
+    float vmin, vmax, tmax_min;
+    block_stats<BIG_T>(cnt, lo, hi, sh, &n_valid, &vmin, &vmax, &tmax_min, &n_thr);
 
     uint32_t mask = 0;                   // bit j: position Vt + j chosen
     if (n_valid <= k) {
@@ -610,14 +640,16 @@ __device__ bool select_run(Shared<BIG_T>& sh, const float (&v)[V], int64_t n_pos
         for (int j = 0; j < V; ++j) mask |= v[j] != NEG_INF ? 1u << j : 0u;
         __syncthreads();                 // block_stats' partials read before the scan reuses them
     } else {
-        // ---- histogram and the bin d holding the k-th largest value
-        float inv = vmax > vmin ? (float)NB / (vmax - vmin) : 0.0f;
+        // ---- histogram over [floor, max] (values below the floor cannot be
+        // chosen and stay out of it) and the bin d holding the k-th largest
+        const float floor_ = hist_floor(k, vmin, tmax_min, n_thr);
+        float inv = vmax > floor_ ? (float)NB / (vmax - floor_) : 0.0f;
         if (!(inv < __builtin_huge_valf())) inv = 0.0f;     // range overflowed: one bin
         uint32_t bin[V];
 #pragma unroll
         for (int j = 0; j < V; ++j) {
-            const int bb = (int)((v[j] - vmin) * inv);
-            bin[j] = v[j] == NEG_INF ? 0xffffffffu : (uint32_t)(bb < NB - 1 ? bb : NB - 1);
+            const int bb = (int)((v[j] - floor_) * inv);
+            bin[j] = !(v[j] >= floor_) ? 0xffffffffu : (uint32_t)(bb < NB - 1 ? bb : NB - 1);
             if (bin[j] != 0xffffffffu) atomicAdd(&sh.hist[bin[j]], 1u);
         }
         __syncthreads();
