@@ -188,3 +188,67 @@ def test_paged_cache_validation(L):
                                         FAKE, FAKE, 1 << 20, None)
     assert ri(paged(64)) == 0
     assert ri(paged(48)) == 2
+
+
+C_PROGRAM = r"""
+#include <stdio.h>
+#include <string.h>
+#include "csa2.h"
+int main(void) {
+    csa2_cache c;
+    memset(&c, 0, sizeof c);              /* a zeroed tail: contiguous cache */
+    /* no GPU work: sizes and status strings are host functions */
+    size_t part = (size_t)(32 + 2048) * 4;
+    if (csa2_workspace_bytes(CSA2_OP_DECODE_ATTN, 4, 0, 0, 0, 512) != 4 * 10 * part) return 1;
+    if (csa2_workspace_bytes(CSA2_OP_INDEX_REINDEX, 4, 0, 2048, CSA2_BLOCK, 512) != 4 * 16384 * 4)
+        return 2;
+    if (strcmp(csa2_status_string(CSA2_OK), "ok") != 0) return 3;
+    if (csa2_quantize_kv(NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, NULL) !=
+        CSA2_ERR_INVALID_ARG) return 4;
+    printf("c-abi ok %zu\n", sizeof c);
+    return 0;
+}
+"""
+
+
+def _hip_include():
+    return os.environ.get("ROCM_PATH", "/opt/rocm") + "/include"
+
+
+def test_header_compiles_as_c_and_cxx(tmp_path):
+    """include/csa2.h is a plain C header (usable from C11 and C++17)."""
+    import shutil
+    import subprocess
+    src = tmp_path / "h.c"
+    src.write_text('#include "csa2.h"\nint main(void) { return CSA2_OK; }\n')
+    for cc, args in (("gcc", ["-std=c11", "-x", "c"]), ("g++", ["-std=c++17", "-x", "c++"])):
+        if shutil.which(cc) is None:
+            pytest.skip(f"{cc} not available")
+        r = subprocess.run([cc, *args, "-Wall", "-Werror=implicit-function-declaration",
+                            "-fsyntax-only", "-D__HIP_PLATFORM_AMD__", "-I", _hip_include(),
+                            "-I", os.path.join(ROOT, "include"), str(src)],
+                           capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-2000:]
+
+
+def test_c_program_links_and_calls_host_functions(L, tmp_path):
+    """A C program links against libcsa2.so through the header alone and gets
+    the documented sizes, status strings and argument errors."""
+    import shutil
+    import subprocess
+    from fp4_kv_cache_decode_amd import csa2
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src, exe = tmp_path / "p.c", tmp_path / "p"
+    src.write_text(C_PROGRAM)
+    libdir = os.path.dirname(csa2.LIB_PATH)
+    rocm_lib = os.environ.get("ROCM_PATH", "/opt/rocm") + "/lib"
+    r = subprocess.run(["gcc", "-std=c11", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", _hip_include(),
+                        "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe),
+                        f"-L{libdir}", "-l:libcsa2.so", f"-Wl,-rpath,{libdir}",
+                        f"-L{rocm_lib}", f"-Wl,-rpath,{rocm_lib}", "-lamdhip64"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, (r.returncode, r.stdout, r.stderr[-1000:])
+    assert r.stdout.startswith("c-abi ok")
