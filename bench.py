@@ -77,6 +77,27 @@ def counter_traffic(workload: str):
     return fetch + write
 
 
+def row_counter_traffic(profile: str, workload: str):
+    """HBM bytes per launch of a row's timed kernel from the machine-readable
+    block of its committed profile (FETCH_SIZE and WRITE_SIZE in KiB per
+    dispatch, scaled by the copy-kernel calibration); None if the file is
+    absent, names another workload, or the kernel's source changed since."""
+    path = os.path.join(ROOT, "profiles", profile)
+    if not os.path.exists(path):
+        return None
+    kv = dict(re.findall(r"^(\w+)\s*=\s*(\S+)\s*$", open(path).read(), flags=re.M))
+    src = os.path.join(ROOT, kv.get("source", "-"))
+    if kv.get("workload") != workload or not os.path.exists(src):
+        return None
+    if kv.get("source_sha256") != source_hash(src):
+        return None
+    try:
+        return (float(kv["fetch_kib"]) * 1024 * float(kv["copy_fetch_factor"]) +
+                float(kv["write_kib"]) * 1024 * float(kv["copy_write_factor"]))
+    except (KeyError, ValueError):
+        return None
+
+
 class Setup:
     """Device caches (replicas), per-layer inputs and output buffers."""
 
@@ -320,8 +341,9 @@ def row_quantize(args):
     log(f"[bench] bulk quantize {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
     cfg = {"workload": "bulk quantize of decoder20_1m_b4 (4 x 1,048,576 rows)", "rows": n,
            "bytes_per_row": per_row, "dtype": "fp32"}
+    traffic = row_counter_traffic("quantize_bulk_decoder20_1m_b4.txt", "quantize_bulk_4x1m")
     roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+            "frac": gbs / PEAK_HBM_GBS, "traffic": traffic,
             "kernel": "quantize_kernel (csa2_quantize_kv)", "avg_us": ms * 1e3, "alg_bytes": alg}
     return _common(args, "CSA2 quantise-on-write rows/s", n / (ms * 1e-3), "rows/s", ms, cfg,
                    roof)
@@ -374,8 +396,9 @@ def row_gather(args):
     log(f"[bench] gather-attention {ms * 1e3:.1f} us, {gbs:.0f} GB/s")
     cfg = {"workload": "gather_attention_b1024_n64k", "batch": B, "ctx": N, "topk": G.TOPK,
            "window": G.WINDOW, "rotations": R, "dtype": "fp32"}
+    traffic = row_counter_traffic("attn_gather_b1024_n64k.txt", "gather_attention_b1024_n64k")
     roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-            "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+            "frac": gbs / PEAK_HBM_GBS, "traffic": traffic,
             "kernel": "attn_stream_kernel (csa2_decode_attn)", "avg_us": ms * 1e3,
             "alg_bytes": alg}
     return _common(args, "CSA2 gather/dequant/attention queries/s", B / (ms * 1e-3), "queries/s",
@@ -477,8 +500,10 @@ def row_prefill(args):
                          f"the fp64 C oracle's indexer and attention, {secs:.1f} s wall"}
     cfg = {"workload": wl.name, "queries": B, "prefix": N0, "topk": G.TOPK,
            "pool_blocks": G.N_BLOCKS, "window": G.WINDOW, "key_evals": key_evals, "dtype": "fp32"}
+    traffic = row_counter_traffic("prefill_8k_over_128k_kernel_stats.txt",
+                                  "prefill_8k_over_128k")
     roof = {"bound": "alu", "achieved": tfs, "peak": PEAK_FP32_TFS, "unit": "TFLOP/s",
-            "frac": tfs / PEAK_FP32_TFS, "traffic": None,
+            "frac": tfs / PEAK_FP32_TFS, "traffic": traffic,
             "kernel": "scan_kernel (csa2_index_block_scores)", "avg_us": scan_ms * 1e3,
             "flops": flops}
     return _common(args, "CSA2 chunked-prefill queries/s", B / (ms * 1e-3), "queries/s", ms, cfg,

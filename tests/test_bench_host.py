@@ -30,3 +30,15 @@ def test_code_hash_ignores_comments_and_blank_lines():
 def test_counter_traffic_needs_matching_workload():
     import bench
     assert bench.counter_traffic("no_such_workload") is None
+
+
+def test_row_counters_match_their_sources():
+    """Each committed row profile names its timed kernel's source and counters
+    taken on that source's current code (else the bench reports null traffic)."""
+    import bench
+    for prof, wl in (("quantize_bulk_decoder20_1m_b4.txt", "quantize_bulk_4x1m"),
+                     ("attn_gather_b1024_n64k.txt", "gather_attention_b1024_n64k"),
+                     ("prefill_8k_over_128k_kernel_stats.txt", "prefill_8k_over_128k")):
+        t = bench.row_counter_traffic(prof, wl)
+        assert t is None or t > 0
+        assert bench.row_counter_traffic(prof, "another_workload") is None
