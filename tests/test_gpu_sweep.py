@@ -83,3 +83,47 @@ def test_grouped_block_scores_random_sweep(K):
                                  dev(ctx[b0:b1]), N, Ms[b0:b1])
         torch.cuda.synchronize()
         assert np.array_equal(M.cpu().numpy(), Ms.cpu().numpy(), equal_nan=True), (it, B, mode)
+
+
+def test_attention_random_sweep(K):
+    """Random attention calls against the oracle: batch sizes on both kernels
+    (tile, split stream, unsplit stream), top-k lengths 1..2,048 with padding,
+    random contexts and window scales, contiguous and paged caches (shuffled
+    64- or 256-token pages)."""
+    import oracle as O
+    from parity import fill_both, shuffled_pages
+    rng = np.random.default_rng(21)
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    for it in range(8):
+        n_seq, L = 3, 2
+        N = int(rng.integers(200, 3000))
+        P = int(rng.choice([0, 64, 256]))
+        cap = -(-N // 256) * 256 + 256
+        wk_s, wv_s = float(rng.choice([1.0, 0.05])), float(rng.choice([1.0, 40.0, 200.0]))
+        oc = O.Cache(n_seq, cap, L, 4096, 1.0, wk_s, wv_s)
+        if P:
+            table, n_pages = shuffled_pages(it, n_seq, cap, P, [N] * n_seq)
+            gc = K.Cache(n_seq, cap, L, 4096, 1.0, wk_s, wv_s, page_tokens=P, n_pages=n_pages,
+                         page_table=torch.from_numpy(table))
+        else:
+            gc = K.Cache(n_seq, cap, L, 4096, 1.0, wk_s, wv_s)
+        fill_both(300 + it, n_seq, N, L, oc, gc, wlo=0)
+        B = int(rng.choice([1, 3, 40, 96, 300, 1100]))
+        topk = int(rng.choice([1, 37, 512, 700, 2048]))
+        seq = rng.integers(0, n_seq, B).astype(np.int32)
+        ctx = rng.integers(1, N + 1, B).astype(np.int64)
+        idx = np.full((B, topk), -1, np.int32)
+        for b in range(B):
+            m = int(rng.integers(0, min(topk, int(ctx[b])) + 1))
+            idx[b, :m] = np.sort(rng.choice(int(ctx[b]), m, replace=False))
+        layer = int(rng.integers(0, L))
+        q = G.attn_queries(400 + it, layer, B)
+        out = torch.empty((B, 16, 128), dtype=torch.float32, device="cuda")
+        K.decode_attn(gc, layer, dev(q), dev(idx), dev(seq), dev(ctx), out,
+                      K.alloc_workspace(K.OP_DECODE_ATTN, B, topk=topk))
+        torch.cuda.synchronize()
+        sample = np.unique(np.r_[0, B - 1, rng.integers(0, B, 12)])
+        want = oc.decode_attn(layer, q[sample], idx[sample], seq[sample], ctx[sample])
+        got = out.cpu().numpy()[sample]
+        err = float(np.max(np.abs(got - want)))
+        assert err <= 1e-4 * max(1.0, float(np.max(np.abs(want)))), (it, B, topk, P, err)
