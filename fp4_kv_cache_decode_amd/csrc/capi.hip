@@ -1,6 +1,7 @@
 // C ABI of libcsa2: argument validation, workspace layout, launch order.
 // The operations and their sources are documented in include/csa2.h.
 #include <math.h>
+#include <string.h>
 
 #include "csa2_device.h"
 #include "csa2_internal.h"
@@ -13,7 +14,8 @@ constexpr size_t ALIGN = 256;
 
 size_t align_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
-bool good_scale(float s) { return isfinite(s) && s > 0.0f; }
+// scales are positive normal floats (their reciprocals are finite too)
+bool good_scale(float s) { return isnormal(s) && s > 0.0f; }
 
 // Block-maxima row stride (floats) for contexts up to max_ctx.
 int64_t m_stride(int64_t max_ctx) {
@@ -89,7 +91,11 @@ csa2_status launched(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR
 extern "C" {
 
 const char* csa2_status_string(csa2_status s) {
-    switch (s) {
+    // A C caller may pass any int; reading it as the enum type would be
+    // undefined for values outside the enumerators' range, so read its bits.
+    int v;
+    memcpy(&v, &s, sizeof v);
+    switch (v) {
         case CSA2_OK: return "ok";
         case CSA2_ERR_INVALID_ARG: return "invalid argument";
         case CSA2_ERR_UNSUPPORTED: return "unsupported size";
