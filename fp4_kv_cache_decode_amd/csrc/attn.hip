@@ -137,10 +137,9 @@ __device__ __forceinline__ void fp4x8_scaled(uint32_t w, half2_t scale, uint32_t
 }
 
 constexpr float LOG2E = 1.4426950408889634f;
-// stream kernel softmax: weights up to 2^8 = 256, times a window V scale of at
-// most 128, stay below the f16 maximum 65504
+// stream kernel softmax: the running reference max lags the true max by at most
+// 2^8 in weight, so every weight stays far inside f16 for the hi/lo split
 constexpr float RESCALE_SLACK = 8.0f;
-constexpr float RESCALE_VSC_MAX = 128.0f;
 constexpr float LN2 = 0.6931471805599453f;
 
 
@@ -533,8 +532,20 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
         }
     }
     __syncthreads();
+    // The window's per-tensor V scale multiplies the PV products of window
+    // steps only.  A wave takes its main steps before its window steps, so O is
+    // divided by the scale before its first window step and multiplied back
+    // after the loop: the softmax weights enter the f16 split unscaled, which
+    // keeps them inside f16 whatever the scale.
+    bool in_window = false;
     for (; st < t_end; st += AT_WAVES) {
         const bool is_main = st < a.n_sub_main;
+        if (!is_main && !in_window) {
+            in_window = true;
+            const float inv = 1.0f / a.wv_scale;
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) o[mt] *= inv;
+        }
         // ---- dequantise this step: K into A-operand fragments, V into LDS (V^T)
         half4_t kf[8];
         uint32_t vv[16];                      // f16x2: channels 8g+32k+2i, +1 in vv[4k+i]
@@ -641,12 +652,9 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
         }
         tmax = max_xor32(max_xor16(tmax));
         // The reference max moves only when a logit exceeds it by more than
-        // `slack` (log2 units), so O is rescaled rarely.  Any reference gives
-        // the same softmax; weights stay below 2^slack, and p * vsc must stay
-        // inside f16 for the hi/lo split, hence no slack for a large window scale.
-        const float vsc = is_main ? 1.0f : a.wv_scale;
-        const float slack = vsc <= RESCALE_VSC_MAX ? RESCALE_SLACK : 0.0f;
-        const bool grew = tmax > m_run + slack;
+        // RESCALE_SLACK (log2 units), so O is rescaled rarely.  Any reference
+        // gives the same softmax; weights stay below 2^RESCALE_SLACK.
+        const bool grew = tmax > m_run + RESCALE_SLACK;
         const float m_new = grew ? tmax : m_run;
         const float alpha = m_run == NEG_INF ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
         half4_t phi, plo;
@@ -655,10 +663,9 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
         for (int r = 0; r < 4; ++r) {
             const float p = sv[r] == NEG_INF ? 0.0f : __builtin_amdgcn_exp2f(sv[r] - m_new);
             psum += p;
-            const float pv = p * vsc;
-            const _Float16 h = (_Float16)pv;
+            const _Float16 h = (_Float16)p;
             phi[r] = h;
-            plo[r] = (_Float16)(pv - (float)h);
+            plo[r] = (_Float16)(p - (float)h);
         }
         l_run = l_run * alpha + psum;
         m_run = m_new;
@@ -678,6 +685,11 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
         cur = nxt;
         ok_cur = ok_nxt;
         asm volatile("" ::: "memory");     // next step's tile writes after these reads
+    }
+
+    if (in_window) {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) o[mt] *= a.wv_scale;
     }
 
     // ---- combine the 4 waves: l over the 4 lanes of a head, then LDS

@@ -6,10 +6,12 @@
 // channels; the sliding-window K/V stay FP8 (E4M3); indexer keys are FP8 too
 // (this library's reading: one per-tensor fp32 scale for each FP8 store).
 //
-// One thread owns one 16-channel group: it reads 64 contiguous bytes of fp32,
-// so a wave streams 4 KB of input per instruction group.  Part 0 writes main-KV
-// records (16 groups per row: 8 of K, 8 of V), part 1 indexer keys (4 groups per
-// row), part 2+l the window rows of layer l (8 groups of K, 8 of V).
+// Every part of the grid covers the same 16 rows per block, 16 threads per row.
+// Part 0 writes main-KV records (one 16-channel group per thread: 8 of K, 8 of
+// V), part 1 indexer keys (4 channels per thread), part 2+l the window rows of
+// layer l (one 16-channel group per thread: 8 of K, 8 of V).  A group's thread
+// reads 64 contiguous bytes of fp32, so a wave streams 4 KB of input per
+// instruction group.
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
@@ -18,8 +20,7 @@ namespace csa2 {
 namespace {
 
 constexpr int QTHREADS = 256;
-constexpr int ROWS_MAIN = QTHREADS / 16;   // rows per block for 16-group parts
-constexpr int ROWS_IDX = QTHREADS / 4;     // rows per block for the indexer part
+constexpr int ROWS_MAIN = QTHREADS / 16;   // rows per block (16 threads per row)
 
 struct QuantArgs {
     uint8_t* kv;
@@ -79,14 +80,16 @@ __global__ void __launch_bounds__(QTHREADS) quantize_kernel(QuantArgs a) {
     const int part = blockIdx.y;
     const int t = threadIdx.x;
     if (part == 1) {
-        // indexer keys: 4 groups of 16 channels per row
-        int64_t row = (int64_t)blockIdx.x * ROWS_IDX + t / 4;
-        int u = t & 3;
+        // indexer keys: channels 4u .. 4u+3 of the row
+        const int64_t row = (int64_t)blockIdx.x * ROWS_MAIN + t / 16;
+        const int u = t & 15;
         int64_t dst;
         if (!a.idx_k || row >= a.n || !row_target(a, row, dst)) return;
-        float x[16];
-        load16(a.idx_k + row * IDX_DIM + 16 * u, x);
-        *reinterpret_cast<uint4*>(a.idxk + dst * IDX_DIM + 16 * u) = fp8_group(x, a.idxk_scale);
+        const float4 x = *reinterpret_cast<const float4*>(a.idx_k + row * IDX_DIM + 4 * u);
+        const float sc = a.idxk_scale;
+        const uint32_t w = e4m3_encode(x.x / sc) | (e4m3_encode(x.y / sc) << 8) |
+                           (e4m3_encode(x.z / sc) << 16) | (e4m3_encode(x.w / sc) << 24);
+        *reinterpret_cast<uint32_t*>(a.idxk + dst * IDX_DIM + 4 * u) = w;
         return;
     }
     int64_t row = (int64_t)blockIdx.x * ROWS_MAIN + t / 16;
@@ -166,7 +169,7 @@ hipError_t launch_quantize(const csa2_cache& c, const csa2_window* w, const floa
         parts = 2 + w->n_layers;
     }
     // with windows but no indexer input, part 1 blocks exit at once
-    dim3 grid((unsigned)((n + ROWS_MAIN - 1) / ROWS_MAIN), parts);
+    const dim3 grid((unsigned)((n + ROWS_MAIN - 1) / ROWS_MAIN), parts);
     hipLaunchKernelGGL(quantize_kernel, grid, dim3(QTHREADS), 0, stream, a);
     return hipGetLastError();
 }

@@ -101,7 +101,7 @@ typedef enum csa2_status {
 typedef struct csa2_cache {
     uint8_t* kv;        /* device [n_seq][cap][144], or [n_pages][page_tokens][144] */
     uint8_t* idxk;      /* device [n_seq][cap][64],  or [n_pages][page_tokens][64]  */
-    float idxk_scale;   /* per-tensor scale of the indexer keys (> 0) */
+    float idxk_scale;   /* per-tensor scale of the indexer keys (positive, normal) */
     int32_t n_seq;
     int64_t cap;        /* positions per sequence */
     const int32_t* page_table;  /* NULL, or device [n_seq][cap / page_tokens] page ids */
@@ -113,7 +113,7 @@ typedef struct csa2_cache {
 typedef struct csa2_window {
     uint8_t* k;         /* device [n_layers][n_seq][w_cap][128] */
     uint8_t* v;         /* device, same shape */
-    float k_scale;      /* per-tensor scales (> 0) */
+    float k_scale;      /* per-tensor scales (positive, normal floats) */
     float v_scale;
     int32_t n_layers;
     int32_t n_seq;      /* must equal the cache's n_seq */

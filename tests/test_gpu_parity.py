@@ -231,6 +231,51 @@ def test_index_reindex(K):
     assert np.array_equal(idx.cpu().numpy(), fidx)
 
 
+@pytest.mark.parametrize("scale,page_tokens", [(0.37, 0), (3.0, 0), (3.0, 256)])
+def test_index_nonunit_key_scale(K, scale, page_tokens):
+    """The indexer keys' per-tensor scale (reading: one fp32 scale per tensor,
+    applied to the E4M3 code value) through block scores, the pool, the Full
+    top-512 and a Reindex layer with its own query, on a contiguous and a paged
+    cache; block maxima within 2e-6 relative, index sets under the exemption."""
+    from parity import shuffled_pages
+    _say(f"index non-unit key scale {scale} page_tokens={page_tokens}")
+    N, B, seed = 30001, 3, 31
+    cap = N if not page_tokens else (-(-N // page_tokens) + 1) * page_tokens
+    oc = O.Cache(B, cap, 1, 128, scale)
+    if page_tokens:
+        table, n_pages = shuffled_pages(seed, B, cap, page_tokens, [N] * B)
+        gc = K.Cache(B, cap, 1, idxk_scale=scale, page_tokens=page_tokens, n_pages=n_pages,
+                     page_table=torch.from_numpy(table))
+    else:
+        gc = K.Cache(B, cap, 1, idxk_scale=scale)
+    fill_both(seed, B, N, 1, oc, gc)
+    torch.cuda.synchronize()
+    q0, w0 = G.index_queries(seed, 0, B)
+    q1, w1 = G.index_queries(seed, 1, B)
+    seq = np.array([1, 2, 0], np.int32)
+    ctx = np.array([N, N - 9, 12345], np.int64)
+    M = torch.empty((B, K.block_stride(N)), dtype=torch.float32, device="cuda")
+    K.index_block_scores(gc, dev(q0), dev(w0), dev(seq), dev(ctx), N, M)
+    gpool, gidx = _run_full(K, gc, q0, w0, seq, ctx, N)
+    gM = M.cpu().numpy()
+    for b in range(B):
+        sc = oc.scores(int(seq[b]), q0[b], w0[b], int(ctx[b]))
+        Mb = block_scores(sc, int(ctx[b]))
+        np.testing.assert_allclose(gM[b, :Mb.size], Mb, rtol=2e-6, atol=1e-6)
+    nd = _check_full(oc, q0, w0, seq, ctx, gpool, gidx, 2048, 512)
+    opool, _, _, _ = oc.index_full(q0, w0, seq, ctx)
+    oidx, kp = oc.index_reindex(q1, w1, seq, ctx, opool)
+    idx = torch.empty((B, 512), dtype=torch.int32, device="cuda")
+    K.index_reindex(gc, dev(q1), dev(w1), dev(seq), dev(ctx), dev(opool), idx,
+                    K.alloc_workspace(K.OP_INDEX_REINDEX, B))
+    torch.cuda.synchronize()
+    ridx = idx.cpu().numpy()
+    for b in range(B):
+        sc = oc.scores(int(seq[b]), q1[b], w1[b], int(ctx[b]))
+        nd += check_index_set(ridx[b], oidx[b], lambda t: sc[t], kp[b])
+    _say(f"  exempt differences: {nd}")
+
+
 # ----------------------------------------------------------------- attention
 
 def _attn_case(K, N, B, n_layers, layer, seed, topk=512, w_cap=128, idx=None):
@@ -465,13 +510,13 @@ def test_reuse_gathered_records_bit_exact(K, B):
     assert not gh[~valid].any()             # invalid entries left untouched
 
 
-@pytest.mark.parametrize("wv_scale", [50.0, 300.0])
+@pytest.mark.parametrize("wv_scale", [0.01, 50.0, 300.0])
 @pytest.mark.parametrize("B", [3, 96])
 def test_decode_attn_window_scales(K, B, wv_scale):
-    """Per-tensor window scales away from 1 on both kernels.  The stream kernel
-    (B = 96) lets its softmax reference lag by up to 2^8 only while weight times
-    window V scale stays inside f16 (scale <= 128): 50 takes that path, 300 the
-    exact-max path."""
+    """Per-tensor window scales away from 1 on both kernels.  Both apply the
+    window's V scale to the PV products, never to the softmax weights before
+    their f16 hi/lo split: a small scale (0.01) would otherwise push weights into
+    f16 subnormals and a large one past the f16 maximum."""
     _say(f"decode_attn window scales B={B} wv_scale={wv_scale}")
     N, L = 2000, 2
     oc = O.Cache(3, N, L, wk_scale=0.02, wv_scale=wv_scale)
