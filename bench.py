@@ -13,9 +13,12 @@ data.  Inputs are resident in HBM before the timed region; steps rotate over
 cache replicas so the 268 MB indexer-key set is re-read from HBM every step
 rather than from the 256 MB Infinity Cache.
 
-Prints one JSON line (rank 0) with queries/s, the roofline of the dominant
-kernel (the Full layer's indexer scan) measured with HIP events on the launch
-stream, and the CPU oracle timed on a bounded sample on the host.
+Prints one JSON line (rank 0) with queries/s and the HBM roofline of the whole
+decode step (the step's algorithmic bytes over its measured time), with the
+Full layer's indexer scan, the step's largest single kernel by bytes, timed on
+its own with HIP events on the launch stream and reported beside it; and the
+CPU oracle timed on a bounded sample on the host, at one thread and at the
+host's thread count.
 """
 from __future__ import annotations
 
@@ -37,6 +40,8 @@ PEAK_FP32_TFS = 157.3      # MI355X published fp32 vector peak (packed FMA)
 METRIC = "CSA2 decode queries/s at 1M ctx + achieved HBM GB/s as % of MI355X peak"
 SCORE_SRC = os.path.join(ROOT, "fp4_kv_cache_decode_amd", "csrc", "index_score.hip")
 COUNTER_FILE = os.path.join(ROOT, "profiles", "scan_decoder20_1m_b4_counters.txt")
+STEP_COUNTER_FILE = os.path.join(ROOT, "profiles", "decoder20_1m_b4_step_counters.txt")
+CSRC = os.path.join(ROOT, "fp4_kv_cache_decode_amd", "csrc")
 
 
 def log(*a):
@@ -75,6 +80,75 @@ def counter_traffic(workload: str):
     except (KeyError, ValueError):
         return None
     return fetch + write
+
+
+def step_alg_bytes(wl) -> int:
+    """Algorithmic HBM bytes of one decode step: what the method itself must
+    read or write once per step, whatever the kernels' intermediates.  Per
+    query: the Full layer's scan over N indexer keys (64 B each), each Reindex
+    layer's 2,048 pool blocks of 8 keys, one gather of topk 144-byte records per
+    Full or Reindex layer (its Reuse layers take the same rows), every layer's
+    128 window rows (K and V, 128 B each) and its query and output (16 x 128
+    fp32 each)."""
+    from fp4_kv_cache_decode_amd import datagen as G
+    n_full = sum(m == "F" for m in wl.layers)
+    n_reindex = sum(m == "I" for m in wl.layers)
+    per_q = (n_full * wl.N * G.DI +
+             n_reindex * G.N_BLOCKS * G.BLOCK * G.DI +
+             (n_full + n_reindex) * G.TOPK * 144 +
+             len(wl.layers) * (G.WINDOW * 2 * G.D + 2 * G.H * G.D * 4))
+    return wl.B * per_q
+
+
+def csrc_hash() -> str:
+    """Code hash over every kernel source of the library (sorted by name)."""
+    parts = []
+    for name in sorted(os.listdir(CSRC)):
+        if name.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+                parts.append(name + "\n" + f.read())
+    return code_hash("\n".join(parts))
+
+
+def step_counter_traffic(workload: str):
+    """HBM bytes of one whole decode step from committed per-kernel counters:
+    the sum over the step's kernels of calls x (FETCH_SIZE x fetch factor +
+    WRITE_SIZE x write factor), in KiB per dispatch; None if the file is
+    absent, names another workload, or any kernel source changed since."""
+    if not os.path.exists(STEP_COUNTER_FILE):
+        return None
+    txt = open(STEP_COUNTER_FILE).read()
+    kv = dict(re.findall(r"^(\w+)\s*=\s*(\S+)\s*$", txt, flags=re.M))
+    if kv.get("workload") != workload or kv.get("csrc_sha256") != csrc_hash():
+        return None
+    try:
+        ff, wf = float(kv["copy_fetch_factor"]), float(kv["copy_write_factor"])
+    except (KeyError, ValueError):
+        return None
+    rows = re.findall(r"^kernel\s+(\S+)\s+calls_per_step=(\d+)\s+fetch_kib=(\S+)\s+"
+                      r"write_kib=(\S+)\s*$", txt, flags=re.M)
+    if not rows:
+        return None
+    return sum(int(c) * (float(f) * 1024 * ff + float(w) * 1024 * wf) for _, c, f, w in rows)
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def set_oracle_threads(n: int) -> None:
+    """Thread count of the oracle's OpenMP regions (calling thread's setting)."""
+    import ctypes
+    import ctypes.util
+    name = ctypes.util.find_library("gomp") or "libgomp.so.1"
+    ctypes.CDLL(name).omp_set_num_threads(int(n))
 
 
 def row_counter_traffic(profile: str, workload: str):
@@ -186,8 +260,8 @@ class Setup:
         self.kvg = torch.empty((B, G.TOPK, K.RECORD), dtype=torch.uint8, device="cuda")
 
     # A step is three parts: the quantise-on-write of the new token, the Full
-    # layer's scan over the whole context (the dominant kernel, timed with HIP
-    # events), and everything after it (pool, top-k, Reindex layers, attention).
+    # layer's scan over the whole context (the step's largest kernel by bytes,
+    # timed with HIP events), and everything after it (pool, top-k, Reindex layers, attention).
     def part_quant(self, c):
         n = self.new
         self.K.quantize_kv(c, n["k"], n["v"], n["seq"], n["pos"], idx_k=n["ik"],
@@ -583,29 +657,41 @@ def main():
     score_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
     log(f"[bench] {ms:.3f} ms/step, Full-layer scan {score_ms * 1e3:.1f} us")
 
-    # roofline of the dominant kernel: the Full layer's indexer scan
+    # the Full layer's indexer scan, timed on its own with events
     n_keys = B * N
-    alg_bytes = n_keys * 64 + B * (-(-N // 8)) * 4 + B * (4 * 64 + 4) * 4
+    scan_bytes = n_keys * 64 + B * (-(-N // 8)) * 4 + B * (4 * 64 + 4) * 4
     if args.page_tokens:
-        alg_bytes += B * (-(-N // args.page_tokens)) * 4      # page-table entries
-    achieved = alg_bytes / (score_ms * 1e-3) / 1e9
+        scan_bytes += B * (-(-N // args.page_tokens)) * 4      # page-table entries
+    scan_gbs = scan_bytes / (score_ms * 1e-3) / 1e9
     # the committed counters were taken on the contiguous cache
-    traffic = None if args.page_tokens else counter_traffic(wl.name)
+    scan_traffic = None if args.page_tokens else counter_traffic(wl.name)
+    # the whole step: its algorithmic bytes over the measured step time
+    alg_bytes = step_alg_bytes(wl)
+    achieved = alg_bytes / (ms * 1e-3) / 1e9
+    step_traffic = None if args.page_tokens else step_counter_traffic(wl.name)
 
     cpu = None
     if want_cpu:
         threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-        # whole decode steps through the oracle until about 10 s of wall time
+        # whole decode steps through the oracle: at one thread (one step, the
+        # bounded sample), then at the host's thread count until ~10 s
+        set_oracle_threads(1)
+        secs1 = oracle_step(S)
+        set_oracle_threads(threads)
         reps, secs = 0, 0.0
         while reps < 2 or (secs < 10.0 and reps < 50):
             secs += oracle_step(S)
             reps += 1
         cpu = {"value": B * reps / secs, "unit": "queries/s", "cores": threads,
-               "kind": "oracle",
+               "kind": "oracle", "cpu_model": cpu_model(),
+               "value_1_thread": B / secs1,
                "sample": f"{reps} full decode steps of {wl.name} ({B} queries x "
                          f"{len(wl.layers)} layers at {N} tokens each) through the fp64 C "
-                         f"oracle, OpenMP over positions/queries, {secs:.1f} s wall"}
-        log(f"[bench] oracle {reps} steps in {secs:.2f} s")
+                         f"oracle, OpenMP over positions/queries on {threads} threads, "
+                         f"{secs:.1f} s wall; value_1_thread: one such step on one thread, "
+                         f"{secs1:.1f} s wall"}
+        log(f"[bench] oracle {reps} steps in {secs:.2f} s on {threads} threads; "
+            f"1 step in {secs1:.2f} s on 1 thread")
 
     res = {
         "metric": METRIC,
@@ -628,9 +714,14 @@ def main():
                              if args.page_tokens else "contiguous")},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": achieved / PEAK_HBM_GBS,
-                     "traffic": traffic,
-                     "kernel": "scan_kernel (csa2_index_block_scores)",
-                     "avg_us": score_ms * 1e3, "alg_bytes": alg_bytes},
+                     "traffic": step_traffic,
+                     "scope": "whole decode step (every kernel of the step, graph replay)",
+                     "alg_bytes": alg_bytes, "avg_us": ms * 1e3,
+                     "kernels": {"scan_kernel": {
+                         "entry": "csa2_index_block_scores", "bound": "hbm",
+                         "achieved": scan_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                         "frac": scan_gbs / PEAK_HBM_GBS, "traffic": scan_traffic,
+                         "avg_us": score_ms * 1e3, "alg_bytes": scan_bytes}}},
         "cpu_baseline": cpu,
         "hbm_copy_gbs": copy_gbs,
     }
