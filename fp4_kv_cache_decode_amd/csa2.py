@@ -66,6 +66,9 @@ def lib():
         L.csa2_decode_attn_ex.argtypes = [C.POINTER(csa2_cache), C.POINTER(csa2_window),
                                           C.c_int32, _P, _P, _P, _P, C.c_int32, C.c_int32,
                                           C.c_float, _P, _P, _P, _P, C.c_size_t, _P]
+        L.csa2_decode_attn_noalloc.argtypes = [C.POINTER(csa2_cache), C.POINTER(csa2_window),
+                                               C.c_int32, _P, _P, _P, _P, C.c_int32, C.c_int32,
+                                               C.c_float, _P, _P, _P, _P]
         L.csa2_workspace_bytes.argtypes = [C.c_int32, C.c_int32, C.c_int64, C.c_int32, C.c_int32,
                                            C.c_int32]
         L.csa2_workspace_bytes.restype = C.c_size_t
@@ -73,7 +76,7 @@ def lib():
         L.csa2_status_string.restype = C.c_char_p
         for f in ("csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex",
                   "csa2_decode_attn", "csa2_decode_attn_ex", "csa2_index_block_scores",
-                  "csa2_index_select_pool"):
+                  "csa2_index_select_pool", "csa2_decode_attn_noalloc"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -274,6 +277,27 @@ def decode_attn(cache: Cache, layer: int, q, idx, seq, ctx, out, ws, sm_scale=No
                                _ptr(kvg_in), _ptr(kvg_out), _ptr(out),
                                _ptr(ws), ws.numel(), _stream(stream))
     _check(st, "csa2_decode_attn_ex")
+
+
+def decode_attn_noalloc(cache: Cache, layer: int, q, idx, seq, ctx, out, sm_scale=None,
+                        stream=None, kvg_in=None, kvg_out=None) -> None:
+    """csa2_decode_attn_noalloc: decode_attn with no workspace (the library's
+    fixed per-GPU scratch holds the partial records)."""
+    B, topk = idx.shape
+    _need(q, torch.float32, (B, HEADS, D), "q")
+    _need(idx, torch.int32, (B, topk), "idx")
+    _need(seq, torch.int32, (B,), "seq")
+    _need(ctx, torch.int64, (B,), "ctx")
+    _need(out, torch.float32, (B, HEADS, D), "out")
+    for name, g in (("kvg_in", kvg_in), ("kvg_out", kvg_out)):
+        if g is not None:
+            _need(g, torch.uint8, (B, topk, RECORD), name)
+    if sm_scale is None:
+        sm_scale = float(torch.tensor(D ** -0.5, dtype=torch.float32))
+    st = lib().csa2_decode_attn_noalloc(C.byref(cache.c), C.byref(cache.w), layer, _ptr(q),
+                                        _ptr(idx), _ptr(seq), _ptr(ctx), B, topk, sm_scale,
+                                        _ptr(kvg_in), _ptr(kvg_out), _ptr(out), _stream(stream))
+    _check(st, "csa2_decode_attn_noalloc")
 
 
 def alloc_workspace(op: int, B: int, max_ctx: int = 0, n_blocks: int = 2048, topk: int = 512,

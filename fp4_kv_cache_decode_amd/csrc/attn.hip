@@ -794,19 +794,28 @@ struct AttnPlan {
     int32_t n_split;         // workgroups (partial records) per query
 };
 
-AttnPlan attn_plan(int32_t B, int32_t topk) {
+// max_parts caps the partial records (a fixed scratch): the stream kernel's
+// split is lowered until B x split fits, down to one workgroup per query,
+// which writes no partials.  The tile kernel's B x tiles <= 768 records must
+// fit the cap (callers pass at least that many).
+AttnPlan attn_plan(int32_t B, int32_t topk, int64_t max_parts) {
     const int32_t n_tiles = (topk + TILE - 1) / TILE + WINDOW / TILE;
     if ((int64_t)B * n_tiles <= TILE_KERNEL_MAX_WG) return {true, n_tiles};
     const int32_t n_sub = (topk + SUB - 1) / SUB + WINDOW / SUB;
     const int32_t max_split = (n_sub + AT_WAVES - 1) / AT_WAVES;
-    const int32_t split = (STREAM_WG_TARGET + B - 1) / B;
-    return {false, split < 1 ? 1 : (split > max_split ? max_split : split)};
+    int32_t split = (STREAM_WG_TARGET + B - 1) / B;
+    split = split < 1 ? 1 : (split > max_split ? max_split : split);
+    if (split > 1 && (int64_t)B * split > max_parts) {
+        const int64_t fit = max_parts / B;
+        split = fit < 2 ? 1 : (int32_t)fit;
+    }
+    return {false, split};
 }
 
 }  // namespace
 
-int64_t attn_partials(int32_t B, int32_t topk) {
-    const AttnPlan p = attn_plan(B, topk);
+int64_t attn_partials(int32_t B, int32_t topk, int64_t max_parts) {
+    const AttnPlan p = attn_plan(B, topk, max_parts);
     return p.n_split > 1 ? (int64_t)B * p.n_split : 0;
 }
 
@@ -814,8 +823,8 @@ hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
                        const float* q, const int32_t* idx, const int32_t* seq,
                        const int64_t* ctx, int32_t B, int32_t topk, float sm_scale,
                        const uint8_t* kvg_in, uint8_t* kvg_out, float* out, float* partials,
-                       hipStream_t stream) {
-    const AttnPlan p = attn_plan(B, topk);
+                       int64_t max_parts, hipStream_t stream) {
+    const AttnPlan p = attn_plan(B, topk, max_parts);
     if (p.tile) {
         // few queries: one workgroup per 64-entry tile, the shortest dependency chain
         TileArgs a{};

@@ -3,6 +3,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
@@ -50,7 +52,8 @@ size_t reindex_bytes(int32_t B, int32_t n_blocks) {
 }
 
 size_t attn_bytes(int32_t B, int32_t topk) {
-    return align_up((size_t)csa2::attn_partials(B, topk) * csa2::ATTN_PART_FLOATS * sizeof(float));
+    return align_up((size_t)csa2::attn_partials(B, topk, csa2::ATTN_NO_CAP) *
+                    csa2::ATTN_PART_FLOATS * sizeof(float));
 }
 
 csa2_status check_cache(const csa2_cache* c, bool need_kv, bool need_idxk) {
@@ -85,6 +88,41 @@ csa2_status check_select(int32_t B, int32_t n_blocks, int32_t block, int32_t top
 }
 
 csa2_status launched(hipError_t e) { return e == hipSuccess ? CSA2_OK : CSA2_ERR_LAUNCH; }
+
+// ---------------------------------------------------------------------------
+// Fixed scratch of csa2_decode_attn_noalloc: the split queries' partial records
+// live in a file-scope device array instead of a caller workspace.  Every GPU
+// the library runs on holds its own copy until the process ends.  In host code
+// the array's name is only a host-side stand-in, so its device address is
+// looked up once per device (hipGetSymbolAddress, with that device current)
+// and only that address is handed to kernels.
+constexpr size_t NOALLOC_SCRATCH_BYTES = CSA2_NOALLOC_SCRATCH_BYTES;
+constexpr int64_t NOALLOC_MAX_PARTS =
+    (int64_t)(NOALLOC_SCRATCH_BYTES / (csa2::ATTN_PART_FLOATS * sizeof(float)));
+static_assert(NOALLOC_MAX_PARTS >= csa2::ATTN_MIN_CAP, "the tile kernel's partials must fit");
+constexpr int MAX_DEVICES = 64;
+
+std::mutex scratch_mu;
+float* scratch_ptr[MAX_DEVICES];   // device address of `scratch` per device id, once looked up
+
+}  // namespace
+
+static __device__ __align__(256) float scratch[NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+// Device address of this device's scratch array (null on failure).
+float* device_scratch() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= MAX_DEVICES) return nullptr;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        scratch_ptr[dev] = static_cast<float*>(p);
+    }
+    return scratch_ptr[dev];
+}
 
 }  // namespace
 
@@ -249,7 +287,35 @@ csa2_status csa2_decode_attn_ex(const csa2_cache* cache, const csa2_window* win,
     const size_t need = attn_bytes(B, topk);
     if (need > 0 && (!ws || ws_bytes < need)) return CSA2_ERR_WORKSPACE;
     return launched(csa2::launch_attn(*cache, *win, layer, q, idx, seq, ctx, B, topk, sm_scale,
-                                      kvg_in, kvg_out, out, static_cast<float*>(ws), stream));
+                                      kvg_in, kvg_out, out, static_cast<float*>(ws),
+                                      csa2::ATTN_NO_CAP, stream));
+}
+
+csa2_status csa2_decode_attn_noalloc(const csa2_cache* cache, const csa2_window* win,
+                                     int32_t layer, const float* q, const int32_t* idx,
+                                     const int32_t* seq, const int64_t* ctx, int32_t B,
+                                     int32_t topk, float sm_scale, const uint8_t* kvg_in,
+                                     uint8_t* kvg_out, float* out, hipStream_t stream) {
+    csa2_status st = check_cache(cache, true, false);
+    if (st != CSA2_OK) return st;
+    st = check_window(win, cache);
+    if (st != CSA2_OK) return st;
+    if (!q || !idx || !seq || !ctx || !out) return CSA2_ERR_INVALID_ARG;
+    if (kvg_in && kvg_out) return CSA2_ERR_INVALID_ARG;
+    if (layer < 0 || layer >= win->n_layers || B < 0 || !isfinite(sm_scale))
+        return CSA2_ERR_INVALID_ARG;
+    if (topk < 1 || topk > CSA2_MAX_TOPK || B > 65535) return CSA2_ERR_UNSUPPORTED;
+    if (B == 0) return CSA2_OK;
+    // the launch plan is capped to the scratch; a plan past it is refused
+    const int64_t parts = csa2::attn_partials(B, topk, NOALLOC_MAX_PARTS);
+    if (parts > NOALLOC_MAX_PARTS) return CSA2_ERR_WORKSPACE;
+    float* part = nullptr;
+    if (parts > 0) {
+        part = device_scratch();
+        if (!part) return CSA2_ERR_LAUNCH;
+    }
+    return launched(csa2::launch_attn(*cache, *win, layer, q, idx, seq, ctx, B, topk, sm_scale,
+                                      kvg_in, kvg_out, out, part, NOALLOC_MAX_PARTS, stream));
 }
 
 csa2_status csa2_decode_attn(const csa2_cache* cache, const csa2_window* win, int32_t layer,

@@ -57,14 +57,18 @@ size_t topk_workspace_bytes(int32_t B, int64_t max_n);
 // Split-K gather/dequant attention for one layer plus the cross-split merge.
 // kvg_in (optional): main records read from [B][topk][RECORD] instead of the
 // cache; kvg_out (optional): the main records read are also stored there.
+// The launch plan writes at most max_parts partial records (ATTN_NO_CAP: the
+// plan's own choice; a cap must be at least ATTN_MIN_CAP).
 hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
                        const float* q, const int32_t* idx, const int32_t* seq,
                        const int64_t* ctx, int32_t B, int32_t topk, float sm_scale,
                        const uint8_t* kvg_in, uint8_t* kvg_out, float* out, float* partials,
-                       hipStream_t stream);
+                       int64_t max_parts, hipStream_t stream);
 
 // Partial records an attention call writes (0 when no query is split).
-int64_t attn_partials(int32_t B, int32_t topk);
+int64_t attn_partials(int32_t B, int32_t topk, int64_t max_parts);
 constexpr size_t ATTN_PART_FLOATS = 16 + 16 + 16 * 128;
+constexpr int64_t ATTN_NO_CAP = INT64_MAX;
+constexpr int64_t ATTN_MIN_CAP = 768;   // the tile kernel's largest grid
 
 }  // namespace csa2

@@ -267,6 +267,33 @@ csa2_status csa2_decode_attn_ex(const csa2_cache* cache, const csa2_window* win,
                                 const uint8_t* kvg_in, uint8_t* kvg_out, float* out, void* ws,
                                 size_t ws_bytes, hipStream_t stream);
 
+/*
+ * csa2_decode_attn_noalloc - csa2_decode_attn_ex for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  It takes no workspace and allocates
+ * nothing: the split queries' partial records go to a fixed scratch array of
+ * CSA2_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, held from
+ * the first call on that GPU until the process ends (its device address is
+ * looked up on that first call).  The launch plan is that of
+ * csa2_decode_attn_ex, except that a large batch on the split streaming path
+ * uses fewer splits when its partial records would not fit the scratch (down
+ * to one workgroup per query, which writes none), so results agree with
+ * csa2_decode_attn_ex within the attention tolerance and are bit-identical
+ * whenever the plans agree.  Arguments, results and status codes are those of
+ * csa2_decode_attn_ex without ws / ws_bytes; CSA2_ERR_WORKSPACE if a plan ever
+ * needed more than the scratch, CSA2_ERR_LAUNCH if the scratch's address
+ * cannot be obtained.  Every call on one GPU shares that GPU's scratch: calls
+ * that overlap on one GPU (other streams, other host threads) race and must be
+ * serialised by the caller.  Nothing in the scratch needs clearing between
+ * calls (each call writes every partial record it reads).
+ */
+#define CSA2_NOALLOC_SCRATCH_BYTES (8u << 20)
+csa2_status csa2_decode_attn_noalloc(const csa2_cache* cache, const csa2_window* win,
+                                     int32_t layer, const float* q, const int32_t* idx,
+                                     const int32_t* seq, const int64_t* ctx, int32_t B,
+                                     int32_t topk, float sm_scale, const uint8_t* kvg_in,
+                                     uint8_t* kvg_out, float* out, hipStream_t stream);
+
 /* Workspace bytes an operation needs (0 for unknown op or invalid sizes). */
 size_t csa2_workspace_bytes(int32_t op, int32_t B, int64_t max_ctx, int32_t n_blocks,
                             int32_t block, int32_t topk);

@@ -92,6 +92,14 @@ int main(void) {
         EXPECT(csa2_decode_attn(&c, &bw, 0, ff, fi, fi, fl, 4, 512, 0.088f, ff, ws, 1u << 30, NULL), CSA2_ERR_INVALID_ARG);
     }
 
+    /* the no-allocation attention call: argument errors and an empty batch
+       (none of them touches the library's scratch) */
+    EXPECT(csa2_decode_attn_noalloc(&c, &w, 0, ff, fi, fi, fl, 0, 512, 0.088f, NULL, NULL, ff, NULL), CSA2_OK);
+    EXPECT(csa2_decode_attn_noalloc(&c, &w, 0, ff, fi, fi, fl, 4, 512, 0.088f, fake, fake, ff, NULL), CSA2_ERR_INVALID_ARG);
+    EXPECT(csa2_decode_attn_noalloc(&c, &w, 0, ff, fi, fi, fl, 4, 4096, 0.088f, NULL, NULL, ff, NULL), CSA2_ERR_UNSUPPORTED);
+    EXPECT(csa2_decode_attn_noalloc(&c, &w, 20, ff, fi, fi, fl, 4, 512, 0.088f, NULL, NULL, ff, NULL), CSA2_ERR_INVALID_ARG);
+    EXPECT(csa2_decode_attn_noalloc(&c, NULL, 0, ff, fi, fi, fl, 4, 512, 0.088f, NULL, NULL, ff, NULL), CSA2_ERR_INVALID_ARG);
+
     /* sizes and strings over a range of shapes */
     size_t total = 0;
     for (int32_t op = 0; op <= 5; ++op)
