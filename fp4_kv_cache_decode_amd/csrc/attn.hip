@@ -65,12 +65,13 @@ constexpr int32_t STREAM_WG_TARGET = 1024;  // stream workgroups to aim for per 
 constexpr int VT_STRIDE = 24;             // f16 per transposed V row (16 entries + 8 pad):
                                           // conflict-free packed writes and operand reads
 constexpr float NEG_INF = -__builtin_huge_valf();
+// floats per head row of the waves' O in LDS when they are combined: the 16
+// lanes that write one 16-byte piece of 16 heads' rows at once land on 16
+// distinct bank groups (a 128-float row would put all 16 on the same one)
+constexpr int OROW = D + 4;
 // tile kernel (small batches): used while B x tiles fits one wave of workgroups
 constexpr int64_t TILE_KERNEL_MAX_WG = 768;
 constexpr int TILE = 64;
-constexpr int KROW = 136;    // f16 per K row in LDS (128 + 8 pad)
-constexpr int VROW = 72;     // f16 per transposed V row (64 + 8 pad)
-constexpr int PROW = 72;     // f16 per P row
 
 struct StreamArgs {
     const uint8_t* kv;
@@ -105,7 +106,7 @@ struct StreamShared {
             half4_t q[2][8][64];                   // query fragments (hi, lo) per ks, per lane
         } st;
         struct {
-            float o[AT_WAVES][HEADS * D];
+            float o[AT_WAVES][HEADS * OROW];
             float m[AT_WAVES][HEADS];
             float l[AT_WAVES][HEADS];
         } mg;                                      // the waves' softmax states
@@ -145,9 +146,16 @@ constexpr float LN2 = 0.6931471805599453f;
 
 // ---------------------------------------------------------------------------
 // Tile kernel (small batches, latency): one workgroup per (query, 64-entry
-// tile).  Four threads gather an entry, the dequantised K and V^T of the tile
-// are staged in LDS, the 4 waves each take 16 entries of S = Q K^T and 32
-// output dims of P V, and the tile writes its (m, l, O) partial.
+// tile), each of its 4 waves owning 16 entries.  The work of a wave is one
+// step of the stream kernel's loop (below): lane (c, g) gathers its entry's K
+// channels 32g..32g+31 and V channels {8g + 32k + i}, S^T = K Q^T comes out of
+// MFMA with K straight from the gathering lane's registers (here as
+// v_mfma_f32_16x16x32_f16, four K = 32 slices of the contraction), the
+// softmax weights stay where S^T left them as the B operand of O^T = V^T P^T,
+// and only V is transposed, through the wave's own LDS tile.  The 4 waves'
+// (m, l, O) are combined in LDS and the tile writes one partial record.
+// The index load is issued first and the query's loads right after it, so
+// the query's conversion overlaps the record loads.
 
 struct TileArgs {
     const uint8_t* kv;
@@ -173,14 +181,20 @@ struct TileArgs {
     float sm_scale;
 };
 
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
 struct TileShared {
-    _Float16 K[TILE * KROW];
-    _Float16 Vt[D * VROW];
-    _Float16 Phi[HEADS * PROW];
-    _Float16 Plo[HEADS * PROW];
-    float red[4][HEADS];
-    float lsum[4][HEADS];
-    int valid[TILE];
+    union {
+        struct {
+            _Float16 vt[AT_WAVES][D * VT_STRIDE];  // per-wave V^T of its 16 entries
+            half8_t q[2][4][64];                   // query slices (hi, lo) per lane
+        } st;
+        struct {
+            float o[AT_WAVES][HEADS * OROW];
+            float m[AT_WAVES][HEADS];
+            float l[AT_WAVES][HEADS];
+        } mg;                                      // the waves' softmax states
+    };
 };
 
 template <bool PAGED>
@@ -189,220 +203,259 @@ __global__ void __launch_bounds__(AT_THREADS) attn_tile_kernel(TileArgs a) {
     const int tile = blockIdx.x;
     const int b = blockIdx.y;
     const int t = threadIdx.x;
-    const int lane = t & 63, wave = t >> 6;
+    const int lane = t & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+    const int c = lane & 15, g = lane >> 4;
+    const bool is_main = tile < a.n_main;
+    // this lane's entry: index j of the list (main) or offset `off` in the window
+    const int j = tile * TILE + 16 * wave + c;
+    const int off = (tile - a.n_main) * TILE + 16 * wave + c;   // window tiles: < 128 <= w_cap
+
+    // ---- loads in order of need: the index (and the query's sequence and
+    // length), the query, then the records
+    int32_t pos = -1;
+    if (is_main && j < a.topk) pos = a.idx[(int64_t)b * a.topk + j];
     const int32_t s = a.seq[b];
     const int64_t N = clamp64(a.ctx[b], 0, a.cap);
     const bool seq_ok = s >= 0 && s < a.n_seq;
-    const bool is_main = tile < a.n_main;
-    float* part = a.part + ((int64_t)b * a.n_tiles + tile) * ATTN_PART_FLOATS;
-
-    // ---- query fragments first, independent of the gather chain (A operand,
-    // hi/lo f16): Q[h = lane%16][16ks + 4(lane/16) + 0..3]
-    half4_t qhi[8], qlo[8];
-    {
-        const int h = lane & 15, g = lane >> 4;
-        const float* qrow = a.q + ((int64_t)b * HEADS + h) * D + 4 * g;
+    // the query, once per workgroup and coalesced: two float4 per thread
+    float4 qv[2];
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const float4 v = *reinterpret_cast<const float4*>(qrow + 16 * ks);
-            const float x[4] = {v.x, v.y, v.z, v.w};
+    for (int k = 0; k < 2; ++k)
+        qv[k] = *reinterpret_cast<const float4*>(a.q + (int64_t)b * HEADS * D +
+                                                  4 * (t + AT_THREADS * k));
+
+    // ---- per kind of tile: the record (or window row) loads, the query's
+    // conversion while they are in flight, then the dequantisation.  Each
+    // branch consumes everything it loads, so no load is pending where the
+    // branches join (a pending load there would make the compiler wait for all
+    // of them before the first record load).
+    half8_t kf[4];                        // K: A-operand slices of S^T = K Q^T
+    uint32_t vv[16];                      // V f16x2: channels 8g+32k+2i, +1 in vv[4k+i]
+    // q as f16 hi + lo in the B-operand slices of S^T = K Q^T: slice sl of
+    // lane (c, g) takes channels 32g + 8 sl .. +7 of head c; each float4 goes
+    // to the lane, slice and half that take it (read back after a barrier)
+    auto convert_q = [&]() {
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int e = 4 * (t + AT_THREADS * k);          // h * 128 + d, d % 4 == 0
+            const int h = e >> 7, d = e & (D - 1);
+            const float x[4] = {qv[k].x, qv[k].y, qv[k].z, qv[k].w};
+            half4_t hi4, lo4;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                _Float16 hi = (_Float16)x[i];
-                qhi[ks][i] = hi;
-                qlo[ks][i] = (_Float16)(x[i] - (float)hi);
+                const _Float16 hi = (_Float16)x[i];
+                hi4[i] = hi;
+                lo4[i] = (_Float16)(x[i] - (float)hi);
             }
+            const int fl = 16 * (d >> 5) + h, sl = (d >> 3) & 3;
+            _Float16* qh = reinterpret_cast<_Float16*>(&sh.st.q[0][sl][fl]) + (d & 4);
+            _Float16* ql = reinterpret_cast<_Float16*>(&sh.st.q[1][sl][fl]) + (d & 4);
+            *reinterpret_cast<half4_t*>(qh) = hi4;
+            *reinterpret_cast<half4_t*>(ql) = lo4;
+        }
+    };
+    bool ok;
+    if (is_main) {
+        // r[0..3] K codes of channels 32g.., r[4..7] V codes of channels
+        // 8g+32k..+7, r[8..11] the record's 16 scale bytes
+        ok = seq_ok && pos >= 0 && pos < N;
+        const uint8_t* rec =
+            a.kvg_in ? a.kvg_in + ((int64_t)b * a.topk + (j < a.topk ? j : 0)) * RECORD
+                     : a.kv + (ok ? cache_row<PAGED>(a.pm, a.cap, s, pos) * RECORD : 0);
+        uint32_t r[12];
+        const uint4 kc = *reinterpret_cast<const uint4*>(rec + 16 * g);
+        const uint4 sc = *reinterpret_cast<const uint4*>(rec + 128);
+        r[0] = kc.x; r[1] = kc.y; r[2] = kc.z; r[3] = kc.w;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            r[4 + k] = *reinterpret_cast<const uint32_t*>(rec + 64 + 4 * g + 16 * k);
+        r[8] = sc.x; r[9] = sc.y; r[10] = sc.z; r[11] = sc.w;
+        convert_q();
+        if (a.kvg_out && ok) {
+            // this lane's share of the record: K bytes 16g.., V dwords 64 + 4g +
+            // 16k, and (g = 0) the 16 scale bytes
+            uint8_t* dst = a.kvg_out + ((int64_t)b * a.topk + j) * RECORD;
+            *reinterpret_cast<uint4*>(dst + 16 * g) = make_uint4(r[0], r[1], r[2], r[3]);
+#pragma unroll
+            for (int k = 0; k < 4; ++k)
+                *reinterpret_cast<uint32_t*>(dst + 64 + 4 * g + 16 * k) = r[4 + k];
+            if (g == 0)
+                *reinterpret_cast<uint4*>(dst + 128) = make_uint4(r[8], r[9], r[10], r[11]);
+        }
+        // K scales of groups 2g, 2g+1 (adjacent bytes); V scales of groups
+        // 2k + g/2, k = 0..3 (bytes g/2, g/2 + 2, ... of the V scale block)
+        const half2_t ks2 = fp8x2_h2<false>(((g >> 1) ? r[9] : r[8]) >> (16 * (g & 1)));
+        const uint32_t gh = (uint32_t)(g >> 1);
+        const uint32_t vsel = gh | ((2u + gh) << 8) | ((4u + gh) << 16) | ((6u + gh) << 24);
+        const uint32_t vsb = __builtin_amdgcn_perm(r[11], r[10], vsel);
+        const half2_t vs01 = fp8x2_h2<false>(vsb), vs23 = fp8x2_h2<true>(vsb);
+        const half2_t k0 = half2_t{ks2.x, ks2.x}, k1 = half2_t{ks2.y, ks2.y};
+        const half2_t vsc[4] = {half2_t{vs01.x, vs01.x}, half2_t{vs01.y, vs01.y},
+                                half2_t{vs23.x, vs23.x}, half2_t{vs23.y, vs23.y}};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            uint32_t w4[4];
+            fp4x8_scaled(r[i], i < 2 ? k0 : k1, w4);
+            kf[i] = __builtin_bit_cast(half8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) fp4x8_scaled(r[4 + k], vsc[k], vv + 4 * k);
+    } else {
+        // r[0..7] K bytes of channels 32g.., r[8..15] V bytes of channels 8g+32k..+7
+        const int64_t u0 = N > WINDOW ? N - WINDOW : 0;
+        ok = seq_ok && u0 + off < N;
+        // (u0 + off) mod w_cap from the uniform u0 mod w_cap: one subtract
+        int32_t w = (int32_t)(u0 % a.w_cap) + off;
+        w = w >= a.w_cap ? w - a.w_cap : w;
+        const int64_t row = ok ? (((int64_t)a.layer * a.n_seq + s) * a.w_cap + w) * D : 0;
+        uint32_t r[16];
+        const uint4 k0 = *reinterpret_cast<const uint4*>(a.wk + row + 32 * g);
+        const uint4 k1 = *reinterpret_cast<const uint4*>(a.wk + row + 32 * g + 16);
+        r[0] = k0.x; r[1] = k0.y; r[2] = k0.z; r[3] = k0.w;
+        r[4] = k1.x; r[5] = k1.y; r[6] = k1.z; r[7] = k1.w;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const uint2 v = *reinterpret_cast<const uint2*>(a.wv + row + 8 * g + 32 * k);
+            r[8 + 2 * k] = v.x;
+            r[9 + 2 * k] = v.y;
+        }
+        convert_q();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t a0 = __builtin_bit_cast(uint32_t, fp8x2_h2<false>(r[2 * i]));
+            const uint32_t a1 = __builtin_bit_cast(uint32_t, fp8x2_h2<true>(r[2 * i]));
+            const uint32_t a2 = __builtin_bit_cast(uint32_t, fp8x2_h2<false>(r[2 * i + 1]));
+            const uint32_t a3 = __builtin_bit_cast(uint32_t, fp8x2_h2<true>(r[2 * i + 1]));
+            kf[i] = __builtin_bit_cast(half8_t, make_uint4(a0, a1, a2, a3));
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            vv[4 * k] = __builtin_bit_cast(uint32_t, fp8x2_h2<false>(r[8 + 2 * k]));
+            vv[4 * k + 1] = __builtin_bit_cast(uint32_t, fp8x2_h2<true>(r[8 + 2 * k]));
+            vv[4 * k + 2] = __builtin_bit_cast(uint32_t, fp8x2_h2<false>(r[9 + 2 * k]));
+            vv[4 * k + 3] = __builtin_bit_cast(uint32_t, fp8x2_h2<true>(r[9 + 2 * k]));
         }
     }
-    // ---- gather + dequantise: 4 threads per entry, 32 channels each
+    if (!ok) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kf[i] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < 16; ++i) vv[i] = 0u;
+    }
+    const uint64_t vmask = __ballot(ok);        // bit e (e < 16): entry e of the wave valid
+
+    // ---- V^T into the wave's LDS tile: lanes c and c^1 swap halves so that
+    // each writes one dword of two entries (row stride VT_STRIDE: conflict free)
+    _Float16* vt = sh.st.vt[wave];
     {
-        const int e = t >> 2, q4 = t & 3;
-        bool ok = false;
-        uint32_t kw[16], vw[16];      // f16x2 words: channels 32*q4 + 2j, 2j+1
-        if (is_main) {
-            const int j = tile * TILE + e;
-            const int32_t pos = (j < a.topk) ? a.idx[(int64_t)b * a.topk + j] : -1;
-            // gathered records sit at known addresses: their loads go out
-            // together with the index load instead of after it
-            const uint8_t* grec =
-                a.kvg_in ? a.kvg_in + ((int64_t)b * a.topk + (j < a.topk ? j : 0)) * RECORD
-                         : nullptr;
-            uint4 kc, vc, sc;
-            if (grec) {
-                kc = *reinterpret_cast<const uint4*>(grec + 16 * q4);
-                vc = *reinterpret_cast<const uint4*>(grec + 64 + 16 * q4);
-                sc = *reinterpret_cast<const uint4*>(grec + 128);
+        const uint32_t pair_sel = (c & 1) ? 0x03020706u : 0x05040100u;
+        const int vt_w = (c & 1) ? VT_STRIDE + (c - 1) : c;
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t x = vv[4 * k + i];
+                const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, DPP_XOR1, 0xf, 0xf,
+                                                                      false);
+                const int d = 8 * g + 32 * k + 2 * i;
+                *reinterpret_cast<uint32_t*>(vt + vt_w + d * VT_STRIDE) =
+                    __builtin_amdgcn_perm(y, x, pair_sel);
             }
-            ok = seq_ok && pos >= 0 && pos < N;
-            if (ok) {
-                if (!grec) {
-                    const uint8_t* rec = a.kv + cache_row<PAGED>(a.pm, a.cap, s, pos) * RECORD;
-                    kc = *reinterpret_cast<const uint4*>(rec + 16 * q4);
-                    vc = *reinterpret_cast<const uint4*>(rec + 64 + 16 * q4);
-                    sc = *reinterpret_cast<const uint4*>(rec + 128);
-                }
-                if (a.kvg_out) {
-                    uint8_t* dst = a.kvg_out + ((int64_t)b * a.topk + j) * RECORD;
-                    *reinterpret_cast<uint4*>(dst + 16 * q4) = kc;
-                    *reinterpret_cast<uint4*>(dst + 64 + 16 * q4) = vc;
-                    if (q4 == 0) *reinterpret_cast<uint4*>(dst + 128) = sc;
-                }
-                // K scales are bytes 0..7 of sc, V scales bytes 8..15; this
-                // thread's 32 channels are groups 2*q4 and 2*q4 + 1
-                const half2_t ks2 =
-                    fp8x2_h2<false>((q4 < 2 ? sc.x : sc.y) >> (16 * (q4 & 1)));
-                const half2_t vs2 =
-                    fp8x2_h2<false>((q4 < 2 ? sc.z : sc.w) >> (16 * (q4 & 1)));
-                const half2_t k0 = half2_t{ks2.x, ks2.x}, k1 = half2_t{ks2.y, ks2.y};
-                const half2_t v0 = half2_t{vs2.x, vs2.x}, v1 = half2_t{vs2.y, vs2.y};
-                fp4x8_scaled(kc.x, k0, kw + 0);
-                fp4x8_scaled(kc.y, k0, kw + 4);
-                fp4x8_scaled(kc.z, k1, kw + 8);
-                fp4x8_scaled(kc.w, k1, kw + 12);
-                fp4x8_scaled(vc.x, v0, vw + 0);
-                fp4x8_scaled(vc.y, v0, vw + 4);
-                fp4x8_scaled(vc.z, v1, vw + 8);
-                fp4x8_scaled(vc.w, v1, vw + 12);
-            }
-        } else {
-            const int64_t u0 = N > WINDOW ? N - WINDOW : 0;
-            const int off = (tile - a.n_main) * TILE + e;               // < 128 <= w_cap
-            ok = seq_ok && u0 + off < N;
-            if (ok) {
-                // (u0 + off) mod w_cap from the uniform u0 mod w_cap: one subtract
-                int32_t w = (int32_t)(u0 % a.w_cap) + off;
-                w = w >= a.w_cap ? w - a.w_cap : w;
-                const int64_t slot =
-                    (((int64_t)a.layer * a.n_seq + s) * a.w_cap + w) * D + 32 * q4;
-                const uint4* kp = reinterpret_cast<const uint4*>(a.wk + slot);
-                const uint4* vp = reinterpret_cast<const uint4*>(a.wv + slot);
-                const uint4 k0 = kp[0], k1 = kp[1], v0 = vp[0], v1 = vp[1];
-                const uint32_t kr[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-                const uint32_t vr[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-#pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    kw[2 * i] = __builtin_bit_cast(uint32_t, fp8x2_h2<false>(kr[i]));
-                    kw[2 * i + 1] = __builtin_bit_cast(uint32_t, fp8x2_h2<true>(kr[i]));
-                    vw[2 * i] = __builtin_bit_cast(uint32_t, fp8x2_h2<false>(vr[i]));
-                    vw[2 * i + 1] = __builtin_bit_cast(uint32_t, fp8x2_h2<true>(vr[i]));
-                }
-            }
-        }
-        if (!ok) {
-#pragma unroll
-            for (int i = 0; i < 16; ++i) kw[i] = vw[i] = 0u;
-        }
-        uint4* krow = reinterpret_cast<uint4*>(&sh.K[e * KROW + 32 * q4]);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            krow[i] = make_uint4(kw[4 * i], kw[4 * i + 1], kw[4 * i + 2], kw[4 * i + 3]);
-        unsigned short* vt = reinterpret_cast<unsigned short*>(sh.Vt);
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            vt[(32 * q4 + 2 * i) * VROW + e] = (unsigned short)(vw[i] & 0xffffu);
-            vt[(32 * q4 + 2 * i + 1) * VROW + e] = (unsigned short)(vw[i] >> 16);
-        }
-        if (q4 == 0) sh.valid[e] = ok;
     }
+    // the tile is private to this wave and LDS executes a wave's operations in
+    // order; this only keeps the compiler from moving its reads above the writes
+    asm volatile("" ::: "memory");
 
-    __syncthreads();
+    __syncthreads();                            // the query slices are in LDS
 
-    // ---- S = Q K^T for entries 16*wave .. +15 (hi and lo parts of q in two
-    // independent accumulator chains)
+    // ---- S^T = K Q^T: lane (c, g) gets S[head c][entry 4g + r]; hi and lo
+    // parts of q in two independent accumulator chains
     float4_t sacc;
     {
         float4_t shi = {0.f, 0.f, 0.f, 0.f}, slo = {0.f, 0.f, 0.f, 0.f};
-        const int ent = 16 * wave + (lane & 15), g = lane >> 4;
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const half4_t kf = *reinterpret_cast<const half4_t*>(&sh.K[ent * KROW + 16 * ks + 4 * g]);
-            shi = __builtin_amdgcn_mfma_f32_16x16x16f16(qhi[ks], kf, shi, 0, 0, 0);
-            slo = __builtin_amdgcn_mfma_f32_16x16x16f16(qlo[ks], kf, slo, 0, 0, 0);
+        for (int sl = 0; sl < 4; ++sl) {
+            shi = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[sl], sh.st.q[0][sl][lane], shi, 0, 0,
+                                                         0);
+            slo = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[sl], sh.st.q[1][sl][lane], slo, 0, 0,
+                                                         0);
         }
         sacc = shi + slo;
     }
-    // lane holds S[head 4*(lane/16) + r][entry 16*wave + lane%16]; logits in
-    // log2 units (log2(e) folded into the scale), so exp2 is one v_exp_f32
+    // logits in log2 units (log2(e) folded into the scale): exp2 is one v_exp_f32
     const float lscale = a.sm_scale * LOG2E * (is_main ? 1.0f : a.wk_scale);
-    const bool ent_ok = sh.valid[16 * wave + (lane & 15)];
     float sv[4];
+    float m = NEG_INF;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) sv[r] = ent_ok ? sacc[r] * lscale : NEG_INF;
+    for (int q4 = 0; q4 < 4; ++q4) {
+        const bool v_ok = (vmask >> (4 * g + q4)) & 1u;
+        sv[q4] = v_ok ? sacc[q4] * lscale : NEG_INF;
+        m = fmaxf(m, sv[q4]);
+    }
+    m = max_xor32(max_xor16(m));                // the wave's max for head c
+    half4_t phi, plo;
+    float lsum = 0.0f;
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+        const float p = sv[q4] == NEG_INF ? 0.0f : __builtin_amdgcn_exp2f(sv[q4] - m);
+        lsum += p;
+        const _Float16 h = (_Float16)p;
+        phi[q4] = h;
+        plo[q4] = (_Float16)(p - (float)h);
+    }
+    lsum = add_xor32(add_xor16(lsum));
 
-    // ---- tile max per head: 16 lanes of a row, then the 4 waves
-    float mx[4];
+    // ---- O^T = V^T P^T over the wave's 16 entries: O^T[d = 16 mt + 4g + r][h = c]
+    float4_t o[8];
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        float v = sv[r];
-        v = fmaxf(v, dpp_f32<DPP_XOR1>(v));
-        v = fmaxf(v, dpp_f32<DPP_XOR2>(v));
-        v = fmaxf(v, dpp_f32<DPP_ROR4>(v));
-        v = fmaxf(v, dpp_f32<DPP_ROR8>(v));
-        mx[r] = v;
+    for (int mt = 0; mt < 8; ++mt) {
+        const half4_t vf = *reinterpret_cast<const half4_t*>(&vt[(16 * mt + c) * VT_STRIDE + 4 * g]);
+        float4_t acc = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, phi, float4_t{0.f, 0.f, 0.f, 0.f},
+                                                             0, 0, 0);
+        o[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, plo, acc, 0, 0, 0);
     }
-    if ((lane & 15) == 0) {
+
+    // ---- combine the 4 waves in LDS and write the tile's partial record
+    __syncthreads();                            // every wave is done with its V^T tile
+    if (g == 0) {
+        sh.mg.m[wave][c] = m;
+        sh.mg.l[wave][c] = lsum;
+    }
 #pragma unroll
-        for (int r = 0; r < 4; ++r) sh.red[wave][4 * (lane >> 4) + r] = mx[r];
-    }
+    for (int mt = 0; mt < 8; ++mt)
+        *reinterpret_cast<float4_t*>(&sh.mg.o[wave][c * OROW + 16 * mt + 4 * g]) = o[mt];
     __syncthreads();
-    float m_tile[4], p[4], lsum[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int h = 4 * (lane >> 4) + r;
-        m_tile[r] = fmaxf(fmaxf(sh.red[0][h], sh.red[1][h]), fmaxf(sh.red[2][h], sh.red[3][h]));
-        p[r] = (m_tile[r] == NEG_INF || sv[r] == NEG_INF) ? 0.0f
-                                                        : __builtin_amdgcn_exp2f(sv[r] - m_tile[r]);
-        float v = p[r];
-        v += dpp_f32<DPP_XOR1>(v);
-        v += dpp_f32<DPP_XOR2>(v);
-        v += dpp_f32<DPP_ROR4>(v);
-        v += dpp_f32<DPP_ROR8>(v);
-        lsum[r] = v;
-        const int ent = 16 * wave + (lane & 15);
-        _Float16 ph = (_Float16)p[r];
-        sh.Phi[h * PROW + ent] = ph;
-        sh.Plo[h * PROW + ent] = (_Float16)(p[r] - (float)ph);
-    }
-    if ((lane & 15) == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) sh.lsum[wave][4 * (lane >> 4) + r] = lsum[r];
-    }
-    __syncthreads();   // P and the per-wave sums written
-    if (t < HEADS) {
-        part[HEADS + t] = sh.lsum[0][t] + sh.lsum[1][t] + sh.lsum[2][t] + sh.lsum[3][t];
-    }
-
-    // ---- O = P V for dims 32*wave .. +31 (two 16-dim tiles)
-    float4_t oacc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
     {
-        const int h = lane & 15, g = lane >> 4;
+        const int h = t >> 4, d0 = (t & 15) * 8;
+        float mw[AT_WAVES], M = NEG_INF;
 #pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            const half4_t ph = *reinterpret_cast<const half4_t*>(&sh.Phi[h * PROW + 16 * ks + 4 * g]);
-            const half4_t pl = *reinterpret_cast<const half4_t*>(&sh.Plo[h * PROW + 16 * ks + 4 * g]);
+        for (int w = 0; w < AT_WAVES; ++w) {
+            mw[w] = sh.mg.m[w][h];
+            M = fmaxf(M, mw[w]);
+        }
+        float L = 0.0f, acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+        if (M != NEG_INF) {
 #pragma unroll
-            for (int nt = 0; nt < 2; ++nt) {
-                const int d = 32 * wave + 16 * nt + (lane & 15);
-                const half4_t vf = *reinterpret_cast<const half4_t*>(&sh.Vt[d * VROW + 16 * ks + 4 * g]);
-                oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(ph, vf, oacc[nt], 0, 0, 0);
-                oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x16f16(pl, vf, oacc[nt], 0, 0, 0);
+            for (int w = 0; w < AT_WAVES; ++w) {
+                const float wt = mw[w] == NEG_INF ? 0.0f : __builtin_amdgcn_exp2f(mw[w] - M);
+                L += wt * sh.mg.l[w][h];
+                const float4* src = reinterpret_cast<const float4*>(&sh.mg.o[w][h * OROW + d0]);
+                const float4 x0 = src[0], x1 = src[1];
+                acc[0] += wt * x0.x; acc[1] += wt * x0.y; acc[2] += wt * x0.z; acc[3] += wt * x0.w;
+                acc[4] += wt * x1.x; acc[5] += wt * x1.y; acc[6] += wt * x1.z; acc[7] += wt * x1.w;
             }
         }
-    }
-    // lane holds O[head 4*(lane/16) + r][dim 32*wave + 16*nt + lane%16]
-    const float vscale = is_main ? 1.0f : a.wv_scale;
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int h = 4 * (lane >> 4) + r;
-            const int d = 32 * wave + 16 * nt + (lane & 15);
-            part[2 * HEADS + h * D + d] = oacc[nt][r] * vscale;
+        // the window's per-tensor V scale multiplies its PV products
+        const float vscale = is_main ? 1.0f : a.wv_scale;
+        float* part = a.part + ((int64_t)b * a.n_tiles + tile) * ATTN_PART_FLOATS;
+        if ((t & 15) == 0) {
+            part[h] = M * LN2;                  // partials carry natural-log maxima
+            part[HEADS + h] = L;
         }
-    }
-    if (wave == 0 && (lane & 15) == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) part[4 * (lane >> 4) + r] = m_tile[r] * LN2;   // natural log
+        float4* dst = reinterpret_cast<float4*>(part + 2 * HEADS + h * D + d0);
+        dst[0] = make_float4(acc[0] * vscale, acc[1] * vscale, acc[2] * vscale, acc[3] * vscale);
+        dst[1] = make_float4(acc[4] * vscale, acc[5] * vscale, acc[6] * vscale, acc[7] * vscale);
     }
 }
 
@@ -511,15 +564,21 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
     }
     // ---- query fragments (B operand of S^T = K Q^T): Q[h = c][32g + 4ks + j],
     // split into f16 hi + lo; built after the first steps' loads were issued,
-    // so the two latencies overlap.  Every wave uses the same fragments; wave 0 builds
-    // them once into LDS (in lane order, so the per-step reads are conflict
-    // free) instead of each wave holding 32 VGPRs of them.
-    if (wave == 0) {
-        const float* qrow = a.q + ((int64_t)b * HEADS + c) * D + 32 * g;
+    // so the two latencies overlap.  Every wave uses the same fragments: the
+    // workgroup loads the query once, coalesced (two float4 per thread), and
+    // stores each float4 as the half4 of the lane and ks that take it (in lane
+    // order, so the per-step reads are conflict free).
+    {
+        float4 qv[2];
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            const float4 v = *reinterpret_cast<const float4*>(qrow + 4 * ks);
-            const float x[4] = {v.x, v.y, v.z, v.w};
+        for (int k = 0; k < 2; ++k)
+            qv[k] = *reinterpret_cast<const float4*>(a.q + (int64_t)b * HEADS * D +
+                                                      4 * (t + AT_THREADS * k));
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const int e = 4 * (t + AT_THREADS * k);          // h * 128 + d, d % 4 == 0
+            const int h = e >> 7, d = e & (D - 1);
+            const float x[4] = {qv[k].x, qv[k].y, qv[k].z, qv[k].w};
             half4_t hi4, lo4;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -527,8 +586,9 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
                 hi4[i] = hi;
                 lo4[i] = (_Float16)(x[i] - (float)hi);
             }
-            sh.st.q[0][ks][lane] = hi4;
-            sh.st.q[1][ks][lane] = lo4;
+            const int fl = 16 * (d >> 5) + h, ks = (d >> 2) & 7;
+            sh.st.q[0][ks][fl] = hi4;
+            sh.st.q[1][ks][fl] = lo4;
         }
     }
     __syncthreads();
@@ -701,7 +761,7 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
     }
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
-        *reinterpret_cast<float4_t*>(&sh.mg.o[wave][c * D + 16 * mt + 4 * g]) = o[mt];
+        *reinterpret_cast<float4_t*>(&sh.mg.o[wave][c * OROW + 16 * mt + 4 * g]) = o[mt];
     __syncthreads();
     {
         const int h = t >> 4, d0 = (t & 15) * 8;
@@ -717,7 +777,7 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
             for (int w = 0; w < AT_WAVES; ++w) {
                 const float wt = mw[w] == NEG_INF ? 0.0f : __builtin_amdgcn_exp2f(mw[w] - M);
                 L += wt * sh.mg.l[w][h];
-                const float4* src = reinterpret_cast<const float4*>(&sh.mg.o[w][h * D + d0]);
+                const float4* src = reinterpret_cast<const float4*>(&sh.mg.o[w][h * OROW + d0]);
                 const float4 x0 = src[0], x1 = src[1];
                 acc[0] += wt * x0.x; acc[1] += wt * x0.y; acc[2] += wt * x0.z; acc[3] += wt * x0.w;
                 acc[4] += wt * x1.x; acc[5] += wt * x1.y; acc[6] += wt * x1.z; acc[7] += wt * x1.w;
