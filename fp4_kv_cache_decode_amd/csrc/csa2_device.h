@@ -151,4 +151,54 @@ __device__ __forceinline__ int64_t cache_row(const PageMap& m, int64_t cap, int3
     return ((int64_t)pg << m.shift) + (t & (((int64_t)1 << m.shift) - 1));
 }
 
+// ---------------------------------------------------------------- LDS copies
+// 64-byte rows (an indexer key, or 16 floats of a top-k row) staged in LDS by
+// global_load_lds_dwordx4: one instruction copies a contiguous 1 KB (lane l's
+// 16 bytes land at lds + 16 l), so the global side is fully coalesced and no
+// VGPR holds data in flight.  Reading 16 consecutive rows' same 16-byte chunk
+// would hit only four 16-byte bank groups, so the chunks of row j (j mod 16)
+// are stored rotated by chunk_rot(j): chunk m sits at position
+// (m + chunk_rot(j)) mod 4 of the row's 64 bytes.  The rotation is applied on
+// the load side (each lane fetches the chunk that belongs at its LDS position,
+// the same contiguous 1 KB per instruction) and undone by per-lane read
+// addresses.  chunk_rot is a permutation within every group of 4 rows with
+// equal j mod 4 (16-lane passes over 64 banks) and within every group of 4
+// rows of equal parity in an aligned run of 8 (8-lane passes over 32 banks).
+__device__ __forceinline__ int chunk_rot(int j) { return ((j >> 1) ^ (j >> 3)) & 3; }
+
+// One 1 KB copy: lane l's 16 bytes from sbase + voff to LDS address
+// lds_addr + 16 l.  m0 is named as clobbered: it carries the LDS address, and
+// no code of these kernels keeps a value in m0.  NT marks the load
+// non-temporal (data read once).  Written as inline asm so that the compiler
+// neither reorders the copies nor drains vmcnt before every LDS read; callers
+// wait explicitly with wait_vm (loads complete in order).  The memory clobber
+// keeps LDS reads after their wait and before the next refill of the slot.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+template <bool NT>
+__device__ __forceinline__ void dma_1k(uint32_t voff, const uint8_t* sbase, uint32_t lds_addr) {
+    if (NT)
+        asm volatile(
+            "s_mov_b32 m0, %2\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %0, %1 nt"
+            :
+            : "v"(voff), "s"(sbase), "s"(lds_addr)
+            : "memory", "m0");
+    else
+        asm volatile(
+            "s_mov_b32 m0, %2\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %0, %1"
+            :
+            : "v"(voff), "s"(sbase), "s"(lds_addr)
+            : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
 }  // namespace csa2

@@ -235,40 +235,7 @@ score_kernel(ScoreArgs a, const float* __restrict__ q_all, const uint8_t* __rest
 constexpr int SCAN_STAGES = 2;   // 16 waves x 2 x 4 KB = 128 KB of LDS per CU
 constexpr int SCAN_STEP_BYTES = STEP * IDX_DIM;   // 4096
 
-__device__ __forceinline__ int chunk_rot(int j) { return ((j >> 1) ^ (j >> 3)) & 3; }
-
-// m0 is named as clobbered: it carries the LDS address of the copy, and no
-// other code of these kernels keeps a value in m0.  NT marks the load
-// non-temporal: a decode scan reads each key once per step, and a long
-// context's keys outgrow the caches anyway (measured at the decode shape:
-// 48-52 us instead of 56-58 us for 4 x 1 Mi keys).
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-template <bool NT>
-__device__ __forceinline__ void dma_1k(uint32_t voff, const uint8_t* sbase, uint32_t lds_addr) {
-    if (NT)
-        asm volatile(
-            "s_mov_b32 m0, %2\n\t"
-            "s_nop 0\n\t"
-            "global_load_lds_dwordx4 %0, %1 nt"
-            :
-            : "v"(voff), "s"(sbase), "s"(lds_addr)
-            : "memory", "m0");
-    else
-        asm volatile(
-            "s_mov_b32 m0, %2\n\t"
-            "s_nop 0\n\t"
-            "global_load_lds_dwordx4 %0, %1"
-            :
-            : "v"(voff), "s"(sbase), "s"(lds_addr)
-            : "memory", "m0");
-}
-#pragma clang diagnostic pop
-
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
-}
+// chunk_rot, dma_1k and wait_vm live in csa2_device.h (shared with top-k).
 
 // One workgroup per CU: 16 waves (4 per SIMD), each with a private LDS ring.
 // (Measured: 16 waves with 2 slots beat 12 waves with 3 slots by about 3%.)
