@@ -15,17 +15,21 @@
 //
 // Stream kernel (gfx950, wave64): each wave streams 16-entry steps of one query with
 // its own online softmax (flash-decoding).  For a step, lane (c, g) (c = lane
-// mod 16, g = lane / 16) gathers entry c: 32 K channels 32g..32g+31 and 32 V
-// channels {8g + 32k + i}.  Scores are computed transposed, S^T = K Q^T, on
-// v_mfma_f32_16x16x16_f16 with K as the A operand straight from the gathering
-// lane's registers: the contraction over channels is taken in the order
-// d = 32g + 4ks + j, which is the order the lane holds them in, and the query
-// fragments are loaded in the same order.  The result leaves lane (c, g) with
-// the scores of head c for entries 4g..4g+3, which is exactly the B-operand
-// layout of O^T = V^T P^T, so the softmax weights never move between lanes.
-// Only V is transposed, through a per-wave LDS tile; no barrier is needed
-// inside the loop because every wave touches only its own tile.  The next
-// step's records are in flight while a step is computed.
+// mod 16, g = lane / 16) gathers K channels 32g..32g+31 of entry c and the V
+// channel group m = 4(c mod 2) + g (channels 16m..16m+15) of the entry pair
+// 2j, 2j+1 (j = c / 2), so each V conversion yields one f16 pair of two
+// entries, which is one dword of the transposed V tile.  Scores are computed
+// transposed, S^T = K Q^T, on v_mfma_f32_16x16x32_f16 with K as the A operand
+// straight from the gathering lane's registers: slice ks of the contraction
+// takes channels 32g + 8ks .. +7, the order the lane holds them in, and the
+// query slices are staged in LDS in the same order.  The result leaves lane
+// (c, g) with the scores of head c for entries 4g..4g+3, which is exactly the
+// B-operand layout of O^T = V^T P^T (v_mfma_f32_16x16x16_f16), so the softmax
+// weights never move between lanes.  Only V is transposed, through a per-wave
+// LDS tile; no barrier is needed inside the loop because every wave touches
+// only its own tile.  The next step's records are in flight while a step is
+// computed.  Records are read with buffer loads: 32-bit offsets from the
+// sequence's base, the constant parts in the instruction.
 //
 // Precision: dequantised values are exact in f16 (an E2M1 value times an E4M3
 // scale has at most 6 significant bits, an E4M3 value has 4).  The fp32 query
@@ -99,11 +103,40 @@ struct StreamArgs {
     float sm_scale;
 };
 
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+
+// Stream kernel V^T tile of one wave, in dwords.  Row d = 16m + t (channel d,
+// m = d / 16) holds the step's 16 entries as 8 f16 pairs (dword j: entries 2j,
+// 2j+1) and starts at vt_block(m) + VT_ROW * t.  Writes go out as one row per
+// instruction from each of 8 lanes per group m; reads are the PV A operand,
+// rows 16mt + i and dwords 2kb, 2kb + 1 for lane (i, kb).  With 32 four-byte
+// banks served per half wave (4-byte accesses) or quarter wave (8-byte):
+//  * a write instruction's half wave covers groups m with equal bit 1, whose
+//    blocks start in distinct quarters of the banks (vt_block(m) mod 32), so
+//    its 4 rows x 8 dwords hit 32 distinct banks;
+//  * a read's quarter wave covers 16 rows of one block at stride 10 dwords,
+//    whose 2-dword pieces fall on 16 distinct even banks.
+// Over 64 banks the 8 block starts are distinct too.  Blocks are 192 dwords
+// apart plus that offset, so they do not overlap (a block spans 158 dwords).
+constexpr int VT_ROW = 10;
+__host__ __device__ constexpr int vt_block(int m) {
+    return 192 * m + 8 * ((m & 1) | (((m >> 2) & 1) << 1) | (((m >> 1) & 1) << 2));
+}
+constexpr int VT_DWORDS = vt_block(7) + VT_ROW * 15 + 8 + 2;   // 8-byte multiple
+
+// Lane slot holding query slice ks for lane L: L with its low three bits
+// flipped by ks and bit 4 of L.  Reads by 8-lane groups stay a permutation of
+// the group; the prologue's 16-lane stores of one head (varying ks and g)
+// land on 8 distinct slots mod 8.
+__host__ __device__ constexpr int q_slot(int ks, int L) {
+    return L ^ (ks | (((L >> 4) & 1) << 2));
+}
+
 struct StreamShared {
     union {
         struct {
-            _Float16 vt[AT_WAVES][D * VT_STRIDE];  // per-wave V^T of one step
-            half4_t q[2][8][64];                   // query fragments (hi, lo) per ks, per lane
+            uint32_t vt[AT_WAVES][VT_DWORDS];      // per-wave V^T of one step
+            half8_t q[2][4][64];                   // query slices (hi, lo), by q_slot
         } st;
         struct {
             float o[AT_WAVES][HEADS * OROW];
@@ -180,8 +213,6 @@ struct TileArgs {
     float wv_scale;
     float sm_scale;
 };
-
-typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 
 struct TileShared {
     union {
@@ -462,17 +493,29 @@ __global__ void __launch_bounds__(AT_THREADS) attn_tile_kernel(TileArgs a) {
 // ---------------------------------------------------------------------------
 // Stream kernel (large batches, bandwidth): see the file header.
 
-// Raw bytes of one step's entry for this lane, loaded ahead of use.
-//  main:   r[0..3] K codes of channels 32g..32g+31, r[4..7] V codes of channels
-//          8g+32k..8g+32k+7 (k = 0..3), r[8..11] the record's 16 scale bytes
-//  window: r[0..7] K bytes of channels 32g..32g+31, r[8..15] V bytes of
-//          channels 8g+32k..+7 (two dwords per k)
+// Raw bytes of one step for this lane, loaded ahead of use.
+//  main:   r[0..3] K codes of entry c, channels 32g..32g+31; r[4..7] that
+//          record's 16 scale bytes; r[8..9] and r[10..11] V codes of channel
+//          group m of entries 2j and 2j+1
+//  window: r[0..7] K bytes of entry c, channels 32g..32g+31; r[8..11] and
+//          r[12..15] V bytes of channels 16m..16m+15 of entries 2j and 2j+1
 struct Raw {
     uint32_t r[16];
 };
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// Buffer resource word 3 on gfx9-family targets (32-bit data format, no
+// swizzle); loads past num_records return zeros.
+constexpr int BUF_DWORD3 = 0x00020000;
+
+// Address modes of the main records: 32-bit offsets from the sequence's base
+// (every contiguous cache whose sequences span at most 4 GiB), 64-bit offsets,
+// or a page table.
+enum { AM_OFF32 = 0, AM_FLAT64 = 1, AM_PAGED = 2 };
+
 // 4 workgroups (16 waves) per CU: at most 128 VGPRs
-template <bool PAGED>
+template <int AM>
 __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a) {
     __shared__ StreamShared sh;
     const int split = blockIdx.x;
@@ -481,6 +524,7 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int c = lane & 15, g = lane >> 4;
+    const int j = c >> 1, o = c & 1, m = 4 * o + g;    // V: entries 2j, 2j+1, channel group m
     const int32_t s = a.seq[b];
     const int64_t N = clamp64(a.ctx[b], 0, a.cap);
     const bool seq_ok = s >= 0 && s < a.n_seq;
@@ -492,82 +536,127 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
     const int t_end = (int)((int64_t)(split + 1) * a.n_sub / a.n_split);
     const int main_end = t_end < a.n_sub_main ? t_end : a.n_sub_main;
     const int32_t* idx_row = a.idx + (int64_t)b * a.topk;
+    // uniform bases: the sequence's first record, the query's gathered records
+    // and its window rows
+    const uint8_t* kv_s = a.kv + (AM != AM_PAGED && seq_ok ? (int64_t)s * a.cap * RECORD : 0);
+    const uint8_t* kvg_b = a.kvg_in ? a.kvg_in + (int64_t)b * a.topk * RECORD : nullptr;
+    const uint8_t* wk_q = a.wk + win_base * D;
+    const uint8_t* wv_q = a.wv + win_base * D;
 
+    // Buffer resources (uniform) for 32-bit-offset loads with the constant
+    // parts in the instruction's offset field: the sequence's records (or the
+    // query's gathered records), the query's window rows and index list.
+    const bool main_buf = kvg_b != nullptr || AM == AM_OFF32;
+    const __amdgpu_buffer_rsrc_t rs_main = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kvg_b ? kvg_b : kv_s), 0,
+        (int)(kvg_b ? (uint32_t)a.topk * (uint32_t)RECORD
+                    : (uint32_t)(AM == AM_OFF32 ? a.cap * RECORD : 0)),
+        BUF_DWORD3);
+    const __amdgpu_buffer_rsrc_t rs_wk =
+        __builtin_amdgcn_make_buffer_rsrc((void*)wk_q, 0, a.w_cap * D, BUF_DWORD3);
+    const __amdgpu_buffer_rsrc_t rs_wv =
+        __builtin_amdgcn_make_buffer_rsrc((void*)wv_q, 0, a.w_cap * D, BUF_DWORD3);
+    const __amdgpu_buffer_rsrc_t rs_idx =
+        __builtin_amdgcn_make_buffer_rsrc((void*)idx_row, 0, a.topk * 4, BUF_DWORD3);
 
+    // index list entry c of step st, loaded one step ahead of its fetch (past
+    // the list the load returns 0; fetch discards it)
     auto load_idx = [&](int st) -> int32_t {
-        const int j = SUB * st + c;
-        return (st < main_end && j < a.topk) ? idx_row[j] : -1;
+        return __builtin_amdgcn_raw_buffer_load_b32(rs_idx, 4 * (SUB * st + c), 0, 0);
     };
-    // issue the loads of step st for this lane; returns whether the entry is valid
-    auto fetch = [&](int st, int32_t pos, Raw& w) -> bool {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) w.r[i] = 0u;
+    // issue the loads of step st; raw is this lane's index list load (entry c).
+    // Returns the validity of entries c, 2j and 2j+1 in bits 0, 1, 2.
+    auto fetch = [&](int st, int32_t raw, Raw& w) -> uint32_t {
+        const int32_t pos = (st < main_end && SUB * st + c < a.topk) ? raw : -1;
+        const int32_t pos_p = __builtin_amdgcn_mov_dpp(pos, DPP_XOR1, 0xf, 0xf, false);
         if (st < a.n_sub_main) {
-            const bool ok = seq_ok && pos >= 0 && pos < N;
-            const int j = SUB * st + c;
-            const uint8_t* rec =
-                a.kvg_in ? a.kvg_in + ((int64_t)b * a.topk + (j < a.topk ? j : 0)) * RECORD
-                         : a.kv + (ok ? cache_row<PAGED>(a.pm, a.cap, s, pos) * RECORD : 0);
-            const uint4 kc = *reinterpret_cast<const uint4*>(rec + 16 * g);
-            const uint4 sc = *reinterpret_cast<const uint4*>(rec + 128);
-            w.r[0] = kc.x; w.r[1] = kc.y; w.r[2] = kc.z; w.r[3] = kc.w;
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                w.r[4 + k] = *reinterpret_cast<const uint32_t*>(rec + 64 + 4 * g + 16 * k);
-            w.r[8] = sc.x; w.r[9] = sc.y; w.r[10] = sc.z; w.r[11] = sc.w;
-            return ok;
+            const int32_t pa = o ? pos_p : pos, pb = o ? pos : pos_p;
+            const bool oka = seq_ok && pa >= 0 && pa < N, okb = seq_ok && pb >= 0 && pb < N;
+            const int e = SUB * st + 2 * j;
+            u32x4 kc, sc;
+            u32x2 va, vb;
+            if (main_buf) {
+                const uint32_t oa = kvg_b ? (uint32_t)(e < a.topk ? e : 0) * RECORD
+                                          : (oka ? (uint32_t)pa * RECORD : 0u);
+                const uint32_t ob = kvg_b ? (uint32_t)(e + 1 < a.topk ? e + 1 : 0) * RECORD
+                                          : (okb ? (uint32_t)pb * RECORD : 0u);
+                const uint32_t oc = o ? ob : oa;
+                kc = __builtin_amdgcn_raw_buffer_load_b128(rs_main, oc + 16 * g, 0, 0);
+                sc = __builtin_amdgcn_raw_buffer_load_b128(rs_main, oc + 128, 0, 0);
+                va = __builtin_amdgcn_raw_buffer_load_b64(rs_main, oa + 8 * m + 64, 0, 0);
+                vb = __builtin_amdgcn_raw_buffer_load_b64(rs_main, ob + 8 * m + 64, 0, 0);
+            } else {
+                auto rec = [&](int32_t p, bool ok) -> const uint8_t* {
+                    if constexpr (AM == AM_PAGED)
+                        return a.kv + (ok ? cache_row<true>(a.pm, a.cap, s, p) * RECORD : 0);
+                    else
+                        return kv_s + (ok ? (int64_t)p * RECORD : 0);
+                };
+                const uint8_t* ra = rec(pa, oka);
+                const uint8_t* rb = rec(pb, okb);
+                const uint8_t* rc = o ? rb : ra;
+                kc = *reinterpret_cast<const u32x4*>(rc + 16 * g);
+                sc = *reinterpret_cast<const u32x4*>(rc + 128);
+                va = *reinterpret_cast<const u32x2*>(ra + 64 + 8 * m);
+                vb = *reinterpret_cast<const u32x2*>(rb + 64 + 8 * m);
+            }
+            w.r[0] = kc[0]; w.r[1] = kc[1]; w.r[2] = kc[2]; w.r[3] = kc[3];
+            w.r[4] = sc[0]; w.r[5] = sc[1]; w.r[6] = sc[2]; w.r[7] = sc[3];
+            w.r[8] = va[0]; w.r[9] = va[1]; w.r[10] = vb[0]; w.r[11] = vb[1];
+            w.r[12] = w.r[13] = w.r[14] = w.r[15] = 0u;     // unused by main steps
+            return (uint32_t)(o ? okb : oka) | ((uint32_t)oka << 1) | ((uint32_t)okb << 2);
         }
-        const int off = (st - a.n_sub_main) * SUB + c;      // < 128 <= w_cap
-        const bool ok = seq_ok && u0 + off < N;
-        int32_t slot = slot0 + off;                          // (u0 + off) mod w_cap
-        slot = slot >= a.w_cap ? slot - a.w_cap : slot;
-        const int64_t row = ok ? (win_base + slot) * D : 0;
-        const uint4 k0 = *reinterpret_cast<const uint4*>(a.wk + row + 32 * g);
-        const uint4 k1 = *reinterpret_cast<const uint4*>(a.wk + row + 32 * g + 16);
-        w.r[0] = k0.x; w.r[1] = k0.y; w.r[2] = k0.z; w.r[3] = k0.w;
-        w.r[4] = k1.x; w.r[5] = k1.y; w.r[6] = k1.z; w.r[7] = k1.w;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint2 v = *reinterpret_cast<const uint2*>(a.wv + row + 8 * g + 32 * k);
-            w.r[8 + 2 * k] = v.x;
-            w.r[9 + 2 * k] = v.y;
-        }
-        return ok;
+        const int off = (st - a.n_sub_main) * SUB;           // + entry < 128 <= w_cap
+        auto wrow = [&](int e) -> uint32_t {
+            int32_t sl = slot0 + off + e;                     // (u0 + off + e) mod w_cap
+            sl = sl >= a.w_cap ? sl - a.w_cap : sl;
+            return (uint32_t)sl * (uint32_t)D;
+        };
+        const bool oka = seq_ok && u0 + off + 2 * j < N, okb = seq_ok && u0 + off + 2 * j + 1 < N;
+        const uint32_t ra = oka ? wrow(2 * j) : 0u, rb = okb ? wrow(2 * j + 1) : 0u;
+        const uint32_t rc = o ? rb : ra;
+        const u32x4 k0 = __builtin_amdgcn_raw_buffer_load_b128(rs_wk, rc + 32 * g, 0, 0);
+        const u32x4 k1 = __builtin_amdgcn_raw_buffer_load_b128(rs_wk, rc + 32 * g + 16, 0, 0);
+        const u32x4 va = __builtin_amdgcn_raw_buffer_load_b128(rs_wv, ra + 16 * m, 0, 0);
+        const u32x4 vb = __builtin_amdgcn_raw_buffer_load_b128(rs_wv, rb + 16 * m, 0, 0);
+        w.r[0] = k0[0]; w.r[1] = k0[1]; w.r[2] = k0[2]; w.r[3] = k0[3];
+        w.r[4] = k1[0]; w.r[5] = k1[1]; w.r[6] = k1[2]; w.r[7] = k1[3];
+        w.r[8] = va[0]; w.r[9] = va[1]; w.r[10] = va[2]; w.r[11] = va[3];
+        w.r[12] = vb[0]; w.r[13] = vb[1]; w.r[14] = vb[2]; w.r[15] = vb[3];
+        return (uint32_t)(o ? okb : oka) | ((uint32_t)oka << 1) | ((uint32_t)okb << 2);
     };
 
     // softmax state of head c (lanes c, c+16, c+32, c+48 hold the same m; l is
     // this lane's partial sum) and O^T[d = 16 mt + 4g + r][h = c]
     float m_run = NEG_INF, l_run = 0.0f;
-    float4_t o[8];
+    float4_t o_acc[8];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) o[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
-    _Float16* vt = sh.st.vt[wave];
-
-    // packed V^T writes: byte selector (even lane: own low half, then the
-    // neighbour's low half; odd lane: the neighbour's high half, then its own)
-    // and the lane's offset inside the tile
-    const uint32_t pair_sel = (c & 1) ? 0x03020706u : 0x05040100u;
-    const int vt_w = (c & 1) ? VT_STRIDE + (c - 1) : c;
-    // v_perm selector gathering V scale bytes g/2, g/2 + 2, g/2 + 4, g/2 + 6 of
-    // the record's 8-byte V scale block (dwords r[10], r[11])
-    const uint32_t gh = (uint32_t)(g >> 1);
-    const uint32_t vsel = gh | ((2u + gh) << 8) | ((4u + gh) << 16) | ((6u + gh) << 24);
+    for (int mt = 0; mt < 8; ++mt) o_acc[mt] = float4_t{0.f, 0.f, 0.f, 0.f};
+    uint32_t* vt = sh.st.vt[wave];
+    // V^T tile addresses: this lane writes row 16m + t, dword j (t = 0..15) and
+    // reads, as the PV A operand, row 16mt + c, dwords 2g, 2g + 1 (mt = 0..7)
+    uint32_t* const vt_wr = vt + vt_block(m) + j;
+    const uint32_t* const vt_rd = vt + VT_ROW * c + 2 * g;
+    // v_perm selector putting the V scale bytes of entries 2j, 2j+1 (byte g of
+    // the lane's own dword and of the one received from lane c ^ 1) in order
+    const uint32_t vsel = o ? ((uint32_t)g | ((4u + g) << 8) | 0x0c0c0000u)
+                            : ((4u + g) | ((uint32_t)g << 8) | 0x0c0c0000u);
     int st = t_begin + wave;
-    // two steps in flight: while step i is computed, step i+1 is arriving and
-    // step i+2 is issued (its index list entries were loaded one step earlier)
-    Raw cur, nxt;
-    bool ok_cur = false, ok_nxt = false;
+    // one step in flight: while step i is computed, step i+1's records are
+    // arriving (their index list entries were loaded one step earlier)
+    Raw cur;
+    uint32_t ok_cur = 0;
     int32_t idx_next = -1;
     if (st < t_end) {
         ok_cur = fetch(st, load_idx(st), cur);
         idx_next = load_idx(st + AT_WAVES);
     }
-    // ---- query fragments (B operand of S^T = K Q^T): Q[h = c][32g + 4ks + j],
-    // split into f16 hi + lo; built after the first steps' loads were issued,
-    // so the two latencies overlap.  Every wave uses the same fragments: the
-    // workgroup loads the query once, coalesced (two float4 per thread), and
-    // stores each float4 as the half4 of the lane and ks that take it (in lane
-    // order, so the per-step reads are conflict free).
+    // ---- query fragments (B operand of S^T = K Q^T on 16x16x32 MFMA): lane
+    // (c, g) takes Q[h = c][32g + 8ks .. +7] for slice ks, split into f16 hi +
+    // lo.  The workgroup loads the query once, coalesced (two float4 per
+    // thread), and stores each half4 in the lane slot q_slot(ks, lane) that
+    // reads it; the slot permutation makes both the stores and the per-step
+    // 16-byte reads bank-conflict free.
     {
         float4 qv[2];
 #pragma unroll
@@ -576,8 +665,9 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
                                                       4 * (t + AT_THREADS * k));
 #pragma unroll
         for (int k = 0; k < 2; ++k) {
-            const int e = 4 * (t + AT_THREADS * k);          // h * 128 + d, d % 4 == 0
-            const int h = e >> 7, d = e & (D - 1);
+            const int f = t + AT_THREADS * k;                // float4 index: h * 32 + d / 4
+            const int h = f >> 5, d = 4 * (f & 31);
+            const int gq = d >> 5, ks = (d >> 3) & 3, half = (d >> 2) & 1;
             const float x[4] = {qv[k].x, qv[k].y, qv[k].z, qv[k].w};
             half4_t hi4, lo4;
 #pragma unroll
@@ -586,11 +676,14 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
                 hi4[i] = hi;
                 lo4[i] = (_Float16)(x[i] - (float)hi);
             }
-            const int fl = 16 * (d >> 5) + h, ks = (d >> 2) & 7;
-            sh.st.q[0][ks][fl] = hi4;
-            sh.st.q[1][ks][fl] = lo4;
+            const int sl = q_slot(ks, 16 * gq + h);
+            reinterpret_cast<half4_t*>(&sh.st.q[0][ks][sl])[half] = hi4;
+            reinterpret_cast<half4_t*>(&sh.st.q[1][ks][sl])[half] = lo4;
         }
     }
+    int qs[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) qs[ks] = q_slot(ks, lane);
     __syncthreads();
     // The window's per-tensor V scale multiplies the PV products of window
     // steps only.  A wave takes its main steps before its window steps, so O is
@@ -604,111 +697,137 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
             in_window = true;
             const float inv = 1.0f / a.wv_scale;
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) o[mt] *= inv;
+            for (int mt = 0; mt < 8; ++mt) o_acc[mt] *= inv;
         }
-        // ---- dequantise this step: K into A-operand fragments, V into LDS (V^T)
-        half4_t kf[8];
-        uint32_t vv[16];                      // f16x2: channels 8g+32k+2i, +1 in vv[4k+i]
-        if (is_main && a.kvg_out && ok_cur) {
-            // this lane's share of the record: K bytes 16g.., V dwords
-            // 64 + 4g + 16k, and (g = 0) the 16 scale bytes
-            uint8_t* dst = a.kvg_out + ((int64_t)b * a.topk + SUB * st + c) * RECORD;
-            *reinterpret_cast<uint4*>(dst + 16 * g) =
-                make_uint4(cur.r[0], cur.r[1], cur.r[2], cur.r[3]);
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                *reinterpret_cast<uint32_t*>(dst + 64 + 4 * g + 16 * k) = cur.r[4 + k];
-            if (g == 0)
-                *reinterpret_cast<uint4*>(dst + 128) =
-                    make_uint4(cur.r[8], cur.r[9], cur.r[10], cur.r[11]);
-        }
+        const bool ok_c = ok_cur & 1u;
+        const uint64_t vmask = __ballot(ok_c);        // bit e (e < 16): entry e valid
+        const bool all_valid = (vmask & 0xffffu) == 0xffffu;
+        // ---- dequantise this step: K into A-operand slices, V into f16 pairs
+        half8_t kf[4];
+        uint32_t vw[16];                      // (V[2j][16m + u], V[2j+1][16m + u]) in vw[u]
         if (is_main) {
-            // K scales of groups 2g, 2g+1 (adjacent bytes); V scales of groups
-            // 2k + g/2, k = 0..3 (bytes g/2, g/2 + 2, ... of the V scale block)
-            const half2_t ks2 =
-                fp8x2_h2<false>(((g >> 1) ? cur.r[9] : cur.r[8]) >> (16 * (g & 1)));
-            const uint32_t vsb = __builtin_amdgcn_perm(cur.r[11], cur.r[10], vsel);
-            const half2_t vs01 = fp8x2_h2<false>(vsb), vs23 = fp8x2_h2<true>(vsb);
-            const half2_t k0 = half2_t{ks2.x, ks2.x}, k1 = half2_t{ks2.y, ks2.y};
-            const half2_t vsc[4] = {half2_t{vs01.x, vs01.x}, half2_t{vs01.y, vs01.y},
-                                    half2_t{vs23.x, vs23.x}, half2_t{vs23.y, vs23.y}};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                uint32_t w4[4];
-                fp4x8_scaled(cur.r[i], i < 2 ? k0 : k1, w4);
-                kf[2 * i] = __builtin_bit_cast(half4_t, make_uint2(w4[0], w4[1]));
-                kf[2 * i + 1] = __builtin_bit_cast(half4_t, make_uint2(w4[2], w4[3]));
+            if (a.kvg_out) {
+                // this lane's share of the records: entry c's K bytes 16g.. and
+                // (g = 0) scale bytes; V group m of entries 2j and 2j+1
+                const int e = SUB * st + 2 * j;
+                uint8_t* da = a.kvg_out + ((int64_t)b * a.topk + e) * RECORD;
+                uint8_t* dc = da + o * RECORD;
+                if (ok_c) {
+                    *reinterpret_cast<uint4*>(dc + 16 * g) =
+                        make_uint4(cur.r[0], cur.r[1], cur.r[2], cur.r[3]);
+                    if (g == 0)
+                        *reinterpret_cast<uint4*>(dc + 128) =
+                            make_uint4(cur.r[4], cur.r[5], cur.r[6], cur.r[7]);
+                }
+                if (ok_cur & 2u)
+                    *reinterpret_cast<uint2*>(da + 64 + 8 * m) = make_uint2(cur.r[8], cur.r[9]);
+                if (ok_cur & 4u)
+                    *reinterpret_cast<uint2*>(da + RECORD + 64 + 8 * m) =
+                        make_uint2(cur.r[10], cur.r[11]);
             }
+            // K scales of groups 2g, 2g+1 (adjacent bytes of the K scale block)
+            const half2_t ks2 = fp8x2_h2<false>(((g >> 1) ? cur.r[5] : cur.r[4]) >> (16 * (g & 1)));
 #pragma unroll
-            for (int k = 0; k < 4; ++k) fp4x8_scaled(cur.r[4 + k], vsc[k], vv + 4 * k);
+            for (int ks = 0; ks < 4; ++ks) {
+                uint32_t w4[4];
+                fp4x8_scaled(cur.r[ks], ks < 2 ? half2_t{ks2.x, ks2.x} : half2_t{ks2.y, ks2.y}, w4);
+                kf[ks] = __builtin_bit_cast(half8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+            }
+            // V scales of group m of entries 2j, 2j+1: byte g of V scale dword o
+            // of each record; the partner lane c ^ 1 holds the other record
+            const uint32_t send = o ? cur.r[6] : cur.r[7];
+            const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, DPP_XOR1, 0xf, 0xf,
+                                                                    false);
+            const half2_t vs = fp8x2_h2<false>(__builtin_amdgcn_perm(o ? cur.r[7] : cur.r[6], recv,
+                                                                     vsel));
+            // interleave the two entries' nibbles so that one conversion gives
+            // a (2j, 2j+1) pair: byte k of x holds channel 2k of both, of y
+            // channel 2k + 1
+#pragma unroll
+            for (int u = 0; u < 2; ++u) {
+                const uint32_t A = cur.r[8 + u], Bv = cur.r[10 + u];
+                const uint32_t x = (A & 0x0f0f0f0fu) | ((Bv << 4) & 0xf0f0f0f0u);
+                const uint32_t y = ((A >> 4) & 0x0f0f0f0fu) | (Bv & 0xf0f0f0f0u);
+                vw[8 * u + 0] = __builtin_bit_cast(uint32_t, fp4x2_h2<0>(x) * vs);
+                vw[8 * u + 1] = __builtin_bit_cast(uint32_t, fp4x2_h2<0>(y) * vs);
+                vw[8 * u + 2] = __builtin_bit_cast(uint32_t, fp4x2_h2<1>(x) * vs);
+                vw[8 * u + 3] = __builtin_bit_cast(uint32_t, fp4x2_h2<1>(y) * vs);
+                vw[8 * u + 4] = __builtin_bit_cast(uint32_t, fp4x2_h2<2>(x) * vs);
+                vw[8 * u + 5] = __builtin_bit_cast(uint32_t, fp4x2_h2<2>(y) * vs);
+                vw[8 * u + 6] = __builtin_bit_cast(uint32_t, fp4x2_h2<3>(x) * vs);
+                vw[8 * u + 7] = __builtin_bit_cast(uint32_t, fp4x2_h2<3>(y) * vs);
+            }
         } else {
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                kf[i] = __builtin_bit_cast(
-                    half4_t, make_uint2(__builtin_bit_cast(uint32_t, fp8x2_h2<false>(cur.r[i])),
-                                        __builtin_bit_cast(uint32_t, fp8x2_h2<true>(cur.r[i]))));
+            for (int ks = 0; ks < 4; ++ks)
+                kf[ks] = __builtin_bit_cast(
+                    half8_t,
+                    make_uint4(__builtin_bit_cast(uint32_t, fp8x2_h2<false>(cur.r[2 * ks])),
+                               __builtin_bit_cast(uint32_t, fp8x2_h2<true>(cur.r[2 * ks])),
+                               __builtin_bit_cast(uint32_t, fp8x2_h2<false>(cur.r[2 * ks + 1])),
+                               __builtin_bit_cast(uint32_t, fp8x2_h2<true>(cur.r[2 * ks + 1]))));
+            // bytes of the two entries interleaved: (A0 B0 A1 B1), (A2 B2 A3 B3)
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                vv[4 * k] = __builtin_bit_cast(uint32_t, fp8x2_h2<false>(cur.r[8 + 2 * k]));
-                vv[4 * k + 1] = __builtin_bit_cast(uint32_t, fp8x2_h2<true>(cur.r[8 + 2 * k]));
-                vv[4 * k + 2] = __builtin_bit_cast(uint32_t, fp8x2_h2<false>(cur.r[9 + 2 * k]));
-                vv[4 * k + 3] = __builtin_bit_cast(uint32_t, fp8x2_h2<true>(cur.r[9 + 2 * k]));
+            for (int u = 0; u < 4; ++u) {
+                const uint32_t A = cur.r[8 + u], Bv = cur.r[12 + u];
+                const uint32_t p0 = __builtin_amdgcn_perm(Bv, A, 0x05010400u);
+                const uint32_t p1 = __builtin_amdgcn_perm(Bv, A, 0x07030602u);
+                vw[4 * u + 0] = __builtin_bit_cast(uint32_t, fp8x2_h2<false>(p0));
+                vw[4 * u + 1] = __builtin_bit_cast(uint32_t, fp8x2_h2<true>(p0));
+                vw[4 * u + 2] = __builtin_bit_cast(uint32_t, fp8x2_h2<false>(p1));
+                vw[4 * u + 3] = __builtin_bit_cast(uint32_t, fp8x2_h2<true>(p1));
             }
         }
-        if (!ok_cur) {
+        if (!all_valid) {
+            // absent entries contribute exact zeros whatever their bytes hold
+            if (!ok_c) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) kf[i] = half4_t{0, 0, 0, 0};
+                for (int ks = 0; ks < 4; ++ks) kf[ks] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+            }
+            const uint32_t keep = ((ok_cur & 2u) ? 0x0000ffffu : 0u) | ((ok_cur & 4u) ? 0xffff0000u : 0u);
 #pragma unroll
-            for (int i = 0; i < 16; ++i) vv[i] = 0u;
+            for (int u = 0; u < 16; ++u) vw[u] &= keep;
         }
-        const uint64_t vmask = __ballot(ok_cur);     // bit e (e < 16): entry e valid
-        {
-            // lanes c and c^1 swap halves so that each writes one dword of two
-            // entries: the even lane (V[c][d], V[c+1][d]) into row d, the odd
-            // lane (V[c-1][d+1], V[c][d+1]) into row d+1
 #pragma unroll
-            for (int k = 0; k < 4; ++k)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const uint32_t x = vv[4 * k + i];
-                    const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, DPP_XOR1, 0xf, 0xf,
-                                                                          false);
-                    const int d = 8 * g + 32 * k + 2 * i;
-                    *reinterpret_cast<uint32_t*>(vt + vt_w + d * VT_STRIDE) =
-                        __builtin_amdgcn_perm(y, x, pair_sel);
-                }
-        }
+        for (int u = 0; u < 16; ++u) vt_wr[VT_ROW * u] = vw[u];
         // the V^T tile is private to this wave and LDS executes a wave's
         // operations in order; this only keeps the compiler from moving the
         // tile's reads above its writes
         asm volatile("" ::: "memory");
-        // ---- step i+2's loads go out now and overlap the MFMA work below
+        // ---- step i+1's loads go out now and overlap the MFMA work below
         const int sn = st + AT_WAVES;
         if (sn < t_end) {
-            ok_nxt = fetch(sn, idx_next, nxt);
+            ok_cur = fetch(sn, idx_next, cur);
             idx_next = load_idx(sn + AT_WAVES);
         }
         __builtin_amdgcn_sched_barrier(0);
 
-        // ---- S^T = K Q^T: lane (c, g) gets S[head c][entry 4g + r]
-        float4_t sacc = {0.f, 0.f, 0.f, 0.f};
+        // ---- S^T = K Q^T: lane (c, g) gets S[head c][entry 4g + r]; the hi and
+        // lo halves of the query accumulate in two independent chains
+        float4_t shi = {0.f, 0.f, 0.f, 0.f}, slo = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-            sacc = __builtin_amdgcn_mfma_f32_16x16x16f16(kf[ks], sh.st.q[0][ks][lane], sacc, 0,
-                                                         0, 0);
-            sacc = __builtin_amdgcn_mfma_f32_16x16x16f16(kf[ks], sh.st.q[1][ks][lane], sacc, 0,
-                                                         0, 0);
+        for (int ks = 0; ks < 4; ++ks) {
+            shi = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[ks], sh.st.q[0][ks][qs[ks]], shi, 0, 0, 0);
+            slo = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[ks], sh.st.q[1][ks][qs[ks]], slo, 0, 0, 0);
         }
         // logits in log2 units (log2(e) folded into the scale): exp2 is one
         // v_exp_f32; m_run is kept in the same units
         const float lscale = a.sm_scale * LOG2E * (is_main ? 1.0f : a.wk_scale);
         float sv[4];
         float tmax = NEG_INF;
+        if (all_valid) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const bool ok = (vmask >> (4 * g + r)) & 1u;
-            sv[r] = ok ? sacc[r] * lscale : NEG_INF;
-            tmax = fmaxf(tmax, sv[r]);
+            for (int r = 0; r < 4; ++r) {
+                sv[r] = (shi[r] + slo[r]) * lscale;
+                tmax = fmaxf(tmax, sv[r]);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const bool ok = (vmask >> (4 * g + r)) & 1u;
+                sv[r] = ok ? (shi[r] + slo[r]) * lscale : NEG_INF;
+                tmax = fmaxf(tmax, sv[r]);
+            }
         }
         tmax = max_xor32(max_xor16(tmax));
         // The reference max moves only when a logit exceeds it by more than
@@ -716,16 +835,30 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
         // gives the same softmax; weights stay below 2^RESCALE_SLACK.
         const bool grew = tmax > m_run + RESCALE_SLACK;
         const float m_new = grew ? tmax : m_run;
-        const float alpha = m_run == NEG_INF ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
         half4_t phi, plo;
         float psum = 0.0f;
+        float alpha;
+        if (all_valid) {
+            // m_new is finite here; exp2(-inf) is 0 on the first step
+            alpha = __builtin_amdgcn_exp2f(m_run - m_new);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const float p = sv[r] == NEG_INF ? 0.0f : __builtin_amdgcn_exp2f(sv[r] - m_new);
-            psum += p;
-            const _Float16 h = (_Float16)p;
-            phi[r] = h;
-            plo[r] = (_Float16)(p - (float)h);
+            for (int r = 0; r < 4; ++r) {
+                const float p = __builtin_amdgcn_exp2f(sv[r] - m_new);
+                psum += p;
+                const _Float16 h = (_Float16)p;
+                phi[r] = h;
+                plo[r] = (_Float16)(p - (float)h);
+            }
+        } else {
+            alpha = m_run == NEG_INF ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float p = sv[r] == NEG_INF ? 0.0f : __builtin_amdgcn_exp2f(sv[r] - m_new);
+                psum += p;
+                const _Float16 h = (_Float16)p;
+                phi[r] = h;
+                plo[r] = (_Float16)(p - (float)h);
+            }
         }
         l_run = l_run * alpha + psum;
         m_run = m_new;
@@ -733,23 +866,20 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
         // running max did not move, so the rescale is skipped when none moved
         if (__ballot(grew)) {
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) o[mt] *= alpha;
+            for (int mt = 0; mt < 8; ++mt) o_acc[mt] *= alpha;
         }
 #pragma unroll
         for (int mt = 0; mt < 8; ++mt) {
-            const half4_t vf =
-                *reinterpret_cast<const half4_t*>(&vt[(16 * mt + c) * VT_STRIDE + 4 * g]);
-            o[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, phi, o[mt], 0, 0, 0);
-            o[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, plo, o[mt], 0, 0, 0);
+            const half4_t vf = *reinterpret_cast<const half4_t*>(vt_rd + vt_block(mt));
+            o_acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, phi, o_acc[mt], 0, 0, 0);
+            o_acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, plo, o_acc[mt], 0, 0, 0);
         }
-        cur = nxt;
-        ok_cur = ok_nxt;
         asm volatile("" ::: "memory");     // next step's tile writes after these reads
     }
 
     if (in_window) {
 #pragma unroll
-        for (int mt = 0; mt < 8; ++mt) o[mt] *= a.wv_scale;
+        for (int mt = 0; mt < 8; ++mt) o_acc[mt] *= a.wv_scale;
     }
 
     // ---- combine the 4 waves: l over the 4 lanes of a head, then LDS
@@ -761,7 +891,7 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
     }
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
-        *reinterpret_cast<float4_t*>(&sh.mg.o[wave][c * OROW + 16 * mt + 4 * g]) = o[mt];
+        *reinterpret_cast<float4_t*>(&sh.mg.o[wave][c * OROW + 16 * mt + 4 * g]) = o_acc[mt];
     __syncthreads();
     {
         const int h = t >> 4, d0 = (t & 15) * 8;
@@ -945,11 +1075,16 @@ hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
     a.n_sub_main = (topk + SUB - 1) / SUB;
     a.n_sub = a.n_sub_main + WINDOW / SUB;
     a.n_split = p.n_split;
+    // 32-bit record offsets while one sequence's records span at most 4 GiB
+    const bool off32 = (uint64_t)c.cap * RECORD <= 0xffffffffull;
     if (c.page_table)
-        hipLaunchKernelGGL(attn_stream_kernel<true>, dim3(a.n_split, B), dim3(AT_THREADS), 0,
+        hipLaunchKernelGGL(attn_stream_kernel<AM_PAGED>, dim3(a.n_split, B), dim3(AT_THREADS), 0,
+                           stream, a);
+    else if (off32)
+        hipLaunchKernelGGL(attn_stream_kernel<AM_OFF32>, dim3(a.n_split, B), dim3(AT_THREADS), 0,
                            stream, a);
     else
-        hipLaunchKernelGGL(attn_stream_kernel<false>, dim3(a.n_split, B), dim3(AT_THREADS), 0,
+        hipLaunchKernelGGL(attn_stream_kernel<AM_FLAT64>, dim3(a.n_split, B), dim3(AT_THREADS), 0,
                            stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_split == 1) return e;
