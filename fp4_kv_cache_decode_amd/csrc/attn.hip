@@ -66,8 +66,6 @@ constexpr int AT_THREADS = 256;
 constexpr int AT_WAVES = AT_THREADS / 64;
 constexpr int SUB = 16;                   // entries per wave step
 constexpr int32_t STREAM_WG_TARGET = 1024;  // stream workgroups to aim for per launch
-constexpr int VT_STRIDE = 24;             // f16 per transposed V row (16 entries + 8 pad):
-                                          // conflict-free packed writes and operand reads
 constexpr float NEG_INF = -__builtin_huge_valf();
 // floats per head row of the waves' O in LDS when they are combined: the 16
 // lanes that write one 16-byte piece of 16 heads' rows at once land on 16
@@ -132,7 +130,7 @@ __host__ __device__ constexpr int q_slot(int ks, int L) {
     return L ^ (ks | (((L >> 4) & 1) << 2));
 }
 
-struct StreamShared {
+struct AttnShared {
     union {
         struct {
             uint32_t vt[AT_WAVES][VT_DWORDS];      // per-wave V^T of one step
@@ -180,15 +178,15 @@ constexpr float LN2 = 0.6931471805599453f;
 // ---------------------------------------------------------------------------
 // Tile kernel (small batches, latency): one workgroup per (query, 64-entry
 // tile), each of its 4 waves owning 16 entries.  The work of a wave is one
-// step of the stream kernel's loop (below): lane (c, g) gathers its entry's K
-// channels 32g..32g+31 and V channels {8g + 32k + i}, S^T = K Q^T comes out of
-// MFMA with K straight from the gathering lane's registers (here as
-// v_mfma_f32_16x16x32_f16, four K = 32 slices of the contraction), the
-// softmax weights stay where S^T left them as the B operand of O^T = V^T P^T,
-// and only V is transposed, through the wave's own LDS tile.  The 4 waves'
-// (m, l, O) are combined in LDS and the tile writes one partial record.
-// The index load is issued first and the query's loads right after it, so
-// the query's conversion overlaps the record loads.
+// step of the stream kernel's loop (below), with the same lane roles: lane
+// (c, g) gathers K channels 32g..32g+31 of entry c and V channel group
+// 4(c mod 2) + g of the entry pair containing c; S^T = K Q^T comes out of
+// v_mfma_f32_16x16x32_f16 with K straight from the gathering lane's
+// registers, the softmax weights stay where S^T left them as the B operand of
+// O^T = V^T P^T, and only V is transposed, through the wave's own LDS tile.
+// The 4 waves' (m, l, O) are combined in LDS and the tile writes one partial
+// record.  The index load is issued first and the query's loads right after
+// it, so the query's staging overlaps the record loads.
 
 struct TileArgs {
     const uint8_t* kv;
@@ -214,185 +212,256 @@ struct TileArgs {
     float sm_scale;
 };
 
-struct TileShared {
-    union {
-        struct {
-            _Float16 vt[AT_WAVES][D * VT_STRIDE];  // per-wave V^T of its 16 entries
-            half8_t q[2][4][64];                   // query slices (hi, lo) per lane
-        } st;
-        struct {
-            float o[AT_WAVES][HEADS * OROW];
-            float m[AT_WAVES][HEADS];
-            float l[AT_WAVES][HEADS];
-        } mg;                                      // the waves' softmax states
-    };
-};
+// Address modes of the main records: 32-bit offsets from the sequence's base
+// (every contiguous cache whose sequences span at most 4 GiB), 64-bit offsets,
+// or a page table.
+enum { AM_OFF32 = 0, AM_FLAT64 = 1, AM_PAGED = 2 };
 
-template <bool PAGED>
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+// Buffer resource word 3 on gfx9-family targets (32-bit data format, no
+// swizzle); loads past num_records return zeros.
+constexpr int BUF_DWORD3 = 0x00020000;
+
+// The query's f16 hi + lo slices in LDS (B operand of S^T = K Q^T on
+// 16x16x32 MFMA): lane (c, g) takes Q[h = c][32g + 8ks .. +7] for slice ks.
+// The workgroup loads the query once, coalesced (two float4 per thread), and
+// stores each half4 in the lane slot q_slot(ks, lane) that reads it.
+__device__ __forceinline__ void stage_query(AttnShared& sh, const float* q, int t) {
+    float4 qv[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+        qv[k] = *reinterpret_cast<const float4*>(q + 4 * (t + AT_THREADS * k));
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        const int f = t + AT_THREADS * k;                    // float4 index: h * 32 + d / 4
+        const int h = f >> 5, d = 4 * (f & 31);
+        const int gq = d >> 5, ks = (d >> 3) & 3, half = (d >> 2) & 1;
+        const float x[4] = {qv[k].x, qv[k].y, qv[k].z, qv[k].w};
+        half4_t hi4, lo4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const _Float16 hi = (_Float16)x[i];
+            hi4[i] = hi;
+            lo4[i] = (_Float16)(x[i] - (float)hi);
+        }
+        const int sl = q_slot(ks, 16 * gq + h);
+        reinterpret_cast<half4_t*>(&sh.st.q[0][ks][sl])[half] = hi4;
+        reinterpret_cast<half4_t*>(&sh.st.q[1][ks][sl])[half] = lo4;
+    }
+}
+
+// Dequantisation of one 16-entry step held by the lane (c, g):
+//  main:   r[0..3] K codes of entry c, channels 32g..32g+31; r[4..7] that
+//          record's 16 scale bytes; r[8..9] and r[10..11] V codes of channel
+//          group m of entries 2j and 2j+1
+//  window: r[0..7] K bytes of entry c, channels 32g..32g+31; r[8..11] and
+//          r[12..15] V bytes of channels 16m..16m+15 of entries 2j and 2j+1
+// K becomes the four A-operand slices of S^T = K Q^T, V the 16 f16 pairs
+// (V[2j][16m + u], V[2j+1][16m + u]) of the transposed V tile.
+__device__ __forceinline__ void dequant_main(const uint32_t* r, int g, int o, uint32_t vsel,
+                                             half8_t* kf, uint32_t* vw) {
+    // K scales of groups 2g, 2g+1 (adjacent bytes of the K scale block)
+    const half2_t ks2 = fp8x2_h2<false>(((g >> 1) ? r[5] : r[4]) >> (16 * (g & 1)));
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        uint32_t w4[4];
+        fp4x8_scaled(r[ks], ks < 2 ? half2_t{ks2.x, ks2.x} : half2_t{ks2.y, ks2.y}, w4);
+        kf[ks] = __builtin_bit_cast(half8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
+    }
+    // V scales of group m of entries 2j, 2j+1: byte g of V scale dword o of
+    // each record; the partner lane c ^ 1 holds the other record
+    const uint32_t send = o ? r[6] : r[7];
+    const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, DPP_XOR1, 0xf, 0xf, false);
+    const half2_t vs = fp8x2_h2<false>(__builtin_amdgcn_perm(o ? r[7] : r[6], recv, vsel));
+    // interleave the two entries' nibbles so that one conversion gives a
+    // (2j, 2j+1) pair: byte k of x holds channel 2k of both, of y channel 2k+1
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const uint32_t A = r[8 + u], Bv = r[10 + u];
+        const uint32_t x = (A & 0x0f0f0f0fu) | ((Bv << 4) & 0xf0f0f0f0u);
+        const uint32_t y = ((A >> 4) & 0x0f0f0f0fu) | (Bv & 0xf0f0f0f0u);
+        vw[8 * u + 0] = __builtin_bit_cast(uint32_t, fp4x2_h2<0>(x) * vs);
+        vw[8 * u + 1] = __builtin_bit_cast(uint32_t, fp4x2_h2<0>(y) * vs);
+        vw[8 * u + 2] = __builtin_bit_cast(uint32_t, fp4x2_h2<1>(x) * vs);
+        vw[8 * u + 3] = __builtin_bit_cast(uint32_t, fp4x2_h2<1>(y) * vs);
+        vw[8 * u + 4] = __builtin_bit_cast(uint32_t, fp4x2_h2<2>(x) * vs);
+        vw[8 * u + 5] = __builtin_bit_cast(uint32_t, fp4x2_h2<2>(y) * vs);
+        vw[8 * u + 6] = __builtin_bit_cast(uint32_t, fp4x2_h2<3>(x) * vs);
+        vw[8 * u + 7] = __builtin_bit_cast(uint32_t, fp4x2_h2<3>(y) * vs);
+    }
+}
+__device__ __forceinline__ void dequant_window(const uint32_t* r, half8_t* kf, uint32_t* vw) {
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+        kf[ks] = __builtin_bit_cast(
+            half8_t, make_uint4(__builtin_bit_cast(uint32_t, fp8x2_h2<false>(r[2 * ks])),
+                                __builtin_bit_cast(uint32_t, fp8x2_h2<true>(r[2 * ks])),
+                                __builtin_bit_cast(uint32_t, fp8x2_h2<false>(r[2 * ks + 1])),
+                                __builtin_bit_cast(uint32_t, fp8x2_h2<true>(r[2 * ks + 1]))));
+    // bytes of the two entries interleaved: (A0 B0 A1 B1), (A2 B2 A3 B3)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const uint32_t A = r[8 + u], Bv = r[12 + u];
+        const uint32_t p0 = __builtin_amdgcn_perm(Bv, A, 0x05010400u);
+        const uint32_t p1 = __builtin_amdgcn_perm(Bv, A, 0x07030602u);
+        vw[4 * u + 0] = __builtin_bit_cast(uint32_t, fp8x2_h2<false>(p0));
+        vw[4 * u + 1] = __builtin_bit_cast(uint32_t, fp8x2_h2<true>(p0));
+        vw[4 * u + 2] = __builtin_bit_cast(uint32_t, fp8x2_h2<false>(p1));
+        vw[4 * u + 3] = __builtin_bit_cast(uint32_t, fp8x2_h2<true>(p1));
+    }
+}
+
+// v_perm selector putting the V scale bytes of entries 2j, 2j+1 (byte g of the
+// lane's own dword and of the one received from lane c ^ 1) in order
+__device__ __forceinline__ uint32_t vscale_sel(int o, int g) {
+    return o ? ((uint32_t)g | ((4u + g) << 8) | 0x0c0c0000u)
+             : ((4u + g) | ((uint32_t)g << 8) | 0x0c0c0000u);
+}
+
+template <int AM>
 __global__ void __launch_bounds__(AT_THREADS) attn_tile_kernel(TileArgs a) {
-    __shared__ TileShared sh;
+    __shared__ AttnShared sh;
     const int tile = blockIdx.x;
     const int b = blockIdx.y;
     const int t = threadIdx.x;
     const int lane = t & 63;
     const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
     const int c = lane & 15, g = lane >> 4;
+    const int jp = c >> 1, o = c & 1, m = 4 * o + g;    // V: entries 2jp, 2jp+1, group m
     const bool is_main = tile < a.n_main;
-    // this lane's entry: index j of the list (main) or offset `off` in the window
-    const int j = tile * TILE + 16 * wave + c;
-    const int off = (tile - a.n_main) * TILE + 16 * wave + c;   // window tiles: < 128 <= w_cap
+    // the wave's 16 entries: list indices e0.. (main) or window offsets off0..
+    const int e0 = tile * TILE + 16 * wave;
+    const int off0 = (tile - a.n_main) * TILE + 16 * wave;   // window tiles: < 128 <= w_cap
 
     // ---- loads in order of need: the index (and the query's sequence and
     // length), the query, then the records
     int32_t pos = -1;
-    if (is_main && j < a.topk) pos = a.idx[(int64_t)b * a.topk + j];
+    if (is_main && e0 + c < a.topk) pos = a.idx[(int64_t)b * a.topk + e0 + c];
     const int32_t s = a.seq[b];
     const int64_t N = clamp64(a.ctx[b], 0, a.cap);
     const bool seq_ok = s >= 0 && s < a.n_seq;
-    // the query, once per workgroup and coalesced: two float4 per thread
-    float4 qv[2];
-#pragma unroll
-    for (int k = 0; k < 2; ++k)
-        qv[k] = *reinterpret_cast<const float4*>(a.q + (int64_t)b * HEADS * D +
-                                                  4 * (t + AT_THREADS * k));
+    const uint32_t n_ok = seq_ok ? (uint32_t)(N < INT32_MAX ? N : INT32_MAX) : 0u;
 
     // ---- per kind of tile: the record (or window row) loads, the query's
-    // conversion while they are in flight, then the dequantisation.  Each
-    // branch consumes everything it loads, so no load is pending where the
-    // branches join (a pending load there would make the compiler wait for all
-    // of them before the first record load).
-    half8_t kf[4];                        // K: A-operand slices of S^T = K Q^T
-    uint32_t vv[16];                      // V f16x2: channels 8g+32k+2i, +1 in vv[4k+i]
-    // q as f16 hi + lo in the B-operand slices of S^T = K Q^T: slice sl of
-    // lane (c, g) takes channels 32g + 8 sl .. +7 of head c; each float4 goes
-    // to the lane, slice and half that take it (read back after a barrier)
-    auto convert_q = [&]() {
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int e = 4 * (t + AT_THREADS * k);          // h * 128 + d, d % 4 == 0
-            const int h = e >> 7, d = e & (D - 1);
-            const float x[4] = {qv[k].x, qv[k].y, qv[k].z, qv[k].w};
-            half4_t hi4, lo4;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const _Float16 hi = (_Float16)x[i];
-                hi4[i] = hi;
-                lo4[i] = (_Float16)(x[i] - (float)hi);
-            }
-            const int fl = 16 * (d >> 5) + h, sl = (d >> 3) & 3;
-            _Float16* qh = reinterpret_cast<_Float16*>(&sh.st.q[0][sl][fl]) + (d & 4);
-            _Float16* ql = reinterpret_cast<_Float16*>(&sh.st.q[1][sl][fl]) + (d & 4);
-            *reinterpret_cast<half4_t*>(qh) = hi4;
-            *reinterpret_cast<half4_t*>(ql) = lo4;
-        }
-    };
-    bool ok;
+    // staging while they are in flight, then the dequantisation.  Each branch
+    // consumes everything it loads, so no load is pending where the branches
+    // join (a pending load there would make the compiler wait for all of them
+    // before the first record load).
+    half8_t kf[4];
+    uint32_t vw[16];
+    uint32_t okb3;                          // validity of entries c, 2jp, 2jp+1 (bits 0..2)
     if (is_main) {
-        // r[0..3] K codes of channels 32g.., r[4..7] V codes of channels
-        // 8g+32k..+7, r[8..11] the record's 16 scale bytes
-        ok = seq_ok && pos >= 0 && pos < N;
-        const uint8_t* rec =
-            a.kvg_in ? a.kvg_in + ((int64_t)b * a.topk + (j < a.topk ? j : 0)) * RECORD
-                     : a.kv + (ok ? cache_row<PAGED>(a.pm, a.cap, s, pos) * RECORD : 0);
+        const int32_t pos_p = __builtin_amdgcn_mov_dpp(pos, DPP_XOR1, 0xf, 0xf, false);
+        const int32_t pa = o ? pos_p : pos, pb = o ? pos : pos_p;
+        const bool oka = (uint32_t)pa < n_ok, okb = (uint32_t)pb < n_ok;
+        const int ea = e0 + 2 * jp;
         uint32_t r[12];
-        const uint4 kc = *reinterpret_cast<const uint4*>(rec + 16 * g);
-        const uint4 sc = *reinterpret_cast<const uint4*>(rec + 128);
-        r[0] = kc.x; r[1] = kc.y; r[2] = kc.z; r[3] = kc.w;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-            r[4 + k] = *reinterpret_cast<const uint32_t*>(rec + 64 + 4 * g + 16 * k);
-        r[8] = sc.x; r[9] = sc.y; r[10] = sc.z; r[11] = sc.w;
-        convert_q();
-        if (a.kvg_out && ok) {
-            // this lane's share of the record: K bytes 16g.., V dwords 64 + 4g +
-            // 16k, and (g = 0) the 16 scale bytes
-            uint8_t* dst = a.kvg_out + ((int64_t)b * a.topk + j) * RECORD;
-            *reinterpret_cast<uint4*>(dst + 16 * g) = make_uint4(r[0], r[1], r[2], r[3]);
-#pragma unroll
-            for (int k = 0; k < 4; ++k)
-                *reinterpret_cast<uint32_t*>(dst + 64 + 4 * g + 16 * k) = r[4 + k];
-            if (g == 0)
-                *reinterpret_cast<uint4*>(dst + 128) = make_uint4(r[8], r[9], r[10], r[11]);
+        u32x4 kc, sc;
+        u32x2 va, vb;
+        const bool main_buf = a.kvg_in != nullptr || AM == AM_OFF32;
+        if (main_buf) {
+            const uint8_t* base = a.kvg_in ? a.kvg_in + (int64_t)b * a.topk * RECORD
+                                           : a.kv + (seq_ok ? (int64_t)s * a.cap * RECORD : 0);
+            const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+                (void*)base, 0,
+                (int)(a.kvg_in ? (uint32_t)a.topk * (uint32_t)RECORD
+                               : (uint32_t)(AM == AM_OFF32 ? a.cap * RECORD : 0)),
+                BUF_DWORD3);
+            const uint32_t oa = a.kvg_in ? (uint32_t)(ea < a.topk ? ea : 0) * RECORD
+                                         : (oka ? (uint32_t)pa * RECORD : 0u);
+            const uint32_t ob = a.kvg_in ? (uint32_t)(ea + 1 < a.topk ? ea + 1 : 0) * RECORD
+                                         : (okb ? (uint32_t)pb * RECORD : 0u);
+            const uint32_t oc = o ? ob : oa;
+            kc = __builtin_amdgcn_raw_buffer_load_b128(rs, oc + 16 * g, 0, 0);
+            sc = __builtin_amdgcn_raw_buffer_load_b128(rs, oc + 128, 0, 0);
+            va = __builtin_amdgcn_raw_buffer_load_b64(rs, oa + 8 * m + 64, 0, 0);
+            vb = __builtin_amdgcn_raw_buffer_load_b64(rs, ob + 8 * m + 64, 0, 0);
+        } else {
+            auto rec = [&](int32_t p, bool ok) -> const uint8_t* {
+                if constexpr (AM == AM_PAGED)
+                    return a.kv + (ok ? cache_row<true>(a.pm, a.cap, s, p) * RECORD : 0);
+                else
+                    return a.kv + (ok ? ((int64_t)s * a.cap + p) * RECORD : 0);
+            };
+            const uint8_t* ra = rec(pa, oka);
+            const uint8_t* rb = rec(pb, okb);
+            const uint8_t* rc = o ? rb : ra;
+            kc = *reinterpret_cast<const u32x4*>(rc + 16 * g);
+            sc = *reinterpret_cast<const u32x4*>(rc + 128);
+            va = *reinterpret_cast<const u32x2*>(ra + 64 + 8 * m);
+            vb = *reinterpret_cast<const u32x2*>(rb + 64 + 8 * m);
         }
-        // K scales of groups 2g, 2g+1 (adjacent bytes); V scales of groups
-        // 2k + g/2, k = 0..3 (bytes g/2, g/2 + 2, ... of the V scale block)
-        const half2_t ks2 = fp8x2_h2<false>(((g >> 1) ? r[9] : r[8]) >> (16 * (g & 1)));
-        const uint32_t gh = (uint32_t)(g >> 1);
-        const uint32_t vsel = gh | ((2u + gh) << 8) | ((4u + gh) << 16) | ((6u + gh) << 24);
-        const uint32_t vsb = __builtin_amdgcn_perm(r[11], r[10], vsel);
-        const half2_t vs01 = fp8x2_h2<false>(vsb), vs23 = fp8x2_h2<true>(vsb);
-        const half2_t k0 = half2_t{ks2.x, ks2.x}, k1 = half2_t{ks2.y, ks2.y};
-        const half2_t vsc[4] = {half2_t{vs01.x, vs01.x}, half2_t{vs01.y, vs01.y},
-                                half2_t{vs23.x, vs23.x}, half2_t{vs23.y, vs23.y}};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            uint32_t w4[4];
-            fp4x8_scaled(r[i], i < 2 ? k0 : k1, w4);
-            kf[i] = __builtin_bit_cast(half8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) fp4x8_scaled(r[4 + k], vsc[k], vv + 4 * k);
-    } else {
-        // r[0..7] K bytes of channels 32g.., r[8..15] V bytes of channels 8g+32k..+7
-        const int64_t u0 = N > WINDOW ? N - WINDOW : 0;
-        ok = seq_ok && u0 + off < N;
-        // (u0 + off) mod w_cap from the uniform u0 mod w_cap: one subtract
-        int32_t w = (int32_t)(u0 % a.w_cap) + off;
-        w = w >= a.w_cap ? w - a.w_cap : w;
-        const int64_t row = ok ? (((int64_t)a.layer * a.n_seq + s) * a.w_cap + w) * D : 0;
-        uint32_t r[16];
-        const uint4 k0 = *reinterpret_cast<const uint4*>(a.wk + row + 32 * g);
-        const uint4 k1 = *reinterpret_cast<const uint4*>(a.wk + row + 32 * g + 16);
-        r[0] = k0.x; r[1] = k0.y; r[2] = k0.z; r[3] = k0.w;
-        r[4] = k1.x; r[5] = k1.y; r[6] = k1.z; r[7] = k1.w;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const uint2 v = *reinterpret_cast<const uint2*>(a.wv + row + 8 * g + 32 * k);
-            r[8 + 2 * k] = v.x;
-            r[9 + 2 * k] = v.y;
-        }
-        convert_q();
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t a0 = __builtin_bit_cast(uint32_t, fp8x2_h2<false>(r[2 * i]));
-            const uint32_t a1 = __builtin_bit_cast(uint32_t, fp8x2_h2<true>(r[2 * i]));
-            const uint32_t a2 = __builtin_bit_cast(uint32_t, fp8x2_h2<false>(r[2 * i + 1]));
-            const uint32_t a3 = __builtin_bit_cast(uint32_t, fp8x2_h2<true>(r[2 * i + 1]));
-            kf[i] = __builtin_bit_cast(half8_t, make_uint4(a0, a1, a2, a3));
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            vv[4 * k] = __builtin_bit_cast(uint32_t, fp8x2_h2<false>(r[8 + 2 * k]));
-            vv[4 * k + 1] = __builtin_bit_cast(uint32_t, fp8x2_h2<true>(r[8 + 2 * k]));
-            vv[4 * k + 2] = __builtin_bit_cast(uint32_t, fp8x2_h2<false>(r[9 + 2 * k]));
-            vv[4 * k + 3] = __builtin_bit_cast(uint32_t, fp8x2_h2<true>(r[9 + 2 * k]));
-        }
-    }
-    if (!ok) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) kf[i] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < 16; ++i) vv[i] = 0u;
-    }
-    const uint64_t vmask = __ballot(ok);        // bit e (e < 16): entry e of the wave valid
-
-    // ---- V^T into the wave's LDS tile: lanes c and c^1 swap halves so that
-    // each writes one dword of two entries (row stride VT_STRIDE: conflict free)
-    _Float16* vt = sh.st.vt[wave];
-    {
-        const uint32_t pair_sel = (c & 1) ? 0x03020706u : 0x05040100u;
-        const int vt_w = (c & 1) ? VT_STRIDE + (c - 1) : c;
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const uint32_t x = vv[4 * k + i];
-                const uint32_t y = (uint32_t)__builtin_amdgcn_mov_dpp((int)x, DPP_XOR1, 0xf, 0xf,
-                                                                      false);
-                const int d = 8 * g + 32 * k + 2 * i;
-                *reinterpret_cast<uint32_t*>(vt + vt_w + d * VT_STRIDE) =
-                    __builtin_amdgcn_perm(y, x, pair_sel);
+        stage_query(sh, a.q + (int64_t)b * HEADS * D, t);
+        r[0] = kc[0]; r[1] = kc[1]; r[2] = kc[2]; r[3] = kc[3];
+        r[4] = sc[0]; r[5] = sc[1]; r[6] = sc[2]; r[7] = sc[3];
+        r[8] = va[0]; r[9] = va[1]; r[10] = vb[0]; r[11] = vb[1];
+        const bool okc = o ? okb : oka;
+        okb3 = (uint32_t)okc | ((uint32_t)oka << 1) | ((uint32_t)okb << 2);
+        if (a.kvg_out) {
+            // this lane's share of the records: entry c's K bytes 16g.. and
+            // (g = 0) scale bytes; V group m of entries 2jp and 2jp+1
+            uint8_t* da = a.kvg_out + ((int64_t)b * a.topk + ea) * RECORD;
+            uint8_t* dc = da + o * RECORD;
+            if (okc) {
+                *reinterpret_cast<uint4*>(dc + 16 * g) = make_uint4(r[0], r[1], r[2], r[3]);
+                if (g == 0)
+                    *reinterpret_cast<uint4*>(dc + 128) = make_uint4(r[4], r[5], r[6], r[7]);
             }
+            if (oka) *reinterpret_cast<uint2*>(da + 64 + 8 * m) = make_uint2(r[8], r[9]);
+            if (okb) *reinterpret_cast<uint2*>(da + RECORD + 64 + 8 * m) = make_uint2(r[10], r[11]);
+        }
+        dequant_main(r, g, o, vscale_sel(o, g), kf, vw);
+    } else {
+        const int64_t u0 = N > WINDOW ? N - WINDOW : 0;
+        const int w_ok = seq_ok ? (int)(N - u0) : 0;
+        const bool oka = off0 + 2 * jp < w_ok, okb = off0 + 2 * jp + 1 < w_ok;
+        const int64_t win_base = ((int64_t)a.layer * a.n_seq + (seq_ok ? s : 0)) * a.w_cap;
+        const int32_t slot0 = (int32_t)(u0 % a.w_cap);
+        auto wrow = [&](int e) -> uint32_t {                 // (u0 + e) mod w_cap, times D
+            int32_t sl = slot0 + e;
+            sl = sl >= a.w_cap ? sl - a.w_cap : sl;
+            return (uint32_t)sl * (uint32_t)D;
+        };
+        const uint32_t ra = oka ? wrow(off0 + 2 * jp) : 0u, rb = okb ? wrow(off0 + 2 * jp + 1) : 0u;
+        const uint32_t rc = o ? rb : ra;
+        const __amdgpu_buffer_rsrc_t rk =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(a.wk + win_base * D), 0, a.w_cap * D, BUF_DWORD3);
+        const __amdgpu_buffer_rsrc_t rv =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(a.wv + win_base * D), 0, a.w_cap * D, BUF_DWORD3);
+        const u32x4 k0 = __builtin_amdgcn_raw_buffer_load_b128(rk, rc + 32 * g, 0, 0);
+        const u32x4 k1 = __builtin_amdgcn_raw_buffer_load_b128(rk, rc + 32 * g + 16, 0, 0);
+        const u32x4 va = __builtin_amdgcn_raw_buffer_load_b128(rv, ra + 16 * m, 0, 0);
+        const u32x4 vb = __builtin_amdgcn_raw_buffer_load_b128(rv, rb + 16 * m, 0, 0);
+        stage_query(sh, a.q + (int64_t)b * HEADS * D, t);
+        uint32_t r[16];
+        r[0] = k0[0]; r[1] = k0[1]; r[2] = k0[2]; r[3] = k0[3];
+        r[4] = k1[0]; r[5] = k1[1]; r[6] = k1[2]; r[7] = k1[3];
+        r[8] = va[0]; r[9] = va[1]; r[10] = va[2]; r[11] = va[3];
+        r[12] = vb[0]; r[13] = vb[1]; r[14] = vb[2]; r[15] = vb[3];
+        okb3 = (uint32_t)(o ? okb : oka) | ((uint32_t)oka << 1) | ((uint32_t)okb << 2);
+        dequant_window(r, kf, vw);
+    }
+    const bool ok_c = okb3 & 1u;
+    const uint64_t vmask = __ballot(ok_c);      // bit e (e < 16): entry e of the wave valid
+    const bool all_valid = (vmask & 0xffffu) == 0xffffu;
+    if (!all_valid) {
+        // absent entries contribute exact zeros whatever their bytes hold
+        if (!ok_c) {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) kf[ks] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
+        }
+        const uint32_t keep = ((okb3 & 2u) ? 0x0000ffffu : 0u) | ((okb3 & 4u) ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int u = 0; u < 16; ++u) vw[u] &= keep;
+    }
+
+    // ---- V^T into the wave's LDS tile: row 16m + u, dword jp
+    uint32_t* vt = sh.st.vt[wave];
+    {
+        uint32_t* const vt_wr = vt + vt_block(m) + jp;
+#pragma unroll
+        for (int u = 0; u < 16; ++u) vt_wr[VT_ROW * u] = vw[u];
     }
     // the tile is private to this wave and LDS executes a wave's operations in
     // order; this only keeps the compiler from moving its reads above the writes
@@ -406,30 +475,29 @@ __global__ void __launch_bounds__(AT_THREADS) attn_tile_kernel(TileArgs a) {
     {
         float4_t shi = {0.f, 0.f, 0.f, 0.f}, slo = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int sl = 0; sl < 4; ++sl) {
-            shi = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[sl], sh.st.q[0][sl][lane], shi, 0, 0,
-                                                         0);
-            slo = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[sl], sh.st.q[1][sl][lane], slo, 0, 0,
-                                                         0);
+        for (int ks = 0; ks < 4; ++ks) {
+            const int qs = q_slot(ks, lane);
+            shi = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[ks], sh.st.q[0][ks][qs], shi, 0, 0, 0);
+            slo = __builtin_amdgcn_mfma_f32_16x16x32_f16(kf[ks], sh.st.q[1][ks][qs], slo, 0, 0, 0);
         }
         sacc = shi + slo;
     }
     // logits in log2 units (log2(e) folded into the scale): exp2 is one v_exp_f32
     const float lscale = a.sm_scale * LOG2E * (is_main ? 1.0f : a.wk_scale);
     float sv[4];
-    float m = NEG_INF;
+    float mx = NEG_INF;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
         const bool v_ok = (vmask >> (4 * g + q4)) & 1u;
         sv[q4] = v_ok ? sacc[q4] * lscale : NEG_INF;
-        m = fmaxf(m, sv[q4]);
+        mx = fmaxf(mx, sv[q4]);
     }
-    m = max_xor32(max_xor16(m));                // the wave's max for head c
+    mx = max_xor32(max_xor16(mx));              // the wave's max for head c
     half4_t phi, plo;
     float lsum = 0.0f;
 #pragma unroll
     for (int q4 = 0; q4 < 4; ++q4) {
-        const float p = sv[q4] == NEG_INF ? 0.0f : __builtin_amdgcn_exp2f(sv[q4] - m);
+        const float p = sv[q4] == NEG_INF ? 0.0f : __builtin_amdgcn_exp2f(sv[q4] - mx);
         lsum += p;
         const _Float16 h = (_Float16)p;
         phi[q4] = h;
@@ -438,24 +506,25 @@ __global__ void __launch_bounds__(AT_THREADS) attn_tile_kernel(TileArgs a) {
     lsum = add_xor32(add_xor16(lsum));
 
     // ---- O^T = V^T P^T over the wave's 16 entries: O^T[d = 16 mt + 4g + r][h = c]
-    float4_t o[8];
+    float4_t o_acc[8];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) {
-        const half4_t vf = *reinterpret_cast<const half4_t*>(&vt[(16 * mt + c) * VT_STRIDE + 4 * g]);
+        const half4_t vf =
+            *reinterpret_cast<const half4_t*>(vt + vt_block(mt) + VT_ROW * c + 2 * g);
         float4_t acc = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, phi, float4_t{0.f, 0.f, 0.f, 0.f},
                                                              0, 0, 0);
-        o[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, plo, acc, 0, 0, 0);
+        o_acc[mt] = __builtin_amdgcn_mfma_f32_16x16x16f16(vf, plo, acc, 0, 0, 0);
     }
 
     // ---- combine the 4 waves in LDS and write the tile's partial record
     __syncthreads();                            // every wave is done with its V^T tile
     if (g == 0) {
-        sh.mg.m[wave][c] = m;
+        sh.mg.m[wave][c] = mx;
         sh.mg.l[wave][c] = lsum;
     }
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
-        *reinterpret_cast<float4_t*>(&sh.mg.o[wave][c * OROW + 16 * mt + 4 * g]) = o[mt];
+        *reinterpret_cast<float4_t*>(&sh.mg.o[wave][c * OROW + 16 * mt + 4 * g]) = o_acc[mt];
     __syncthreads();
     {
         const int h = t >> 4, d0 = (t & 15) * 8;
@@ -503,21 +572,12 @@ struct Raw {
     uint32_t r[16];
 };
 
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-// Buffer resource word 3 on gfx9-family targets (32-bit data format, no
-// swizzle); loads past num_records return zeros.
-constexpr int BUF_DWORD3 = 0x00020000;
 
-// Address modes of the main records: 32-bit offsets from the sequence's base
-// (every contiguous cache whose sequences span at most 4 GiB), 64-bit offsets,
-// or a page table.
-enum { AM_OFF32 = 0, AM_FLAT64 = 1, AM_PAGED = 2 };
 
 // 4 workgroups (16 waves) per CU: at most 128 VGPRs
 template <int AM>
 __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a) {
-    __shared__ StreamShared sh;
+    __shared__ AttnShared sh;
     const int split = blockIdx.x;
     const int b = blockIdx.y;
     const int t = threadIdx.x;
@@ -639,8 +699,7 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
     const uint32_t* const vt_rd = vt + VT_ROW * c + 2 * g;
     // v_perm selector putting the V scale bytes of entries 2j, 2j+1 (byte g of
     // the lane's own dword and of the one received from lane c ^ 1) in order
-    const uint32_t vsel = o ? ((uint32_t)g | ((4u + g) << 8) | 0x0c0c0000u)
-                            : ((4u + g) | ((uint32_t)g << 8) | 0x0c0c0000u);
+    const uint32_t vsel = vscale_sel(o, g);
     int st = t_begin + wave;
     // one step in flight: while step i is computed, step i+1's records are
     // arriving (their index list entries were loaded one step earlier)
@@ -651,36 +710,7 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
         ok_cur = fetch(st, load_idx(st), cur);
         idx_next = load_idx(st + AT_WAVES);
     }
-    // ---- query fragments (B operand of S^T = K Q^T on 16x16x32 MFMA): lane
-    // (c, g) takes Q[h = c][32g + 8ks .. +7] for slice ks, split into f16 hi +
-    // lo.  The workgroup loads the query once, coalesced (two float4 per
-    // thread), and stores each half4 in the lane slot q_slot(ks, lane) that
-    // reads it; the slot permutation makes both the stores and the per-step
-    // 16-byte reads bank-conflict free.
-    {
-        float4 qv[2];
-#pragma unroll
-        for (int k = 0; k < 2; ++k)
-            qv[k] = *reinterpret_cast<const float4*>(a.q + (int64_t)b * HEADS * D +
-                                                      4 * (t + AT_THREADS * k));
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const int f = t + AT_THREADS * k;                // float4 index: h * 32 + d / 4
-            const int h = f >> 5, d = 4 * (f & 31);
-            const int gq = d >> 5, ks = (d >> 3) & 3, half = (d >> 2) & 1;
-            const float x[4] = {qv[k].x, qv[k].y, qv[k].z, qv[k].w};
-            half4_t hi4, lo4;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const _Float16 hi = (_Float16)x[i];
-                hi4[i] = hi;
-                lo4[i] = (_Float16)(x[i] - (float)hi);
-            }
-            const int sl = q_slot(ks, 16 * gq + h);
-            reinterpret_cast<half4_t*>(&sh.st.q[0][ks][sl])[half] = hi4;
-            reinterpret_cast<half4_t*>(&sh.st.q[1][ks][sl])[half] = lo4;
-        }
-    }
+    stage_query(sh, a.q + (int64_t)b * HEADS * D, t);
     int qs[4];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) qs[ks] = q_slot(ks, lane);
@@ -725,58 +755,9 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
                     *reinterpret_cast<uint2*>(da + RECORD + 64 + 8 * m) =
                         make_uint2(cur.r[10], cur.r[11]);
             }
-            // K scales of groups 2g, 2g+1 (adjacent bytes of the K scale block)
-            const half2_t ks2 = fp8x2_h2<false>(((g >> 1) ? cur.r[5] : cur.r[4]) >> (16 * (g & 1)));
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks) {
-                uint32_t w4[4];
-                fp4x8_scaled(cur.r[ks], ks < 2 ? half2_t{ks2.x, ks2.x} : half2_t{ks2.y, ks2.y}, w4);
-                kf[ks] = __builtin_bit_cast(half8_t, make_uint4(w4[0], w4[1], w4[2], w4[3]));
-            }
-            // V scales of group m of entries 2j, 2j+1: byte g of V scale dword o
-            // of each record; the partner lane c ^ 1 holds the other record
-            const uint32_t send = o ? cur.r[6] : cur.r[7];
-            const uint32_t recv = (uint32_t)__builtin_amdgcn_mov_dpp((int)send, DPP_XOR1, 0xf, 0xf,
-                                                                    false);
-            const half2_t vs = fp8x2_h2<false>(__builtin_amdgcn_perm(o ? cur.r[7] : cur.r[6], recv,
-                                                                     vsel));
-            // interleave the two entries' nibbles so that one conversion gives
-            // a (2j, 2j+1) pair: byte k of x holds channel 2k of both, of y
-            // channel 2k + 1
-#pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                const uint32_t A = cur.r[8 + u], Bv = cur.r[10 + u];
-                const uint32_t x = (A & 0x0f0f0f0fu) | ((Bv << 4) & 0xf0f0f0f0u);
-                const uint32_t y = ((A >> 4) & 0x0f0f0f0fu) | (Bv & 0xf0f0f0f0u);
-                vw[8 * u + 0] = __builtin_bit_cast(uint32_t, fp4x2_h2<0>(x) * vs);
-                vw[8 * u + 1] = __builtin_bit_cast(uint32_t, fp4x2_h2<0>(y) * vs);
-                vw[8 * u + 2] = __builtin_bit_cast(uint32_t, fp4x2_h2<1>(x) * vs);
-                vw[8 * u + 3] = __builtin_bit_cast(uint32_t, fp4x2_h2<1>(y) * vs);
-                vw[8 * u + 4] = __builtin_bit_cast(uint32_t, fp4x2_h2<2>(x) * vs);
-                vw[8 * u + 5] = __builtin_bit_cast(uint32_t, fp4x2_h2<2>(y) * vs);
-                vw[8 * u + 6] = __builtin_bit_cast(uint32_t, fp4x2_h2<3>(x) * vs);
-                vw[8 * u + 7] = __builtin_bit_cast(uint32_t, fp4x2_h2<3>(y) * vs);
-            }
+            dequant_main(cur.r, g, o, vsel, kf, vw);
         } else {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                kf[ks] = __builtin_bit_cast(
-                    half8_t,
-                    make_uint4(__builtin_bit_cast(uint32_t, fp8x2_h2<false>(cur.r[2 * ks])),
-                               __builtin_bit_cast(uint32_t, fp8x2_h2<true>(cur.r[2 * ks])),
-                               __builtin_bit_cast(uint32_t, fp8x2_h2<false>(cur.r[2 * ks + 1])),
-                               __builtin_bit_cast(uint32_t, fp8x2_h2<true>(cur.r[2 * ks + 1]))));
-            // bytes of the two entries interleaved: (A0 B0 A1 B1), (A2 B2 A3 B3)
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const uint32_t A = cur.r[8 + u], Bv = cur.r[12 + u];
-                const uint32_t p0 = __builtin_amdgcn_perm(Bv, A, 0x05010400u);
-                const uint32_t p1 = __builtin_amdgcn_perm(Bv, A, 0x07030602u);
-                vw[4 * u + 0] = __builtin_bit_cast(uint32_t, fp8x2_h2<false>(p0));
-                vw[4 * u + 1] = __builtin_bit_cast(uint32_t, fp8x2_h2<true>(p0));
-                vw[4 * u + 2] = __builtin_bit_cast(uint32_t, fp8x2_h2<false>(p1));
-                vw[4 * u + 3] = __builtin_bit_cast(uint32_t, fp8x2_h2<true>(p1));
-            }
+            dequant_window(cur.r, kf, vw);
         }
         if (!all_valid) {
             // absent entries contribute exact zeros whatever their bytes hold
@@ -1015,6 +996,8 @@ hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
                        const uint8_t* kvg_in, uint8_t* kvg_out, float* out, float* partials,
                        int64_t max_parts, hipStream_t stream) {
     const AttnPlan p = attn_plan(B, topk, max_parts);
+    // 32-bit record offsets while one sequence's records span at most 4 GiB
+    const bool off32 = (uint64_t)c.cap * RECORD <= 0xffffffffull;
     if (p.tile) {
         // few queries: one workgroup per 64-entry tile, the shortest dependency chain
         TileArgs a{};
@@ -1040,11 +1023,14 @@ hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
         a.wv_scale = w.v_scale;
         a.sm_scale = sm_scale;
         if (c.page_table)
-            hipLaunchKernelGGL(attn_tile_kernel<true>, dim3(a.n_tiles, B), dim3(AT_THREADS), 0,
+            hipLaunchKernelGGL(attn_tile_kernel<AM_PAGED>, dim3(a.n_tiles, B), dim3(AT_THREADS), 0,
+                               stream, a);
+        else if (off32)
+            hipLaunchKernelGGL(attn_tile_kernel<AM_OFF32>, dim3(a.n_tiles, B), dim3(AT_THREADS), 0,
                                stream, a);
         else
-            hipLaunchKernelGGL(attn_tile_kernel<false>, dim3(a.n_tiles, B), dim3(AT_THREADS), 0,
-                               stream, a);
+            hipLaunchKernelGGL(attn_tile_kernel<AM_FLAT64>, dim3(a.n_tiles, B), dim3(AT_THREADS),
+                               0, stream, a);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(attn_merge_kernel, dim3(HEADS, B), dim3(D), 0, stream, partials,
@@ -1075,8 +1061,6 @@ hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
     a.n_sub_main = (topk + SUB - 1) / SUB;
     a.n_sub = a.n_sub_main + WINDOW / SUB;
     a.n_split = p.n_split;
-    // 32-bit record offsets while one sequence's records span at most 4 GiB
-    const bool off32 = (uint64_t)c.cap * RECORD <= 0xffffffffull;
     if (c.page_table)
         hipLaunchKernelGGL(attn_stream_kernel<AM_PAGED>, dim3(a.n_split, B), dim3(AT_THREADS), 0,
                            stream, a);
