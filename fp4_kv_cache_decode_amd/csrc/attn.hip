@@ -319,6 +319,12 @@ __device__ __forceinline__ uint32_t vscale_sel(int o, int g) {
              : ((4u + g) | ((uint32_t)g << 8) | 0x0c0c0000u);
 }
 
+// Window slot of position u0 (u0 mod w_cap); 32-bit division whenever u0 fits.
+__device__ __forceinline__ int32_t window_slot(int64_t u0, int32_t w_cap) {
+    return u0 <= (int64_t)0xffffffffll ? (int32_t)((uint32_t)u0 % (uint32_t)w_cap)
+                                       : (int32_t)(u0 % w_cap);
+}
+
 template <int AM>
 __global__ void __launch_bounds__(AT_THREADS) attn_tile_kernel(TileArgs a) {
     __shared__ AttnShared sh;
@@ -417,7 +423,7 @@ __global__ void __launch_bounds__(AT_THREADS) attn_tile_kernel(TileArgs a) {
         const int w_ok = seq_ok ? (int)(N - u0) : 0;
         const bool oka = off0 + 2 * jp < w_ok, okb = off0 + 2 * jp + 1 < w_ok;
         const int64_t win_base = ((int64_t)a.layer * a.n_seq + (seq_ok ? s : 0)) * a.w_cap;
-        const int32_t slot0 = (int32_t)(u0 % a.w_cap);
+        const int32_t slot0 = window_slot(u0, a.w_cap);
         auto wrow = [&](int e) -> uint32_t {                 // (u0 + e) mod w_cap, times D
             int32_t sl = slot0 + e;
             sl = sl >= a.w_cap ? sl - a.w_cap : sl;
@@ -589,13 +595,17 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
     const int64_t N = clamp64(a.ctx[b], 0, a.cap);
     const bool seq_ok = s >= 0 && s < a.n_seq;
     const int64_t u0 = N > WINDOW ? N - WINDOW : 0;
-    const int32_t slot0 = (int32_t)(u0 % a.w_cap);         // window slot of position u0
+    const int32_t slot0 = window_slot(u0, a.w_cap);         // window slot of position u0
     const int64_t win_base = ((int64_t)a.layer * a.n_seq + (seq_ok ? s : 0)) * a.w_cap;
     // this workgroup's steps [t_begin, t_end); wave w takes t_begin + w, + 4, ...
-    const int t_begin = (int)((int64_t)split * a.n_sub / a.n_split);
-    const int t_end = (int)((int64_t)(split + 1) * a.n_sub / a.n_split);
+    // (split x n_sub stays far below 2^32: n_sub <= 264, split < n_sub)
+    const int t_begin = (int)((uint32_t)(split * a.n_sub) / (uint32_t)a.n_split);
+    const int t_end = (int)((uint32_t)((split + 1) * a.n_sub) / (uint32_t)a.n_split);
     const int main_end = t_end < a.n_sub_main ? t_end : a.n_sub_main;
     const int32_t* idx_row = a.idx + (int64_t)b * a.topk;
+    // valid main positions are [0, n_ok) and valid window entries [0, w_ok)
+    const uint32_t n_ok = seq_ok ? (uint32_t)(N < INT32_MAX ? N : INT32_MAX) : 0u;
+    const int w_ok = seq_ok ? (int)(N - u0) : 0;
     // uniform bases: the sequence's first record, the query's gathered records
     // and its window rows
     const uint8_t* kv_s = a.kv + (AM != AM_PAGED && seq_ok ? (int64_t)s * a.cap * RECORD : 0);
@@ -625,32 +635,39 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
         return __builtin_amdgcn_raw_buffer_load_b32(rs_idx, 4 * (SUB * st + c), 0, 0);
     };
     // issue the loads of step st; raw is this lane's index list load (entry c).
-    // Returns the validity of entries c, 2j and 2j+1 in bits 0, 1, 2.
-    auto fetch = [&](int st, int32_t raw, Raw& w) -> uint32_t {
-        const int32_t pos = (st < main_end && SUB * st + c < a.topk) ? raw : -1;
-        const int32_t pos_p = __builtin_amdgcn_mov_dpp(pos, DPP_XOR1, 0xf, 0xf, false);
+    // Returns the validity of entry c and of its partner c ^ 1 (the pair 2j,
+    // 2j+1 is (c, partner) for even c, (partner, c) for odd c).
+    struct Valid {
+        bool c, p;
+    };
+    auto fetch = [&](int st, int32_t raw, Raw& w) -> Valid {
         if (st < a.n_sub_main) {
+            const int32_t pos = (st < main_end && SUB * st + c < a.topk) ? raw : -1;
+            const int32_t pos_p = __builtin_amdgcn_mov_dpp(pos, DPP_XOR1, 0xf, 0xf, false);
+            const bool okc = (uint32_t)pos < n_ok, okp = (uint32_t)pos_p < n_ok;
             const int32_t pa = o ? pos_p : pos, pb = o ? pos : pos_p;
-            const bool oka = seq_ok && pa >= 0 && pa < N, okb = seq_ok && pb >= 0 && pb < N;
             const int e = SUB * st + 2 * j;
             u32x4 kc, sc;
             u32x2 va, vb;
             if (main_buf) {
+                // an absent entry's offset reads zeros past the buffer, or a
+                // record in it that its validity discards
                 const uint32_t oa = kvg_b ? (uint32_t)(e < a.topk ? e : 0) * RECORD
-                                          : (oka ? (uint32_t)pa * RECORD : 0u);
+                                          : (uint32_t)pa * (uint32_t)RECORD;
                 const uint32_t ob = kvg_b ? (uint32_t)(e + 1 < a.topk ? e + 1 : 0) * RECORD
-                                          : (okb ? (uint32_t)pb * RECORD : 0u);
+                                          : (uint32_t)pb * (uint32_t)RECORD;
                 const uint32_t oc = o ? ob : oa;
                 kc = __builtin_amdgcn_raw_buffer_load_b128(rs_main, oc + 16 * g, 0, 0);
                 sc = __builtin_amdgcn_raw_buffer_load_b128(rs_main, oc + 128, 0, 0);
                 va = __builtin_amdgcn_raw_buffer_load_b64(rs_main, oa + 8 * m + 64, 0, 0);
                 vb = __builtin_amdgcn_raw_buffer_load_b64(rs_main, ob + 8 * m + 64, 0, 0);
             } else {
-                auto rec = [&](int32_t p, bool ok) -> const uint8_t* {
+                const bool oka = o ? okp : okc, okb = o ? okc : okp;
+                auto rec = [&](int32_t pp, bool ok) -> const uint8_t* {
                     if constexpr (AM == AM_PAGED)
-                        return a.kv + (ok ? cache_row<true>(a.pm, a.cap, s, p) * RECORD : 0);
+                        return a.kv + (ok ? cache_row<true>(a.pm, a.cap, s, pp) * RECORD : 0);
                     else
-                        return kv_s + (ok ? (int64_t)p * RECORD : 0);
+                        return kv_s + (ok ? (int64_t)pp * RECORD : 0);
                 };
                 const uint8_t* ra = rec(pa, oka);
                 const uint8_t* rb = rec(pb, okb);
@@ -664,16 +681,17 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
             w.r[4] = sc[0]; w.r[5] = sc[1]; w.r[6] = sc[2]; w.r[7] = sc[3];
             w.r[8] = va[0]; w.r[9] = va[1]; w.r[10] = vb[0]; w.r[11] = vb[1];
             w.r[12] = w.r[13] = w.r[14] = w.r[15] = 0u;     // unused by main steps
-            return (uint32_t)(o ? okb : oka) | ((uint32_t)oka << 1) | ((uint32_t)okb << 2);
+            return Valid{okc, okp};
         }
         const int off = (st - a.n_sub_main) * SUB;           // + entry < 128 <= w_cap
+        // (u0 + off + e) mod w_cap for every entry of the step (absent ones
+        // read a row in the window that their validity discards)
         auto wrow = [&](int e) -> uint32_t {
-            int32_t sl = slot0 + off + e;                     // (u0 + off + e) mod w_cap
+            int32_t sl = slot0 + off + e;
             sl = sl >= a.w_cap ? sl - a.w_cap : sl;
             return (uint32_t)sl * (uint32_t)D;
         };
-        const bool oka = seq_ok && u0 + off + 2 * j < N, okb = seq_ok && u0 + off + 2 * j + 1 < N;
-        const uint32_t ra = oka ? wrow(2 * j) : 0u, rb = okb ? wrow(2 * j + 1) : 0u;
+        const uint32_t ra = wrow(2 * j), rb = wrow(2 * j + 1);
         const uint32_t rc = o ? rb : ra;
         const u32x4 k0 = __builtin_amdgcn_raw_buffer_load_b128(rs_wk, rc + 32 * g, 0, 0);
         const u32x4 k1 = __builtin_amdgcn_raw_buffer_load_b128(rs_wk, rc + 32 * g + 16, 0, 0);
@@ -683,7 +701,7 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
         w.r[4] = k1[0]; w.r[5] = k1[1]; w.r[6] = k1[2]; w.r[7] = k1[3];
         w.r[8] = va[0]; w.r[9] = va[1]; w.r[10] = va[2]; w.r[11] = va[3];
         w.r[12] = vb[0]; w.r[13] = vb[1]; w.r[14] = vb[2]; w.r[15] = vb[3];
-        return (uint32_t)(o ? okb : oka) | ((uint32_t)oka << 1) | ((uint32_t)okb << 2);
+        return Valid{off + c < w_ok, off + (c ^ 1) < w_ok};
     };
 
     // softmax state of head c (lanes c, c+16, c+32, c+48 hold the same m; l is
@@ -704,7 +722,7 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
     // one step in flight: while step i is computed, step i+1's records are
     // arriving (their index list entries were loaded one step earlier)
     Raw cur;
-    uint32_t ok_cur = 0;
+    Valid ok_cur{false, false};
     int32_t idx_next = -1;
     if (st < t_end) {
         ok_cur = fetch(st, load_idx(st), cur);
@@ -729,7 +747,7 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
 #pragma unroll
             for (int mt = 0; mt < 8; ++mt) o_acc[mt] *= inv;
         }
-        const bool ok_c = ok_cur & 1u;
+        const bool ok_c = ok_cur.c;
         const uint64_t vmask = __ballot(ok_c);        // bit e (e < 16): entry e valid
         const bool all_valid = (vmask & 0xffffu) == 0xffffu;
         // ---- dequantise this step: K into A-operand slices, V into f16 pairs
@@ -749,9 +767,9 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
                         *reinterpret_cast<uint4*>(dc + 128) =
                             make_uint4(cur.r[4], cur.r[5], cur.r[6], cur.r[7]);
                 }
-                if (ok_cur & 2u)
+                if (o ? ok_cur.p : ok_cur.c)
                     *reinterpret_cast<uint2*>(da + 64 + 8 * m) = make_uint2(cur.r[8], cur.r[9]);
-                if (ok_cur & 4u)
+                if (o ? ok_cur.c : ok_cur.p)
                     *reinterpret_cast<uint2*>(da + RECORD + 64 + 8 * m) =
                         make_uint2(cur.r[10], cur.r[11]);
             }
@@ -765,7 +783,8 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
 #pragma unroll
                 for (int ks = 0; ks < 4; ++ks) kf[ks] = half8_t{0, 0, 0, 0, 0, 0, 0, 0};
             }
-            const uint32_t keep = ((ok_cur & 2u) ? 0x0000ffffu : 0u) | ((ok_cur & 4u) ? 0xffff0000u : 0u);
+            const bool oka = o ? ok_cur.p : ok_cur.c, okb = o ? ok_cur.c : ok_cur.p;
+            const uint32_t keep = (oka ? 0x0000ffffu : 0u) | (okb ? 0xffff0000u : 0u);
 #pragma unroll
             for (int u = 0; u < 16; ++u) vw[u] &= keep;
         }
