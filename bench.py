@@ -39,7 +39,9 @@ import numpy as np  # noqa: E402
 PEAK_HBM_GBS = 8000.0
 PEAK_FP32_TFS = 157.3      # MI355X published fp32 vector peak (packed FMA)
 METRIC = "CSA2 decode queries/s at 1M ctx + achieved HBM GB/s as % of MI355X peak"
-SCORE_SRC = os.path.join(ROOT, "fp4_kv_cache_decode_amd", "csrc", "index_score.hip")
+# the scan kernel's sources: its file and the scoring core it shares
+SCORE_SRC = ",".join(os.path.join("fp4_kv_cache_decode_amd", "csrc", f)
+                     for f in ("index_score.hip", "score_dev.h"))
 COUNTER_FILE = os.path.join(ROOT, "profiles", "scan_decoder20_1m_b4_counters.txt")
 STEP_COUNTER_FILE = os.path.join(ROOT, "profiles", "decoder20_1m_b4_step_counters.txt")
 CSRC = os.path.join(ROOT, "fp4_kv_cache_decode_amd", "csrc")
@@ -61,9 +63,14 @@ def code_hash(text: str) -> str:
     return hashlib.sha256("\n".join(lines).encode()).hexdigest()[:16]
 
 
-def source_hash(path=SCORE_SRC) -> str:
-    with open(path, encoding="utf-8") as f:
-        return code_hash(f.read())
+def source_hash(paths=SCORE_SRC) -> str:
+    """Code hash of one source, or of a comma-separated list of sources
+    (relative to the repository root), in the order given."""
+    parts = []
+    for p in paths.split(","):
+        with open(os.path.join(ROOT, p), encoding="utf-8") as f:
+            parts.append(f.read())
+    return code_hash("\n".join(parts))
 
 
 def counter_traffic(workload: str):
@@ -161,8 +168,9 @@ def row_counter_traffic(profile: str, workload: str):
     if not os.path.exists(path):
         return None
     kv = dict(re.findall(r"^(\w+)\s*=\s*(\S+)\s*$", open(path).read(), flags=re.M))
-    src = os.path.join(ROOT, kv.get("source", "-"))
-    if kv.get("workload") != workload or not os.path.exists(src):
+    src = kv.get("source", "-")
+    if kv.get("workload") != workload or not all(
+            os.path.exists(os.path.join(ROOT, p)) for p in src.split(",")):
         return None
     if kv.get("source_sha256") != source_hash(src):
         return None
@@ -508,6 +516,91 @@ def row_gather(args):
                    ms, cfg, roof)
 
 
+def _eager_loop(fn, n_calls, steps, warmup):
+    """Average milliseconds per call of fn(i) launched eagerly back to back
+    between one pair of events (the host stays ahead of the GPU)."""
+    import torch
+    for i in range(warmup):
+        fn(i % n_calls)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        fn(i % n_calls)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def row_reindex_layer(args):
+    """One Reindex layer of decoder20_1m_b4 (B=4, 1,048,576 tokens: pool scores
+    over the group's 2,048-block pool, top-512, attention over 512 + 128
+    entries with the gathered records stored for the Reuse layers), two ways:
+    the separate calls (four kernels, replayed as a HIP graph and launched
+    eagerly) and csa2_reindex_layer_fused (one cooperative launch, eagerly; in
+    a graph too where capture accepts it).  Rotates over the workload's four
+    Reindex layers' queries."""
+    import torch
+    import fp4_kv_cache_decode_amd.csa2 as K
+    from fp4_kv_cache_decode_amd import datagen as G
+    wl = G.WORKLOADS["decoder20_1m_b4"]
+    S = Setup(wl, args.seed, 1, False)
+    c, B = S.caches[0], wl.B
+    layers = [l for l, m in enumerate(wl.layers) if m == "I"]
+    # the group's pool from its Full layer
+    S.part_scan(c)
+    K.index_select_pool(S.M, S.ctx, wl.N, S.pool, S.ws_sel)
+    ws_f = torch.zeros(K.workspace_bytes(K.OP_REINDEX_LAYER_FUSED, B, 0, G.N_BLOCKS, G.BLOCK,
+                                         G.TOPK), dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    out = torch.empty((B, G.H, G.D), dtype=torch.float32, device="cuda")
+
+    def separate(i):
+        l = layers[i]
+        qi, wi = S.dqi[l]
+        K.index_reindex(c, qi, wi, S.seq, S.ctx, S.pool, S.idx, S.ws_ri)
+        K.decode_attn(c, l, S.dq[l], S.idx, S.seq, S.ctx, out, S.ws_at, kvg_out=S.kvg)
+
+    def fused(i):
+        l = layers[i]
+        qi, wi = S.dqi[l]
+        K.reindex_layer_fused(c, l, qi, wi, S.dq[l], S.seq, S.ctx, S.pool, S.idx, out, ws_f,
+                              status, kvg_out=S.kvg)
+
+    n = len(layers)
+    sep_graph, _ = _graph_loop(separate, n, args.steps, args.warmup)
+    sep_eager = _eager_loop(separate, n, args.steps, args.warmup)
+    fused_eager = _eager_loop(fused, n, args.steps, args.warmup)
+    try:
+        fused_graph, _ = _graph_loop(fused, n, args.steps, args.warmup)
+    except RuntimeError as e:            # capture refused the cooperative launch
+        log(f"[bench] fused layer not capturable: {e}")
+        fused_graph = None
+    torch.cuda.synchronize()
+    gave_up = int(status.item())
+    log(f"[bench] Reindex layer: separate {sep_graph * 1e3:.2f} us (graph), "
+        f"{sep_eager * 1e3:.2f} us (eager); fused {fused_eager * 1e3:.2f} us (eager)"
+        + (f", {fused_graph * 1e3:.2f} us (graph)" if fused_graph else "")
+        + f"; status {gave_up}")
+    # bytes of one layer: pool keys, pool list, records, window rows, q, outputs
+    alg = B * (G.N_BLOCKS * G.BLOCK * 64 + G.N_BLOCKS * 4 + G.TOPK * 144 * 2 +
+               G.WINDOW * 2 * G.D + (4 * 64 + 4) * 4 + G.H * G.D * 4 * 2 + G.TOPK * 4)
+    best = fused_graph if fused_graph else fused_eager
+    gbs = alg / (best * 1e-3) / 1e9
+    cfg = {"workload": "reindex_layer_decoder20_1m_b4", "batch": B, "ctx": wl.N,
+           "topk": G.TOPK, "pool_blocks": G.N_BLOCKS, "window": G.WINDOW,
+           "separate_graph_us": sep_graph * 1e3, "separate_eager_us": sep_eager * 1e3,
+           "fused_eager_us": fused_eager * 1e3,
+           "fused_graph_us": fused_graph * 1e3 if fused_graph else None,
+           "fused_status": gave_up, "launch": "cooperative", "dtype": "fp32"}
+    roof = {"bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+            "frac": gbs / PEAK_HBM_GBS, "traffic": None,
+            "kernel": "reindex_layer_kernel (csa2_reindex_layer_fused)", "avg_us": best * 1e3,
+            "alg_bytes": alg}
+    return _common(args, "CSA2 fused Reindex layers/s", 1e3 / best, "layers/s", best, cfg,
+                   roof)
+
+
 def row_prefill(args):
     """The 8,192-token prefill chunk over a 131,072-token prefix: quantise the
     chunk (main KV, indexer keys, window rows), then the Full-layer indexer and
@@ -629,10 +722,13 @@ def main():
                     help="launch every kernel from Python instead of replaying HIP graphs")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
-    ap.add_argument("--row", default="decode", choices=["decode", "quantize", "gather", "prefill"],
+    ap.add_argument("--row", default="decode",
+                    choices=["decode", "quantize", "gather", "prefill", "reindex_layer"],
                     help="decode: the whole decode step (default); quantize: bulk quantise-on-write "
                          "of the 1M-context cache; gather: gather/dequant/attention at B=1024; "
-                         "prefill: the 8,192-query chunk over a 131,072-token prefix")
+                         "prefill: the 8,192-query chunk over a 131,072-token prefix; "
+                         "reindex_layer: one Reindex layer, separate calls against the fused "
+                         "cooperative launch")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -649,7 +745,8 @@ def main():
         log(f"[bench] copy probe: {copy_bandwidth():.0f} GB/s")
         return
     if args.row != "decode":
-        res = {"quantize": row_quantize, "gather": row_gather, "prefill": row_prefill}[args.row](args)
+        res = {"quantize": row_quantize, "gather": row_gather, "prefill": row_prefill,
+               "reindex_layer": row_reindex_layer}[args.row](args)
         print(json.dumps(res), flush=True)
         return
 

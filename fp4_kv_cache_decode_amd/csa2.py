@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libcsa2.so")
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_LAUNCH = range(5)
 OP_INDEX_FULL, OP_INDEX_REINDEX, OP_DECODE_ATTN, OP_SELECT_POOL = 1, 2, 3, 4
+OP_REINDEX_LAYER_FUSED = 5
 
 D, HEADS, IDX_HEADS, IDX_DIM, WINDOW, RECORD, BLOCK = 128, 16, 4, 64, 128, 144, 8
 
@@ -69,6 +70,10 @@ def lib():
         L.csa2_decode_attn_noalloc.argtypes = [C.POINTER(csa2_cache), C.POINTER(csa2_window),
                                                C.c_int32, _P, _P, _P, _P, C.c_int32, C.c_int32,
                                                C.c_float, _P, _P, _P, _P]
+        L.csa2_reindex_layer_fused.argtypes = [C.POINTER(csa2_cache), C.POINTER(csa2_window),
+                                               C.c_int32, _P, _P, _P, _P, _P, C.c_int32, _P,
+                                               C.c_int32, C.c_int32, C.c_int32, C.c_float, _P,
+                                               _P, _P, C.c_int32, _P, _P, C.c_size_t, _P]
         L.csa2_workspace_bytes.argtypes = [C.c_int32, C.c_int32, C.c_int64, C.c_int32, C.c_int32,
                                            C.c_int32]
         L.csa2_workspace_bytes.restype = C.c_size_t
@@ -76,7 +81,8 @@ def lib():
         L.csa2_status_string.restype = C.c_char_p
         for f in ("csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex",
                   "csa2_decode_attn", "csa2_decode_attn_ex", "csa2_index_block_scores",
-                  "csa2_index_select_pool", "csa2_decode_attn_noalloc"):
+                  "csa2_index_select_pool", "csa2_decode_attn_noalloc",
+                  "csa2_reindex_layer_fused"):
             getattr(L, f).restype = C.c_int
         _lib = L
     return _lib
@@ -298,6 +304,37 @@ def decode_attn_noalloc(cache: Cache, layer: int, q, idx, seq, ctx, out, sm_scal
                                         _ptr(idx), _ptr(seq), _ptr(ctx), B, topk, sm_scale,
                                         _ptr(kvg_in), _ptr(kvg_out), _ptr(out), _stream(stream))
     _check(st, "csa2_decode_attn_noalloc")
+
+
+def reindex_layer_fused(cache: Cache, layer: int, q_idx, w, q, seq, ctx, pool, idx, out, ws,
+                        status, kvg_out=None, sm_scale=None, max_polls: int = 0,
+                        block: int = 8, stream=None) -> None:
+    """csa2_reindex_layer_fused: index_reindex then decode_attn (with kvg_out)
+    in one cooperative launch.  ws (uint8, OP_REINDEX_LAYER_FUSED bytes) must be
+    zero-filled before its first use; status (int32 [1]) is ORed with 1 when a
+    grid barrier gave up."""
+    B, topk = idx.shape
+    n_blocks = pool.shape[1]
+    _need(q_idx, torch.float32, (B, IDX_HEADS, IDX_DIM), "q_idx")
+    _need(w, torch.float32, (B, IDX_HEADS), "w")
+    _need(q, torch.float32, (B, HEADS, D), "q")
+    _need(seq, torch.int32, (B,), "seq")
+    _need(ctx, torch.int64, (B,), "ctx")
+    _need(pool, torch.int32, (B, n_blocks), "pool")
+    _need(idx, torch.int32, (B, topk), "idx")
+    _need(out, torch.float32, (B, HEADS, D), "out")
+    _need(ws, torch.uint8, None, "ws")
+    _need(status, torch.int32, (1,), "status")
+    if kvg_out is not None:
+        _need(kvg_out, torch.uint8, (B, topk, RECORD), "kvg_out")
+    if sm_scale is None:
+        sm_scale = float(torch.tensor(D ** -0.5, dtype=torch.float32))
+    st = lib().csa2_reindex_layer_fused(C.byref(cache.c), C.byref(cache.w), layer, _ptr(q_idx),
+                                        _ptr(w), _ptr(q), _ptr(seq), _ptr(ctx), B, _ptr(pool),
+                                        n_blocks, block, topk, sm_scale, _ptr(idx),
+                                        _ptr(kvg_out), _ptr(out), max_polls, _ptr(status),
+                                        _ptr(ws), ws.numel(), _stream(stream))
+    _check(st, "csa2_reindex_layer_fused")
 
 
 def alloc_workspace(op: int, B: int, max_ctx: int = 0, n_blocks: int = 2048, topk: int = 512,

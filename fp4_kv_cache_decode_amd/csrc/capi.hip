@@ -51,6 +51,22 @@ size_t reindex_bytes(int32_t B, int32_t n_blocks) {
            select_bytes(B, (int64_t)n_blocks * BLOCK);
 }
 
+// Fused Reindex layer: barrier words, pool scores, the tiles' partial records.
+struct LayerLayout {
+    size_t s_off, part_off, total;
+};
+
+int32_t layer_tiles(int32_t topk) { return (topk + 63) / 64 + CSA2_WINDOW / 64; }
+
+LayerLayout layer_layout(int32_t B, int32_t n_blocks, int32_t topk) {
+    LayerLayout L;
+    L.s_off = align_up(sizeof(csa2::LayerSync));
+    L.part_off = align_up(L.s_off + (size_t)B * (size_t)n_blocks * BLOCK * sizeof(float));
+    L.total = L.part_off + align_up((size_t)B * (size_t)layer_tiles(topk) *
+                                    csa2::ATTN_PART_FLOATS * sizeof(float));
+    return L;
+}
+
 size_t attn_bytes(int32_t B, int32_t topk) {
     return align_up((size_t)csa2::attn_partials(B, topk, csa2::ATTN_NO_CAP) *
                     csa2::ATTN_PART_FLOATS * sizeof(float));
@@ -159,6 +175,9 @@ size_t csa2_workspace_bytes(int32_t op, int32_t B, int64_t max_ctx, int32_t n_bl
         case CSA2_OP_SELECT_POOL:
             if (max_ctx < 0 || n_blocks < 1 || n_blocks > CSA2_MAX_POOL) return 0;
             return select_bytes(B, (max_ctx + BLOCK - 1) / BLOCK);
+        case CSA2_OP_REINDEX_LAYER_FUSED:
+            if (check_select(B, n_blocks, block, topk) != CSA2_OK) return 0;
+            return layer_layout(B, n_blocks, topk).total;
     }
     return 0;
 }
@@ -316,6 +335,37 @@ csa2_status csa2_decode_attn_noalloc(const csa2_cache* cache, const csa2_window*
     }
     return launched(csa2::launch_attn(*cache, *win, layer, q, idx, seq, ctx, B, topk, sm_scale,
                                       kvg_in, kvg_out, out, part, NOALLOC_MAX_PARTS, stream));
+}
+
+csa2_status csa2_reindex_layer_fused(const csa2_cache* cache, const csa2_window* win,
+                                     int32_t layer, const float* q_idx, const float* w,
+                                     const float* q, const int32_t* seq, const int64_t* ctx,
+                                     int32_t B, const int32_t* pool, int32_t n_blocks,
+                                     int32_t block, int32_t topk, float sm_scale, int32_t* idx,
+                                     uint8_t* kvg_out, float* out, int32_t max_polls,
+                                     int32_t* status, void* ws, size_t ws_bytes,
+                                     hipStream_t stream) {
+    csa2_status st = check_cache(cache, true, true);
+    if (st != CSA2_OK) return st;
+    st = check_window(win, cache);
+    if (st != CSA2_OK) return st;
+    if (!q_idx || !w || !q || !seq || !ctx || !pool || !idx || !out || !status)
+        return CSA2_ERR_INVALID_ARG;
+    if (layer < 0 || layer >= win->n_layers || !isfinite(sm_scale)) return CSA2_ERR_INVALID_ARG;
+    st = check_select(B, n_blocks, block, topk);
+    if (st != CSA2_OK) return st;
+    if ((int64_t)B * layer_tiles(topk) > csa2::ATTN_MIN_CAP) return CSA2_ERR_UNSUPPORTED;
+    if (B == 0) return CSA2_OK;
+    const LayerLayout L = layer_layout(B, n_blocks, topk);
+    if (!ws || ws_bytes < L.total) return CSA2_ERR_WORKSPACE;
+    // every workgroup of the launch must be resident at once
+    if (!csa2::reindex_layer_fits(*cache, B, n_blocks, topk)) return CSA2_ERR_UNSUPPORTED;
+    char* base = static_cast<char*>(ws);
+    return launched(csa2::launch_reindex_layer(
+        *cache, *win, layer, q_idx, w, q, seq, ctx, B, pool, n_blocks, topk, sm_scale, idx,
+        kvg_out, out, max_polls, status, reinterpret_cast<csa2::LayerSync*>(base),
+        reinterpret_cast<float*>(base + L.s_off), reinterpret_cast<float*>(base + L.part_off),
+        stream));
 }
 
 csa2_status csa2_decode_attn(const csa2_cache* cache, const csa2_window* win, int32_t layer,

@@ -71,4 +71,33 @@ constexpr size_t ATTN_PART_FLOATS = 16 + 16 + 16 * 128;
 constexpr int64_t ATTN_NO_CAP = INT64_MAX;
 constexpr int64_t ATTN_MIN_CAP = 768;   // the tile kernel's largest grid
 
+// Barrier words of the fused Reindex layer (zero-filled once before first use),
+// each on a 128-byte line of its own: arrivals of the workgroups with equal
+// index mod LAYER_SYNC_GROUPS, arrivals of those groups, and the barriers
+// completed.  Counts are 0 between barriers.
+constexpr int LAYER_SYNC_GROUPS = 8;
+struct LayerSync {
+    struct alignas(128) Word {
+        uint32_t v;
+    };
+    Word group[LAYER_SYNC_GROUPS];
+    Word root;
+    Word gen;
+};
+
+// One Reindex layer (pool scores, top-k, attention tiles, merge) in one
+// cooperative launch; scores holds [B][n_blocks * 8] floats, partials
+// [B][tiles][ATTN_PART_FLOATS].  Bit-identical to launch_score_pool +
+// launch_topk + launch_attn whenever launch_attn takes its tile path.
+hipError_t launch_reindex_layer(const csa2_cache& c, const csa2_window& w, int32_t layer,
+                                const float* q_idx, const float* wts, const float* q,
+                                const int32_t* seq, const int64_t* ctx, int32_t B,
+                                const int32_t* pool, int32_t n_blocks, int32_t topk,
+                                float sm_scale, int32_t* idx, uint8_t* kvg_out, float* out,
+                                int32_t max_polls, int32_t* status, LayerSync* sync,
+                                float* scores, float* partials, hipStream_t stream);
+// Whether that launch's grid (one round of every stage) can be resident on the
+// current device.
+bool reindex_layer_fits(const csa2_cache& c, int32_t B, int32_t n_blocks, int32_t topk);
+
 }  // namespace csa2

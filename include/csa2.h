@@ -125,7 +125,8 @@ enum {
     CSA2_OP_INDEX_FULL = 1,
     CSA2_OP_INDEX_REINDEX = 2,
     CSA2_OP_DECODE_ATTN = 3,
-    CSA2_OP_SELECT_POOL = 4
+    CSA2_OP_SELECT_POOL = 4,
+    CSA2_OP_REINDEX_LAYER_FUSED = 5
 };
 
 /*
@@ -293,6 +294,44 @@ csa2_status csa2_decode_attn_noalloc(const csa2_cache* cache, const csa2_window*
                                      const int32_t* seq, const int64_t* ctx, int32_t B,
                                      int32_t topk, float sm_scale, const uint8_t* kvg_in,
                                      uint8_t* kvg_out, float* out, hipStream_t stream);
+
+/*
+ * csa2_reindex_layer_fused - one Reindex layer in a single cooperative launch:
+ * csa2_index_reindex(q_idx, w, pool -> idx) followed by
+ * csa2_decode_attn_ex(q, idx, kvg_out -> out), with the layer's four stages
+ * (pool scores, top-k, attention tiles, merge) separated by grid-wide barriers
+ * inside one kernel instead of kernel boundaries.
+ * Passage: a Reindex layer re-scores only its group's candidate pool with its
+ * own indexer query over the shared indexer keys, re-selects the top-k
+ * positions and attends over them plus its sliding window ([P4] "How the
+ * architecture shrinks the KV cache"; [P5] "CSA2 and the attention redesign").
+ *   Arguments as in csa2_index_reindex and csa2_decode_attn_ex (block must be
+ *   8; kvg_out may be NULL).  idx, out and kvg_out are bit-identical to those
+ *   two calls.  B * (ceil(topk / 64) + 2) must not exceed 768 (the batches the
+ *   separate attention call runs as 64-entry tiles; else CSA2_ERR_UNSUPPORTED).
+ *   status    device int32: nothing is written when every barrier completes;
+ *             a workgroup that polled a barrier max_polls times without seeing
+ *             it complete ORs 1 into *status and goes on, and the results of
+ *             that call are undefined.  The caller clears it.
+ *   max_polls polls per barrier wait before giving up; <= 0 selects a default
+ *             of about a second.
+ *   ws        csa2_workspace_bytes(CSA2_OP_REINDEX_LAYER_FUSED, B, 0, n_blocks, 8,
+ *             topk) bytes.  Its first 1,280 bytes hold the barrier words: they
+ *             must be zero before the first call with this workspace (zero-fill
+ *             it once) and every call leaves the counts zero, except a call that
+ *             gave up, after which they must be zero-filled again.
+ *   The kernel's workgroups must all be resident at once; the grid is capped at
+ *   the device's resident limit (CSA2_ERR_LAUNCH if the cooperative launch is
+ *   refused).  Calls sharing a workspace must not overlap.
+ */
+csa2_status csa2_reindex_layer_fused(const csa2_cache* cache, const csa2_window* win,
+                                     int32_t layer, const float* q_idx, const float* w,
+                                     const float* q, const int32_t* seq, const int64_t* ctx,
+                                     int32_t B, const int32_t* pool, int32_t n_blocks,
+                                     int32_t block, int32_t topk, float sm_scale, int32_t* idx,
+                                     uint8_t* kvg_out, float* out, int32_t max_polls,
+                                     int32_t* status, void* ws, size_t ws_bytes,
+                                     hipStream_t stream);
 
 /* Workspace bytes an operation needs (0 for unknown op or invalid sizes). */
 size_t csa2_workspace_bytes(int32_t op, int32_t B, int64_t max_ctx, int32_t n_blocks,

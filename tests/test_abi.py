@@ -156,6 +156,46 @@ def test_attn_error_paths(L):
     assert call_ex(FAKE, None, B=0) == 0
 
 
+def test_fused_layer_sizes_and_error_paths(L):
+    """csa2_reindex_layer_fused: workspace = barrier words (ten 128-byte lines)
+    + pool scores + the tiles' partial records; host-side argument checks."""
+    from fp4_kv_cache_decode_amd import csa2 as K
+    part = (32 + 2048) * 4
+    ws = K.workspace_bytes(K.OP_REINDEX_LAYER_FUSED, 4, 0, 2048, 8, 512)
+    assert ws == 1280 + 4 * 16384 * 4 + 4 * 10 * part
+    assert K.workspace_bytes(K.OP_REINDEX_LAYER_FUSED, 4, 0, 2048, 4, 512) == 0   # block != 8
+    assert K.workspace_bytes(K.OP_REINDEX_LAYER_FUSED, 4, 0, 8192, 8, 512) == 0   # pool too big
+    c, w = _cache(K), _win(K, n_layers=2)
+    f = L.csa2_reindex_layer_fused
+    ws2 = K.workspace_bytes(K.OP_REINDEX_LAYER_FUSED, 2, 0, 64, 8, 32)
+
+    def call(**kw):
+        a = dict(c=C.byref(c), w=C.byref(w), layer=1, qi=FAKE, wt=FAKE, q=FAKE, seq=FAKE,
+                 ctx=FAKE, B=2, pool=FAKE, nb=64, block=8, topk=32, sm=0.088, idx=FAKE,
+                 kvg=None, out=FAKE, polls=0, status=FAKE, ws=FAKE, wsb=ws2)
+        a.update(kw)
+        return f(a["c"], a["w"], a["layer"], a["qi"], a["wt"], a["q"], a["seq"], a["ctx"],
+                 a["B"], a["pool"], a["nb"], a["block"], a["topk"], a["sm"], a["idx"],
+                 a["kvg"], a["out"], a["polls"], a["status"], a["ws"], a["wsb"], None)
+
+    assert call(c=None) == 1
+    assert call(w=None) == 1
+    assert call(c=C.byref(_cache(K, idxk=None))) == 1
+    assert call(qi=None) == 1
+    assert call(q=None) == 1
+    assert call(pool=None) == 1
+    assert call(status=None) == 1
+    assert call(layer=2) == 1
+    assert call(sm=float("inf")) == 1
+    assert call(block=16) == 2
+    assert call(nb=5000) == 2
+    assert call(nb=2, topk=32) == 1                   # topk > n_blocks * 8
+    assert call(B=77, topk=512) == 2                  # 77 x 10 tiles > 768
+    assert call(ws=None) == 3
+    assert call(wsb=ws2 - 1) == 3
+    assert call(B=0) == 0
+
+
 def test_paged_cache_validation(L):
     """A page table needs a power-of-two page of 64..65,536 tokens that divides
     cap and at least one physical page; every entry point checks it."""
