@@ -72,16 +72,13 @@ constexpr int64_t ATTN_NO_CAP = INT64_MAX;
 constexpr int64_t ATTN_MIN_CAP = 768;   // the tile kernel's largest grid
 
 // Barrier words of the fused Reindex layer (zero-filled once before first use),
-// each on a 128-byte line of its own: arrivals of the workgroups with equal
-// index mod LAYER_SYNC_GROUPS, arrivals of those groups, and the barriers
-// completed.  Counts are 0 between barriers.
-constexpr int LAYER_SYNC_GROUPS = 8;
+// each on a 128-byte line of its own: arrivals at the current grid barrier (0
+// between barriers) and the barriers completed.
 struct LayerSync {
     struct alignas(128) Word {
         uint32_t v;
     };
-    Word group[LAYER_SYNC_GROUPS];
-    Word root;
+    Word count;
     Word gen;
 };
 

@@ -27,13 +27,11 @@
 //   4. merge: (head, query) merges of 128 threads, up to eight side by side.
 //
 // Grid barrier: the workgroup synchronises, its thread 0 fences (device
-// scope) and arrives on its group's counter (workgroups with equal index mod
-// 8; one counter for all measured 10 us when 64 workgroups arrived together,
-// the device-scope atomics on one address being serialised).  The last
-// arrival of a group resets that counter and arrives on the root counter; the
-// last root arrival resets it and advances a generation word, which everyone
-// else polls.  An acquire fence and a workgroup barrier follow.  Counts are
-// zero between barriers, so zero-filled words serve every later launch.
+// scope) and arrives on a counter.  The last arrival resets the counter and
+// then advances a generation word, which the others poll (the two words on
+// separate cache lines).  An acquire fence and a workgroup barrier follow.
+// The count is zero between barriers, so zero-filled words serve every later
+// launch.
 // Waits are bounded: a workgroup that has polled max_polls times stops
 // waiting, ORs 1 into *status and goes on; its results are then undefined,
 // but every wave still reaches the end of the kernel.
@@ -84,25 +82,15 @@ __device__ __forceinline__ void grid_barrier(LayerSync* sy, uint32_t n_wg, uint3
     // workgroup, not one per wave)
     __syncthreads();
     if (threadIdx.x == 0) {
-        constexpr uint32_t NG = LAYER_SYNC_GROUPS;
-        const uint32_t grp = blockIdx.x % NG;
-        const uint32_t n_grp = n_wg < NG ? n_wg : NG;
-        const uint32_t in_grp = (n_wg - grp + NG - 1) / NG;     // workgroups in this group
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
         bool wait = true;
-        if (__hip_atomic_fetch_add(&sy->group[grp].v, 1u, __ATOMIC_RELAXED,
-                                   __HIP_MEMORY_SCOPE_AGENT) == in_grp - 1) {
-            // last of its group: the group's count is reset before the group
-            // arrives (release: the reset is seen before the next barrier's
-            // arrivals, which follow the generation word's advance)
-            __hip_atomic_store(&sy->group[grp].v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            if (__hip_atomic_fetch_add(&sy->root.v, 1u, __ATOMIC_ACQ_REL,
-                                       __HIP_MEMORY_SCOPE_AGENT) == n_grp - 1) {
-                __hip_atomic_store(&sy->root.v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                __hip_atomic_store(&sy->gen.v, gen + 1u, __ATOMIC_RELEASE,
-                                   __HIP_MEMORY_SCOPE_AGENT);
-                wait = false;
-            }
+        if (__hip_atomic_fetch_add(&sy->count.v, 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT) == n_wg - 1) {
+            // last arrival: reset the count, then release the others (release:
+            // the reset is seen before the next barrier's arrivals)
+            __hip_atomic_store(&sy->count.v, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(&sy->gen.v, gen + 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+            wait = false;
         }
         if (wait) {
             int32_t polls = 0;

@@ -316,9 +316,9 @@ csa2_status csa2_decode_attn_noalloc(const csa2_cache* cache, const csa2_window*
  *   max_polls polls per barrier wait before giving up; <= 0 selects a default
  *             of about a second.
  *   ws        csa2_workspace_bytes(CSA2_OP_REINDEX_LAYER_FUSED, B, 0, n_blocks, 8,
- *             topk) bytes.  Its first 1,280 bytes hold the barrier words: they
- *             must be zero before the first call with this workspace (zero-fill
- *             it once) and every call leaves the counts zero, except a call that
+ *             topk) bytes.  Its first 256 bytes hold the barrier words: they must
+ *             be zero before the first call with this workspace (zero-fill it
+ *             once) and every call leaves its count at zero, except a call that
  *             gave up, after which they must be zero-filled again.
  *   The kernel's workgroups must all be resident at once; the grid is capped at
  *   the device's resident limit (CSA2_ERR_LAUNCH if the cooperative launch is

@@ -157,12 +157,12 @@ def test_attn_error_paths(L):
 
 
 def test_fused_layer_sizes_and_error_paths(L):
-    """csa2_reindex_layer_fused: workspace = barrier words (ten 128-byte lines)
+    """csa2_reindex_layer_fused: workspace = barrier words (two 128-byte lines)
     + pool scores + the tiles' partial records; host-side argument checks."""
     from fp4_kv_cache_decode_amd import csa2 as K
     part = (32 + 2048) * 4
     ws = K.workspace_bytes(K.OP_REINDEX_LAYER_FUSED, 4, 0, 2048, 8, 512)
-    assert ws == 1280 + 4 * 16384 * 4 + 4 * 10 * part
+    assert ws == 256 + 4 * 16384 * 4 + 4 * 10 * part
     assert K.workspace_bytes(K.OP_REINDEX_LAYER_FUSED, 4, 0, 2048, 4, 512) == 0   # block != 8
     assert K.workspace_bytes(K.OP_REINDEX_LAYER_FUSED, 4, 0, 8192, 8, 512) == 0   # pool too big
     c, w = _cache(K), _win(K, n_layers=2)

@@ -101,11 +101,10 @@ class Layer:
 
 
 def _barrier_words(ws):
-    """(the 8 group counts and the root count, the generation word): one
-    uint32 at the start of each 128-byte line of the workspace's first 1,280
-    bytes."""
-    w = ws[:1280].view(torch.int32).cpu().numpy()[::32]
-    return w[:9], int(w[9])
+    """(the arrival count, the generation word): one uint32 at the start of
+    each 128-byte line of the workspace's first 256 bytes."""
+    w = ws[:256].view(torch.int32).cpu().numpy()[::32]
+    return w[:1], int(w[1])
 
 
 def _check_oracle(L, idx, out, kvg):
@@ -164,6 +163,44 @@ def test_fused_layer_matches_oracle_and_separate_calls(K, name):
     assert not counts.any() and gen == 3, (counts, gen)
 
 
+def _sweep_case(seed):
+    """A seeded random shape inside the fused entry point's envelope: B x tiles
+    <= 768 and one round of 1,024-thread workgroups within 256 CUs."""
+    rng = np.random.default_rng(1000 + seed)
+    while True:
+        B = int(rng.integers(1, 13))
+        nb = int(rng.choice([1, 7, 64, 300, 2048, 4096]))
+        topk = int(rng.integers(1, min(2048, nb * 8) + 1))
+        runs = -(-nb * 8 // 256)
+        tiles = -(-topk // 64) + 2
+        if B * tiles <= 768 and -(-B * runs // 4) <= 256 and -(-B * tiles // 4) <= 256:
+            break
+    N = int(rng.integers(max(1, nb), 30001))
+    ctx = [int(rng.integers(0, N + 1)) for _ in range(B)]
+    ctx[0] = N
+    pt = int(rng.choice([0, 64, 1024]))
+    return B, N, ctx, nb, topk, pt
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_fused_layer_random_sweep(K, seed):
+    """Seeded random batches, pool sizes, top-k sizes, contexts (empty ones
+    included) and page sizes: bit for bit against the separate calls, and the
+    oracle's bars."""
+    B, N, ctx, nb, topk, pt = _sweep_case(seed)
+    _say(f"fused reindex layer sweep {seed}: B={B} N={N} n_blocks={nb} topk={topk} "
+         f"paged={pt} ctx={ctx}")
+    L = Layer(K, 300 + seed, B, N, ctx, nb, topk, page_tokens=pt)
+    ws = L.workspace(K)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    got = L.fused(K, ws, status)
+    assert int(status.item()) == 0
+    for g, s_, what in zip(got, L.separate(K), ("idx", "out", "kvg")):
+        assert torch.equal(g, s_), what
+    n_diff, err = _check_oracle(L, *got)
+    _say(f"  exempt index differences {n_diff}, attention max-abs {err:.3g}")
+
+
 def test_fused_layer_repeated_calls(K):
     """One zero-filled workspace serves calls in a row: identical results,
     count back at 0 after each, generation +3 per call."""
@@ -182,9 +219,9 @@ def test_fused_layer_repeated_calls(K):
 
 
 def test_fused_layer_reports_give_up(K):
-    """Barrier words that are not zero (group 0's count never reaches its size,
-    so the barrier never completes) make every workgroup give up after
-    max_polls polls at each barrier: the
+    """Barrier words that are not zero (the count never reaches the grid size,
+    so no barrier completes) make every workgroup give up after max_polls
+    polls at each barrier: the
     launch still completes and the status word reports it.  After a zero fill
     the same workspace gives the separate calls' results again."""
     _say("fused reindex layer give-up path")
