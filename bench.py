@@ -108,26 +108,25 @@ def step_alg_bytes(wl) -> int:
     return wl.B * per_q
 
 
-def csrc_hash() -> str:
-    """Code hash over every kernel source of the library (sorted by name)."""
-    parts = []
-    for name in sorted(os.listdir(CSRC)):
-        if name.endswith((".hip", ".h")):
-            with open(os.path.join(CSRC, name), encoding="utf-8") as f:
-                parts.append(name + "\n" + f.read())
-    return code_hash("\n".join(parts))
+# the sources of the decode step's kernels (the device code of every kernel the
+# step launches, and the helpers it includes)
+STEP_SOURCES = ",".join(os.path.join("fp4_kv_cache_decode_amd", "csrc", f) for f in (
+    "csa2_device.h", "quantize.hip", "index_score.hip", "score_dev.h", "topk.hip", "topk_dev.h",
+    "attn.hip", "attn_dev.h"))
 
 
 def step_counter_traffic(workload: str):
     """HBM bytes of one whole decode step from committed per-kernel counters:
     the sum over the step's kernels of calls x (FETCH_SIZE x fetch factor +
     WRITE_SIZE x write factor), in KiB per dispatch; None if the file is
-    absent, names another workload, or any kernel source changed since."""
+    absent, names another workload, or the step kernels' sources changed since."""
     if not os.path.exists(STEP_COUNTER_FILE):
         return None
     txt = open(STEP_COUNTER_FILE).read()
     kv = dict(re.findall(r"^(\w+)\s*=\s*(\S+)\s*$", txt, flags=re.M))
-    if kv.get("workload") != workload or kv.get("csrc_sha256") != csrc_hash():
+    if kv.get("workload") != workload or kv.get("sources") != STEP_SOURCES:
+        return None
+    if kv.get("source_sha256") != source_hash(STEP_SOURCES):
         return None
     try:
         ff, wf = float(kv["copy_fetch_factor"]), float(kv["copy_write_factor"])
