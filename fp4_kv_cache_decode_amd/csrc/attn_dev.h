@@ -104,7 +104,7 @@ constexpr float LN2 = 0.6931471805599453f;
 // ---------------------------------------------------------------------------
 // Tile kernel (small batches, latency): one workgroup per (query, 64-entry
 // tile), each of its 4 waves owning 16 entries.  The work of a wave is one
-// step of the stream kernel's loop (below), with the same lane roles: lane
+// step of the stream kernel's loop (attn.hip), with the same lane roles: lane
 // (c, g) gathers K channels 32g..32g+31 of entry c and V channel group
 // 4(c mod 2) + g of the entry pair containing c; S^T = K Q^T comes out of
 // v_mfma_f32_16x16x32_f16 with K straight from the gathering lane's
