@@ -42,3 +42,20 @@ def test_row_counters_match_their_sources():
         t = bench.row_counter_traffic(prof, wl)
         assert t is None or t > 0
         assert bench.row_counter_traffic(prof, "another_workload") is None
+
+
+def test_source_hash_covers_every_listed_file():
+    """A counter record names its kernel's sources as a comma-separated list;
+    the hash covers all of them in order, so a change to any shared device
+    header retires the counters."""
+    import bench
+    one = "fp4_kv_cache_decode_amd/csrc/attn.hip"
+    two = one + ",fp4_kv_cache_decode_amd/csrc/attn_dev.h"
+    texts = [open(os.path.join(ROOT, p)).read() for p in two.split(",")]
+    assert bench.source_hash(one) == bench.code_hash(texts[0])
+    assert bench.source_hash(two) == bench.code_hash("\n".join(texts))
+    assert bench.source_hash(two) != bench.source_hash(one)
+    # the step counters list the step kernels' sources, none of the host-only files
+    step = bench.STEP_SOURCES.split(",")
+    assert all(os.path.exists(os.path.join(ROOT, p)) for p in step)
+    assert not any(p.endswith(("capi.hip", "layer.hip", "csa2_internal.h")) for p in step)
