@@ -256,3 +256,36 @@ def test_fused_layer_refuses_what_does_not_fit(K):
         K.reindex_layer_fused(L.gc, 1, d(L.qi), d(L.wi), d(L.q), d(L.seq), d(L.ctx), pool, idx,
                               out, ws, status)
     assert e.value.status == K.ERR_UNSUPPORTED
+
+
+def test_fused_layer_in_hip_graph(K):
+    """The cooperative launch captured in a HIP graph: four replays, with eager
+    work and synchronisations between them, each bit-identical to the eager
+    call; the barrier count is back at zero and the generation advanced by 3
+    per launch."""
+    _say("fused reindex layer in a HIP graph")
+    L = Layer(K, 24, 4, 20000, [20000, 19000, 17000, 18000], 2048, 512)
+    ws = L.workspace(K)
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    want = L.fused(K, ws, status)
+    d = L.d
+    idx, out, kvg = L.outputs()
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        K.reindex_layer_fused(L.gc, L.layer, d["qi"], d["wi"], d["q"], d["seq"], d["ctx"],
+                              d["pool"], idx, out, ws, status, kvg_out=kvg)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        idx.fill_(-7)
+        out.fill_(7.0)
+        kvg.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for a, b, what in zip((idx, out, kvg), want, ("idx", "out", "kvg")):
+            assert torch.equal(a, b), (rep, what)
+        L.separate(K)                   # eager work between replays
+    counts, gen = _barrier_words(ws)
+    assert not counts.any() and gen == 3 * 5, (counts, gen)
+    assert int(status.item()) == 0
