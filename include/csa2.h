@@ -18,8 +18,9 @@
  *  - Every array argument is a DEVICE pointer allocated by the caller; the
  *    descriptor structs themselves are host memory read during the call.
  *  - The library allocates nothing, frees nothing, never synchronises and keeps
- *    no global state: each call validates its arguments on the host, enqueues
- *    kernels on `stream` and returns.  Calls are reentrant; calls on different
+ *    no global state (except the fixed per-GPU scratch array of
+ *    csa2_decode_attn_noalloc, below): each call validates its arguments on the
+ *    host, enqueues kernels on `stream` and returns.  Calls are reentrant; calls on different
  *    streams must not share a workspace.
  *  - Argument errors are reported synchronously through the return value and
  *    enqueue nothing.  Launch errors return CSA2_ERR_LAUNCH.  Device-side
