@@ -90,11 +90,26 @@ struct StreamArgs {
     float sm_scale;
 };
 
-// One workgroup per (64-entry tile, query).
+// The dispatcher deals workgroups round-robin over the 8 XCDs (workgroup id mod 8),
+// each with its own L2.  xcd_work maps a 1-D grid of 8 * ceil(W / 8) workgroups onto
+// W query-major work items so that each XCD runs one contiguous range of them: a
+// query's tiles, and then its merges, sit on the same XCD or two.  -1 marks the
+// padding workgroups.
+__device__ __forceinline__ int xcd_work(int id, int W) {
+    const int per = (W + 7) >> 3;
+    const int work = (id & 7) * per + (id >> 3);
+    return work < W ? work : -1;
+}
+
+dim3 xcd_grid(int64_t W) { return dim3((unsigned)(8 * ((W + 7) / 8))); }
+
+// One workgroup per (64-entry tile, query), placed by xcd_work.
 template <int AM>
-__global__ void __launch_bounds__(AT_THREADS) attn_tile_kernel(TileArgs a) {
+__global__ void __launch_bounds__(AT_THREADS) attn_tile_kernel(TileArgs a, int32_t B) {
     __shared__ AttnShared sh;
-    tile_body<AM>(a, sh, blockIdx.x, blockIdx.y, threadIdx.x);
+    const int work = xcd_work(blockIdx.x, B * a.n_tiles);
+    if (work < 0) return;
+    tile_body<AM>(a, sh, work % a.n_tiles, work / a.n_tiles, threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -463,10 +478,12 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
     }
 }
 
-// One workgroup per (head, query), one thread per output dim.
+// One workgroup per (head, query), placed by xcd_work; one thread per output dim.
 __global__ void __launch_bounds__(D) attn_merge_kernel(const float* part, int32_t n_parts,
-                                                       float* out) {
-    merge_body(part, n_parts, out, blockIdx.x, blockIdx.y, threadIdx.x);
+                                                       float* out, int32_t B) {
+    const int work = xcd_work(blockIdx.x, B * HEADS);
+    if (work < 0) return;
+    merge_body(part, n_parts, out, work % HEADS, work / HEADS, threadIdx.x);
 }
 
 }  // namespace
@@ -539,18 +556,18 @@ hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
         a.wv_scale = w.v_scale;
         a.sm_scale = sm_scale;
         if (c.page_table)
-            hipLaunchKernelGGL(attn_tile_kernel<AM_PAGED>, dim3(a.n_tiles, B), dim3(AT_THREADS), 0,
-                               stream, a);
+            hipLaunchKernelGGL(attn_tile_kernel<AM_PAGED>, xcd_grid((int64_t)B * a.n_tiles),
+                               dim3(AT_THREADS), 0, stream, a, B);
         else if (off32)
-            hipLaunchKernelGGL(attn_tile_kernel<AM_OFF32>, dim3(a.n_tiles, B), dim3(AT_THREADS), 0,
-                               stream, a);
+            hipLaunchKernelGGL(attn_tile_kernel<AM_OFF32>, xcd_grid((int64_t)B * a.n_tiles),
+                               dim3(AT_THREADS), 0, stream, a, B);
         else
-            hipLaunchKernelGGL(attn_tile_kernel<AM_FLAT64>, dim3(a.n_tiles, B), dim3(AT_THREADS),
-                               0, stream, a);
+            hipLaunchKernelGGL(attn_tile_kernel<AM_FLAT64>, xcd_grid((int64_t)B * a.n_tiles),
+                               dim3(AT_THREADS), 0, stream, a, B);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(attn_merge_kernel, dim3(HEADS, B), dim3(D), 0, stream, partials,
-                           a.n_tiles, out);
+        hipLaunchKernelGGL(attn_merge_kernel, xcd_grid((int64_t)B * HEADS), dim3(D), 0, stream,
+                           partials, a.n_tiles, out, B);
         return hipGetLastError();
     }
     StreamArgs a{};
@@ -588,8 +605,8 @@ hipError_t launch_attn(const csa2_cache& c, const csa2_window& w, int32_t layer,
                            stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.n_split == 1) return e;
-    hipLaunchKernelGGL(attn_merge_kernel, dim3(HEADS, B), dim3(D), 0, stream, partials,
-                       a.n_split, out);
+    hipLaunchKernelGGL(attn_merge_kernel, xcd_grid((int64_t)B * HEADS), dim3(D), 0, stream,
+                       partials, a.n_split, out, B);
     return hipGetLastError();
 }
 
