@@ -6,12 +6,19 @@
 // channels; the sliding-window K/V stay FP8 (E4M3); indexer keys are FP8 too
 // (this library's reading: one per-tensor fp32 scale for each FP8 store).
 //
-// Every part of the grid covers the same 16 rows per block, 16 threads per row.
-// Part 0 writes main-KV records (one 16-channel group per thread: 8 of K, 8 of
-// V), part 1 indexer keys (4 channels per thread), part 2+l the window rows of
-// layer l (one 16-channel group per thread: 8 of K, 8 of V).  A group's thread
-// reads 64 contiguous bytes of fp32, so a wave streams 4 KB of input per
-// instruction group.
+// Every part of the grid covers the same 16 * QG rows per block, 16 threads per
+// row and QG groups of 16 rows per thread.  Part 0 writes the main-KV records (one
+// 16-channel group per thread: 8 of K, 8 of V) and, when given, the rows' indexer
+// keys (4 channels per thread); part 1+l writes the window rows of layer l (one
+// 16-channel group per thread: 8 of K, 8 of V).  A group's thread reads 64
+// contiguous bytes of fp32, so a wave streams 4 KB of input per instruction group.
+//
+// QG = 4 from 1,048,576 rows on, where more loads in flight per thread pay (4M
+// rows: 1.17 ms against 1.19 with QG = 1); below that QG = 1, which spreads a call
+// over four times the blocks (256K rows: 73 us against 79).  A thread loads seq
+// and pos of its rows first and then all of its row data, before it decides where
+// any row goes: a wait on a destination then never drains the row loads behind
+// it, and the row data is in flight while the destinations are checked.
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
@@ -20,7 +27,9 @@ namespace csa2 {
 namespace {
 
 constexpr int QTHREADS = 256;
-constexpr int ROWS_MAIN = QTHREADS / 16;   // rows per block (16 threads per row)
+constexpr int ROWS_GROUP = QTHREADS / 16;   // rows per group (16 threads per row)
+constexpr int QG_BULK = 4;                  // row groups per thread in large calls
+constexpr int64_t BULK_BLOCKS = 16384;      // blocks of QG_BULK groups from which to use them
 
 struct QuantArgs {
     uint8_t* kv;
@@ -44,98 +53,129 @@ struct QuantArgs {
     float wv_scale;
 };
 
-__device__ __forceinline__ void load16(const float* p, float* x) {
+__device__ __forceinline__ void load16(const float* p, float4* x) {
     const float4* p4 = reinterpret_cast<const float4*>(p);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        float4 t = p4[i];
-        x[4 * i] = t.x;
-        x[4 * i + 1] = t.y;
-        x[4 * i + 2] = t.z;
-        x[4 * i + 3] = t.w;
-    }
+    for (int i = 0; i < 4; ++i) x[i] = p4[i];
+}
+
+__device__ __forceinline__ float elem(const float4* x, int i) {
+    const float4 t = x[i >> 2];
+    return (i & 3) == 0 ? t.x : (i & 3) == 1 ? t.y : (i & 3) == 2 ? t.z : t.w;
+}
+
+__device__ __forceinline__ uint32_t fp8_word(float4 x, float scale) {
+    return e4m3_encode(x.x / scale) | (e4m3_encode(x.y / scale) << 8) |
+           (e4m3_encode(x.z / scale) << 16) | (e4m3_encode(x.w / scale) << 24);
 }
 
 // 16 channels -> 16 E4M3 bytes of x/scale.
-__device__ __forceinline__ uint4 fp8_group(const float* x, float scale) {
-    uint32_t w[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        w[i] = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w[i] |= e4m3_encode(x[4 * i + j] / scale) << (8 * j);
-    }
-    return make_uint4(w[0], w[1], w[2], w[3]);
+__device__ __forceinline__ uint4 fp8_group(const float4* x, float scale) {
+    return make_uint4(fp8_word(x[0], scale), fp8_word(x[1], scale), fp8_word(x[2], scale),
+                      fp8_word(x[3], scale));
 }
 
-__device__ __forceinline__ bool row_target(const QuantArgs& a, int64_t row, int64_t& dst) {
-    int32_t s = a.seq[row];
-    int64_t p = a.pos[row];
+// Cache row of (s, p), or false when the row is skipped (s or p out of range).
+__device__ __forceinline__ bool row_target(const QuantArgs& a, int32_t s, int64_t p, int64_t& dst) {
     if (s < 0 || s >= a.n_seq || p < 0 || p >= a.cap) return false;
     dst = a.pm.table ? cache_row<true>(a.pm, a.cap, s, p) : cache_row<false>(a.pm, a.cap, s, p);
     return true;
 }
 
+// Row g of the thread, clamped to the last row: loads need no branch (a branch
+// around a load makes the compiler wait for every load in flight at the join);
+// rows past n are loaded again from row n-1 and never stored.
+__device__ __forceinline__ int64_t load_row(const QuantArgs& a, int64_t row0, int g) {
+    const int64_t row = row0 + g * ROWS_GROUP;
+    return row < a.n ? row : a.n - 1;
+}
+
+// seq and pos of the thread's rows, loaded before anything else so that no later
+// wait for them also waits for the row data behind them.
+template <int QG>
+__device__ __forceinline__ void load_rows(const QuantArgs& a, int64_t row0, int32_t* sq,
+                                          int64_t* ps) {
+#pragma unroll
+    for (int g = 0; g < QG; ++g) {
+        const int64_t row = load_row(a, row0, g);
+        sq[g] = a.seq[row];
+        ps[g] = a.pos[row];
+    }
+}
+
+template <int QG>
 __global__ void __launch_bounds__(QTHREADS) quantize_kernel(QuantArgs a) {
     const int part = blockIdx.y;
     const int t = threadIdx.x;
-    if (part == 1) {
-        // indexer keys: channels 4u .. 4u+3 of the row
-        const int64_t row = (int64_t)blockIdx.x * ROWS_MAIN + t / 16;
-        const int u = t & 15;
-        int64_t dst;
-        if (!a.idx_k || row >= a.n || !row_target(a, row, dst)) return;
-        const float4 x = *reinterpret_cast<const float4*>(a.idx_k + row * IDX_DIM + 4 * u);
-        const float sc = a.idxk_scale;
-        const uint32_t w = e4m3_encode(x.x / sc) | (e4m3_encode(x.y / sc) << 8) |
-                           (e4m3_encode(x.z / sc) << 16) | (e4m3_encode(x.w / sc) << 24);
-        *reinterpret_cast<uint32_t*>(a.idxk + dst * IDX_DIM + 4 * u) = w;
-        return;
-    }
-    int64_t row = (int64_t)blockIdx.x * ROWS_MAIN + t / 16;
-    int u = t & 15;
-    int64_t dst = 0;
-    bool ok = row < a.n && row_target(a, row, dst);
+    const int u = t & 15;
+    const int64_t row0 = (int64_t)blockIdx.x * (ROWS_GROUP * QG) + t / 16;
+    int32_t sq[QG];
+    int64_t ps[QG];
+    float4 x[QG][4];
     if (part == 0) {
-        float x[16];
-        uint32_t sc = 0, lo = 0, hi = 0;
-        if (ok) {
-            const float* src = (u < 8 ? a.k : a.v) + row * D + 16 * (u & 7);
-            load16(src, x);
-            float amax = 0.0f;
+        load_rows<QG>(a, row0, sq, ps);
+        float4 ik[QG];
 #pragma unroll
-            for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
-            sc = e4m3_encode(amax / 6.0f);          // amax >= 0: positive code
-            float s = e4m3_value_pos(sc);
+        for (int g = 0; g < QG; ++g)
+            load16((u < 8 ? a.k : a.v) + load_row(a, row0, g) * D + 16 * (u & 7), x[g]);
+        if (a.idx_k) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                uint32_t nib = e2m1_mag(fabsf(x[i]), s) | ((__float_as_uint(x[i]) >> 28) & 8u);
-                if (i < 8) lo |= nib << (4 * i);
-                else hi |= nib << (4 * (i - 8));
-            }
+            for (int g = 0; g < QG; ++g)
+                ik[g] = *reinterpret_cast<const float4*>(a.idx_k + load_row(a, row0, g) * IDX_DIM +
+                                                         4 * u);
         }
-        // gather the 4 scale bytes of lanes u..u+3 (u % 4 == 0) into one dword
-        uint32_t word = sc << (8 * (u & 3));
-        word |= (uint32_t)__builtin_amdgcn_mov_dpp((int)word, DPP_XOR1, 0xf, 0xf, false);
-        word |= (uint32_t)__builtin_amdgcn_mov_dpp((int)word, DPP_XOR2, 0xf, 0xf, false);
-        if (!ok) return;
-        uint8_t* rec = a.kv + dst * RECORD;
-        *reinterpret_cast<uint2*>(rec + 8 * u) = make_uint2(lo, hi);   // K codes, then V
-        if ((u & 3) == 0) *reinterpret_cast<uint32_t*>(rec + 128 + u) = word;
+#pragma unroll
+        for (int g = 0; g < QG; ++g) {
+            const int64_t row = row0 + g * ROWS_GROUP;
+            int64_t dst = 0;
+            const bool ok = row < a.n && row_target(a, sq[g], ps[g], dst);
+            uint32_t sc = 0, lo = 0, hi = 0;
+            if (ok) {
+                float amax = 0.0f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(elem(x[g], i)));
+                sc = e4m3_encode(amax / 6.0f);      // amax >= 0: positive code
+                const float sv = e4m3_value_pos(sc);
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    const float xi = elem(x[g], i);
+                    const uint32_t nib = e2m1_mag(fabsf(xi), sv) | ((__float_as_uint(xi) >> 28) & 8u);
+                    if (i < 8) lo |= nib << (4 * i);
+                    else hi |= nib << (4 * (i - 8));
+                }
+            }
+            // gather the 4 scale bytes of lanes u..u+3 (u % 4 == 0) into one dword
+            uint32_t word = sc << (8 * (u & 3));
+            word |= (uint32_t)__builtin_amdgcn_mov_dpp((int)word, DPP_XOR1, 0xf, 0xf, false);
+            word |= (uint32_t)__builtin_amdgcn_mov_dpp((int)word, DPP_XOR2, 0xf, 0xf, false);
+            if (!ok) continue;
+            uint8_t* rec = a.kv + dst * RECORD;
+            *reinterpret_cast<uint2*>(rec + 8 * u) = make_uint2(lo, hi);   // K codes, then V
+            if ((u & 3) == 0) *reinterpret_cast<uint32_t*>(rec + 128 + u) = word;
+            if (a.idx_k)
+                *reinterpret_cast<uint32_t*>(a.idxk + dst * IDX_DIM + 4 * u) =
+                    fp8_word(ik[g], a.idxk_scale);
+        }
         return;
     }
     // window rows of layer l
-    if (!ok) return;
-    const int l = part - 2;
+    const int l = part - 1;
     const int64_t n = a.n;
-    const float* src = (u < 8 ? a.win_k : a.win_v) + ((int64_t)l * n + row) * D + 16 * (u & 7);
-    float x[16];
-    load16(src, x);
-    int64_t p = a.pos[row];
-    int32_t s = a.seq[row];
-    int64_t slot = (((int64_t)l * a.n_seq + s) * a.w_cap + p % a.w_cap) * D + 16 * (u & 7);
-    uint8_t* dstp = (u < 8 ? a.wk : a.wv) + slot;
-    *reinterpret_cast<uint4*>(dstp) = fp8_group(x, u < 8 ? a.wk_scale : a.wv_scale);
+    load_rows<QG>(a, row0, sq, ps);
+#pragma unroll
+    for (int g = 0; g < QG; ++g)
+        load16((u < 8 ? a.win_k : a.win_v) + ((int64_t)l * n + load_row(a, row0, g)) * D +
+                   16 * (u & 7), x[g]);
+#pragma unroll
+    for (int g = 0; g < QG; ++g) {
+        const int64_t row = row0 + g * ROWS_GROUP;
+        const int32_t s = sq[g];
+        const int64_t p = ps[g];
+        if (row >= n || s < 0 || s >= a.n_seq || p < 0 || p >= a.cap) continue;
+        const int64_t slot = (((int64_t)l * a.n_seq + s) * a.w_cap + p % a.w_cap) * D + 16 * (u & 7);
+        uint8_t* dstp = (u < 8 ? a.wk : a.wv) + slot;
+        *reinterpret_cast<uint4*>(dstp) = fp8_group(x[g], u < 8 ? a.wk_scale : a.wv_scale);
+    }
 }
 
 }  // namespace
@@ -159,18 +199,22 @@ hipError_t launch_quantize(const csa2_cache& c, const csa2_window* w, const floa
     a.pm = page_map(c);
     a.n_seq = c.n_seq;
     a.idxk_scale = c.idxk_scale;
-    int parts = idx_k ? 2 : 1;
+    int parts = 1;
     if (win_k) {
         a.wk = w->k;
         a.wv = w->v;
         a.w_cap = w->w_cap;
         a.wk_scale = w->k_scale;
         a.wv_scale = w->v_scale;
-        parts = 2 + w->n_layers;
+        parts = 1 + w->n_layers;
     }
-    // with windows but no indexer input, part 1 blocks exit at once
-    const dim3 grid((unsigned)((n + ROWS_MAIN - 1) / ROWS_MAIN), parts);
-    hipLaunchKernelGGL(quantize_kernel, grid, dim3(QTHREADS), 0, stream, a);
+    const int64_t bulk_blocks = (n + ROWS_GROUP * QG_BULK - 1) / (ROWS_GROUP * QG_BULK);
+    if (bulk_blocks >= BULK_BLOCKS)
+        hipLaunchKernelGGL(quantize_kernel<QG_BULK>, dim3((unsigned)bulk_blocks, parts),
+                           dim3(QTHREADS), 0, stream, a);
+    else
+        hipLaunchKernelGGL(quantize_kernel<1>, dim3((unsigned)((n + ROWS_GROUP - 1) / ROWS_GROUP), parts),
+                           dim3(QTHREADS), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -14,7 +14,7 @@ import pytest
 
 import oracle as O
 from fp4_kv_cache_decode_amd import datagen as G
-from parity import ATTN_TOL, block_scores, check_index_set, fill_both
+from parity import ATTN_TOL, block_scores, check_index_set, fill_both, shuffled_pages, unpage
 
 pytestmark = pytest.mark.gpu
 
@@ -110,6 +110,50 @@ def test_quantize_all_e4m3_inputs(K):
                   dev(np.arange(n, dtype=np.int64)), idx_k=dev(ik))
     torch.cuda.synchronize()
     assert np.array_equal(gc.idxk.cpu().numpy(), oc.idxk)
+
+
+@pytest.mark.parametrize("P", [0, 256])
+def test_quantize_bulk_call_bit_exact(K, P):
+    """One call of 1,048,613 rows, the size from which the kernel gives each thread
+    four row groups: a ragged last block, destinations scattered over two sequences
+    (P > 0: over a shuffled page pool), 64 rows with seq or pos out of range, one
+    window layer (w_cap = cap, so no two rows share a slot), non-unit scales.  The
+    rows in range must equal the oracle's bytes; the rest must leave no trace."""
+    n, n_seq, cap = (1 << 20) + 37, 2, 1 << 20
+    _say(f"quantize bulk n={n} P={P}")
+    rng = np.random.default_rng(20 + P)
+    k = _adversarial_rows(n, rng)
+    v = _adversarial_rows(n, rng)[::-1].copy()
+    ik = (rng.standard_normal((n, 64)) * 40).astype(np.float32)
+    wk = (rng.standard_normal((1, n, 128)) * 20).astype(np.float32)
+    wv = (rng.standard_normal((1, n, 128)) * 3).astype(np.float32)
+    dst = rng.choice(n_seq * cap, n, replace=False)
+    seq, pos = (dst // cap).astype(np.int32), (dst % cap).astype(np.int64)
+    bad = rng.choice(n, 64, replace=False)
+    seq[bad[:16]], seq[bad[16:32]] = -1, n_seq
+    pos[bad[32:48]], pos[bad[48:]] = cap, -1
+    good = np.setdiff1d(np.arange(n), bad)
+    scales = (0.37, 1.7, 0.5)
+    oc = O.Cache(n_seq, cap, 1, cap, *scales)
+    oc.quantize(k[good], v[good], ik[good], wk[:, good], wv[:, good], seq[good], pos[good])
+    if P:
+        table, n_pages = shuffled_pages(7, n_seq, cap, P, [cap] * n_seq)
+        gc = K.Cache(n_seq, cap, 1, cap, *scales, page_tokens=P, n_pages=n_pages,
+                     page_table=torch.from_numpy(table))
+    else:
+        gc = K.Cache(n_seq, cap, 1, cap, *scales)
+    K.quantize_kv(gc, dev(k), dev(v), dev(seq), dev(pos), idx_k=dev(ik), win_k=dev(wk),
+                  win_v=dev(wv))
+    torch.cuda.synchronize()
+    kv, idxk = gc.kv.cpu().numpy(), gc.idxk.cpu().numpy()
+    if P:
+        unowned = np.setdiff1d(np.arange(gc.n_pages), table[table >= 0])
+        assert not kv[unowned].any() and not idxk[unowned].any()
+        kv, idxk = unpage(kv, table, P, cap), unpage(idxk, table, P, cap)
+    assert np.array_equal(kv, oc.kv)
+    assert np.array_equal(idxk, oc.idxk)
+    assert np.array_equal(gc.wk.cpu().numpy(), oc.wk)
+    assert np.array_equal(gc.wv.cpu().numpy(), oc.wv)
 
 
 # ----------------------------------------------------------------- indexer
