@@ -194,6 +194,73 @@ void oracle_quantize_kv(uint8_t* kv, uint8_t* idxk, float idxk_scale, int64_t ca
     (void)n_seq;
 }
 
+/* Global-KV compression m (origotech.dev deep dive, section "How the
+ * architecture shrinks the KV cache": the encoder's CSA2 layers run at
+ * compression m = 2, the decoder's at m = 1).  The pages give the ratio, not
+ * the operator.  Reading taken here: global entry e of a sequence stands for
+ * its m tokens at positions m*e .. m*e + m - 1, and its K, V and indexer-key
+ * rows are those tokens' rows averaged in fp32 (the sum in position order,
+ * then times 1/m; for m = 2 that is one rounding of the sum and an exact
+ * halving), then quantised exactly as a token row is.  The window keeps every
+ * token.
+ *
+ * Input rows i*m .. i*m + m - 1 form group i (n must be a multiple of m); the
+ * group's entry is pos[i*m] / m of sequence seq[i*m], and a group whose first
+ * position is not a multiple of m is skipped.  Window rows are written for
+ * every token at its own position, as in oracle_quantize_kv.  m = 1 writes the
+ * same bytes as oracle_quantize_kv. */
+static void mean_rows(const float* x, int32_t m, int dim, float* out) {
+    int c, j;
+    for (c = 0; c < dim; ++c) {
+        float acc = x[c];
+        for (j = 1; j < m; ++j) acc = acc + x[(int64_t)j * dim + c];
+        out[c] = acc * (1.0f / (float)m);
+    }
+}
+
+void oracle_compress_kv(uint8_t* kv, uint8_t* idxk, float idxk_scale, int64_t cap,
+                        int32_t n_seq, uint8_t* wk, uint8_t* wv, float wk_scale,
+                        float wv_scale, int32_t w_cap, int32_t n_layers,
+                        const float* k, const float* v, const float* idx_k,
+                        const float* win_k, const float* win_v, const int32_t* seq,
+                        const int64_t* pos, int64_t n, int32_t m) {
+    int64_t g, i;
+#pragma omp parallel for schedule(static)
+    for (g = 0; g < n / m; ++g) {
+        const int64_t i0 = g * m;
+        float xk[OR_D], xv[OR_D], xi[OR_DI];
+        int64_t row;
+        uint8_t* rec;
+        int c;
+        if (pos[i0] % m != 0) continue;
+        row = (int64_t)seq[i0] * cap + pos[i0] / m;
+        rec = kv + row * OR_REC;
+        mean_rows(k + i0 * OR_D, m, OR_D, xk);
+        mean_rows(v + i0 * OR_D, m, OR_D, xv);
+        fp4_vector(xk, OR_D, rec, rec + 128);
+        fp4_vector(xv, OR_D, rec + 64, rec + 136);
+        if (idx_k && idxk) {
+            mean_rows(idx_k + i0 * OR_DI, m, OR_DI, xi);
+            for (c = 0; c < OR_DI; ++c)
+                idxk[row * OR_DI + c] = oracle_e4m3_encode(xi[c] / idxk_scale);
+        }
+    }
+    if (!(win_k && wk)) return;
+#pragma omp parallel for schedule(static)
+    for (i = 0; i < n; ++i) {
+        int c, l;
+        for (l = 0; l < n_layers; ++l) {
+            int64_t slot = (((int64_t)l * n_seq + seq[i]) * w_cap + pos[i] % w_cap) * OR_D;
+            const float* xk = win_k + ((int64_t)l * n + i) * OR_D;
+            const float* xv = win_v + ((int64_t)l * n + i) * OR_D;
+            for (c = 0; c < OR_D; ++c) {
+                wk[slot + c] = oracle_e4m3_encode(xk[c] / wk_scale);
+                wv[slot + c] = oracle_e4m3_encode(xv[c] / wv_scale);
+            }
+        }
+    }
+}
+
 /* ------------------------------------------------------------------ indexer */
 
 /* score_t = sum_h w_h * max(0, q_h . khat_t), khat = E4M3(code) * scale, fp64. */
