@@ -705,6 +705,157 @@ def row_prefill(args):
                    roof, cpu)
 
 
+def row_encoder(args):
+    """The encoder side of CSA2 on one prefill chunk: 8,192 causal tokens after a
+    131,072-token prefix through the 20 encoder layers -- layers 1-2 sliding
+    window only, then 3 x [Full + 5 Reuse] at global-KV compression m = 2, each
+    Full layer with its own store of 2-token entries (65,536 + 4,096 of them).
+    A step writes the chunk (csa2_compress_kv: each group's entries and every
+    layer's window rows), then runs every layer's indexer and attention for all
+    8,192 queries (query i: ctx_i = 131,073 + i tokens, ctx_i // 2 entries)."""
+    import torch
+    import fp4_kv_cache_decode_amd.csa2 as K
+    from fp4_kv_cache_decode_amd import datagen as G
+    wl = G.WORKLOADS["encoder20_m2_chunk8k_over_128k"]
+    B, N0, m = wl.B, wl.N, wl.m
+    cap_c = wl.cap // m
+    groups = [i for i, x in enumerate(wl.layers) if x == "F"]
+    swa = [i for i, x in enumerate(wl.layers) if x == "S"]
+    span = [list(range(f, f + 6)) for f in groups]          # a group's 6 layers
+    # the window stores of a group's layers live with its global store; the
+    # window-only layers' with the first group's
+    wins = [swa + span[0]] + span[1:]
+    t0 = time.time()
+    dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    want_cpu = not args.no_cpu_baseline
+    if want_cpu:
+        import oracle as O
+    zeros = lambda n: np.zeros(n, np.int32)
+    w_lo = N0 - G.WINDOW
+
+    def windows(layers, p0, p1):
+        rows = [G.window_rows(args.seed, l, 0, p0, p1) for l in layers]
+        return np.stack([r[0] for r in rows]), np.stack([r[1] for r in rows])
+
+    # one global store per group, with its layers' window stores
+    gcs, ocs = [], []
+    for gi, ls in enumerate(wins):
+        gc = K.Cache(1, cap_c, len(ls), wl.w_cap)
+        oc = O.Cache(1, cap_c, len(ls), wl.w_cap) if want_cpu else None
+        for p in range(0, N0, G.CHUNK):
+            k, v, ik = G.kv_rows(args.seed, 0, p, p + G.CHUNK, gi)
+            pos = np.arange(p, p + G.CHUNK, dtype=np.int64)
+            K.compress_kv(gc, dev(k), dev(v), dev(zeros(G.CHUNK)), dev(pos), m, idx_k=dev(ik))
+            if oc is not None:
+                oc.compress(k, v, ik, None, None, zeros(G.CHUNK), pos, m)
+        wk, wv = windows(ls, w_lo, N0)
+        pos = np.arange(w_lo, N0, dtype=np.int64)
+        K.compress_kv(gc, None, None, dev(zeros(G.WINDOW)), dev(pos), m, win_k=dev(wk),
+                      win_v=dev(wv))
+        if oc is not None:
+            oc.compress(None, None, None, wk, wv, zeros(G.WINDOW), pos, m)
+        gcs.append(gc)
+        ocs.append(oc)
+    log(f"[bench] encoder prefixes built ({time.time() - t0:.1f}s)")
+
+    # the chunk's rows, written inside every timed step
+    cpos = np.arange(N0, N0 + B, dtype=np.int64)
+    chunk = []
+    for gi, ls in enumerate(wins):
+        k, v, ik = G.kv_rows(args.seed, 0, N0, N0 + B, gi)
+        wk, wv = windows(ls, N0, N0 + B)
+        chunk.append(dict(k=dev(k), v=dev(v), ik=dev(ik), wk=dev(wk), wv=dev(wv)))
+        if ocs[gi] is not None:
+            ocs[gi].compress(k, v, ik, wk, wv, zeros(B), cpos, m)
+    seq_np, ctx_np = wl.seq(), wl.ctx()
+    ctxc_np = ctx_np // m
+    seq, ctx, ctxc, pos_t = dev(seq_np), dev(ctx_np), dev(ctxc_np), dev(cpos)
+    iq = [G.index_queries(args.seed, f, B) for f in groups]
+    qi = [(dev(a), dev(b)) for a, b in iq]
+    q_np = [G.attn_queries(args.seed, l, B) for l in range(len(wl.layers))]
+    q = [dev(x) for x in q_np]
+    none = torch.full((B, G.TOPK), -1, dtype=torch.int32, device="cuda")
+    M = torch.empty((B, K.block_stride(cap_c)), dtype=torch.float32, device="cuda")
+    pool = torch.empty((B, G.N_BLOCKS), dtype=torch.int32, device="cuda")
+    idx = torch.empty((B, G.TOPK), dtype=torch.int32, device="cuda")
+    kvg = torch.empty((B, G.TOPK, 144), dtype=torch.uint8, device="cuda")
+    out = torch.empty((len(wl.layers), B, G.H, G.D), dtype=torch.float32, device="cuda")
+    ws_sel = K.alloc_workspace(K.OP_SELECT_POOL, B, cap_c)
+    ws_ri = K.alloc_workspace(K.OP_INDEX_REINDEX, B)
+    ws_at = K.alloc_workspace(K.OP_DECODE_ATTN, B)
+    torch.cuda.synchronize()
+    log(f"[bench] encoder inputs ready ({time.time() - t0:.1f}s)")
+
+    scan_ev = []
+
+    def step(i, timed=False):
+        for gi in range(len(wins)):
+            c = chunk[gi]
+            K.compress_kv(gcs[gi], c["k"], c["v"], seq, pos_t, m, idx_k=c["ik"], win_k=c["wk"],
+                          win_v=c["wv"])
+        for l in swa:
+            K.decode_attn(gcs[0], wins[0].index(l), q[l], none, seq, ctx, out[l], ws_at)
+        for gi, ls in enumerate(span):
+            if timed:
+                e = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                e[0].record()
+            K.index_block_scores(gcs[gi], qi[gi][0], qi[gi][1], seq, ctxc, cap_c, M)
+            if timed:
+                e[1].record()
+                scan_ev.append(e)
+            K.index_select_pool(M, ctxc, cap_c, pool, ws_sel)
+            K.index_reindex(gcs[gi], qi[gi][0], qi[gi][1], seq, ctxc, pool, idx, ws_ri)
+            for j, l in enumerate(ls):
+                K.decode_attn(gcs[gi], wins[gi].index(l), q[l], idx, seq, ctx, out[l], ws_at,
+                              kvg_out=kvg if j == 0 else None, kvg_in=kvg if j else None)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    for i in range(args.steps):
+        step(i, timed=True)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t1) * 1e3 / args.steps
+    scan_ms = sum(a.elapsed_time(b) for a, b in scan_ev) / args.steps    # the 3 scans of a step
+    key_evals = int(ctxc_np.sum()) * len(groups)
+    flops = 2 * G.HI * G.DI * key_evals
+    tfs = flops / (scan_ms * 1e-3) / 1e12
+    log(f"[bench] encoder chunk {ms:.2f} ms, scans {scan_ms:.2f} ms = {tfs:.1f} TFLOP/s")
+    cpu = None
+    if want_cpu:
+        # a strided sample of the chunk's queries through the oracle: every
+        # layer's indexer and attention
+        sample = np.arange(0, B, 16)
+        ss, sx, sxc = seq_np[sample], ctx_np[sample], ctxc_np[sample]
+        nn = np.full((sample.size, G.TOPK), -1, np.int32)
+        ts = time.perf_counter()
+        for l in swa:
+            ocs[0].decode_attn(wins[0].index(l), q_np[l][sample], nn, ss, sx)
+        for gi, ls in enumerate(span):
+            _, oidx, _, _ = ocs[gi].index_full(iq[gi][0][sample], iq[gi][1][sample], ss, sxc)
+            for l in ls:
+                ocs[gi].decode_attn(wins[gi].index(l), q_np[l][sample], oidx, ss, sx)
+        secs = time.perf_counter() - ts
+        threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        cpu = {"value": sample.size / secs, "unit": "queries/s", "cores": threads,
+               "kind": "oracle",
+               "sample": f"{sample.size} of the chunk's 8,192 queries (every 16th) through "
+                         f"the fp64 C oracle's indexers and all 20 layers' attention, "
+                         f"{secs:.1f} s wall"}
+    cfg = {"workload": wl.name, "queries": B, "prefix": N0, "compression": m,
+           "layers": "".join(wl.layers), "topk": G.TOPK, "pool_blocks": G.N_BLOCKS,
+           "window": G.WINDOW, "key_evals": key_evals, "dtype": "fp32"}
+    roof = {"bound": "alu", "achieved": tfs, "peak": PEAK_FP32_TFS, "unit": "TFLOP/s",
+            "frac": tfs / PEAK_FP32_TFS,
+            "traffic": row_counter_traffic("encoder_chunk8k_m2_kernel_stats.txt",
+                                           "encoder20_m2_chunk8k_over_128k"),
+            "kernel": "scan_kernel (csa2_index_block_scores), the three Full layers' scans",
+            "avg_us": scan_ms * 1e3, "flops": flops}
+    return _common(args, "CSA2 encoder-chunk queries/s (m = 2)", B / (ms * 1e-3), "queries/s",
+                   ms, cfg, roof, cpu)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -722,12 +873,14 @@ def main():
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
     ap.add_argument("--row", default="decode",
-                    choices=["decode", "quantize", "gather", "prefill", "reindex_layer"],
+                    choices=["decode", "quantize", "gather", "prefill", "reindex_layer",
+                             "encoder"],
                     help="decode: the whole decode step (default); quantize: bulk quantise-on-write "
                          "of the 1M-context cache; gather: gather/dequant/attention at B=1024; "
                          "prefill: the 8,192-query chunk over a 131,072-token prefix; "
                          "reindex_layer: one Reindex layer, separate calls against the fused "
-                         "cooperative launch")
+                         "cooperative launch; encoder: the 20 encoder layers (CSA2 at "
+                         "compression 2) on the same chunk")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -745,7 +898,7 @@ def main():
         return
     if args.row != "decode":
         res = {"quantize": row_quantize, "gather": row_gather, "prefill": row_prefill,
-               "reindex_layer": row_reindex_layer}[args.row](args)
+               "reindex_layer": row_reindex_layer, "encoder": row_encoder}[args.row](args)
         print(json.dumps(res), flush=True)
         return
 

@@ -53,6 +53,8 @@ def lib():
         L = C.CDLL(LIB_PATH)
         L.csa2_quantize_kv.argtypes = [C.POINTER(csa2_cache), C.POINTER(csa2_window), _P, _P, _P,
                                        _P, _P, _P, _P, C.c_int64, _P]
+        L.csa2_compress_kv.argtypes = [C.POINTER(csa2_cache), C.POINTER(csa2_window), _P, _P, _P,
+                                       _P, _P, _P, _P, C.c_int64, C.c_int32, _P]
         L.csa2_index_full.argtypes = [C.POINTER(csa2_cache), _P, _P, _P, _P, C.c_int32, C.c_int64,
                                       C.c_int32, C.c_int32, C.c_int32, _P, _P, _P, C.c_size_t, _P]
         L.csa2_index_reindex.argtypes = [C.POINTER(csa2_cache), _P, _P, _P, _P, C.c_int32, _P,
@@ -79,7 +81,7 @@ def lib():
         L.csa2_workspace_bytes.restype = C.c_size_t
         L.csa2_status_string.argtypes = [C.c_int]
         L.csa2_status_string.restype = C.c_char_p
-        for f in ("csa2_quantize_kv", "csa2_index_full", "csa2_index_reindex",
+        for f in ("csa2_quantize_kv", "csa2_compress_kv", "csa2_index_full", "csa2_index_reindex",
                   "csa2_decode_attn", "csa2_decode_attn_ex", "csa2_index_block_scores",
                   "csa2_index_select_pool", "csa2_decode_attn_noalloc",
                   "csa2_reindex_layer_fused"):
@@ -185,6 +187,28 @@ def quantize_kv(cache: Cache, k, v, seq, pos, idx_k=None, win_k=None, win_v=None
                                 _ptr(idx_k), _ptr(win_k), _ptr(win_v), _ptr(seq), _ptr(pos), n,
                                 _stream(stream))
     _check(st, "csa2_quantize_kv")
+
+
+def compress_kv(cache: Cache, k, v, seq, pos, m: int, idx_k=None, win_k=None, win_v=None,
+                stream=None) -> None:
+    """csa2_compress_kv: n tokens; rows i*m .. i*m+m-1 become global entry
+    pos[i*m] / m (their fp32 mean, quantised); window rows for every token.
+    k = v = None: window rows only."""
+    n = win_k.shape[1] if k is None else k.shape[0]
+    if k is not None or v is not None:
+        _need(k, torch.float32, (n, D), "k")
+        _need(v, torch.float32, (n, D), "v")
+    _need(seq, torch.int32, (n,), "seq")
+    _need(pos, torch.int64, (n,), "pos")
+    if idx_k is not None:
+        _need(idx_k, torch.float32, (n, IDX_DIM), "idx_k")
+    if win_k is not None:
+        _need(win_k, torch.float32, (cache.n_layers, n, D), "win_k")
+        _need(win_v, torch.float32, (cache.n_layers, n, D), "win_v")
+    st = lib().csa2_compress_kv(C.byref(cache.c), C.byref(cache.w), _ptr(k), _ptr(v),
+                                _ptr(idx_k), _ptr(win_k), _ptr(win_v), _ptr(seq), _ptr(pos), n,
+                                m, _stream(stream))
+    _check(st, "csa2_compress_kv")
 
 
 def index_full(cache: Cache, q_idx, w, seq, ctx, max_ctx: int, pool, idx, ws,

@@ -139,7 +139,9 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
     const int c = lane & 15, g = lane >> 4;
     const int j = c >> 1, o = c & 1, m = 4 * o + g;    // V: entries 2j, 2j+1, channel group m
     const int32_t s = a.seq[b];
-    const int64_t N = clamp64(a.ctx[b], 0, a.cap);
+    // tokens of context (window [N - 128, N)); main entries below min(N, cap)
+    const int64_t N = clamp64(a.ctx[b], 0, CTX_TOKENS_MAX);
+    const int64_t n_main = N < a.cap ? N : a.cap;
     const bool seq_ok = s >= 0 && s < a.n_seq;
     const int64_t u0 = N > WINDOW ? N - WINDOW : 0;
     const int32_t slot0 = window_slot(u0, a.w_cap);         // window slot of position u0
@@ -151,7 +153,7 @@ __global__ void __launch_bounds__(AT_THREADS, 4) attn_stream_kernel(StreamArgs a
     const int main_end = t_end < a.n_sub_main ? t_end : a.n_sub_main;
     const int32_t* idx_row = a.idx + (int64_t)b * a.topk;
     // valid main positions are [0, n_ok) and valid window entries [0, w_ok)
-    const uint32_t n_ok = seq_ok ? (uint32_t)(N < INT32_MAX ? N : INT32_MAX) : 0u;
+    const uint32_t n_ok = seq_ok ? (uint32_t)(n_main < INT32_MAX ? n_main : INT32_MAX) : 0u;
     const int w_ok = seq_ok ? (int)(N - u0) : 0;
     // uniform bases: the sequence's first record, the query's gathered records
     // and its window rows

@@ -26,6 +26,8 @@ constexpr int OROW = D + 4;
 // tile kernel (small batches): used while B x tiles fits one wave of workgroups
 constexpr int64_t TILE_KERNEL_MAX_WG = 768;
 constexpr int TILE = 64;
+// largest context length (tokens) an attention call takes from ctx[]
+constexpr int64_t CTX_TOKENS_MAX = (int64_t)1 << 40;
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 
@@ -273,9 +275,13 @@ __device__ __forceinline__ void tile_body(const TileArgs& a, AttnShared& sh, int
     int32_t pos = -1;
     if (is_main && e0 + c < a.topk) pos = a.idx[(int64_t)b * a.topk + e0 + c];
     const int32_t s = a.seq[b];
-    const int64_t N = clamp64(a.ctx[b], 0, a.cap);
+    // N counts tokens (the window is [N - 128, N)); main entries are valid below
+    // min(N, cap), which also keeps every record load inside the store (with a
+    // compressed store N exceeds the entries, and the indices stay below N / m)
+    const int64_t N = clamp64(a.ctx[b], 0, CTX_TOKENS_MAX);
+    const int64_t n_main = N < a.cap ? N : a.cap;
     const bool seq_ok = s >= 0 && s < a.n_seq;
-    const uint32_t n_ok = seq_ok ? (uint32_t)(N < INT32_MAX ? N : INT32_MAX) : 0u;
+    const uint32_t n_ok = seq_ok ? (uint32_t)(n_main < INT32_MAX ? n_main : INT32_MAX) : 0u;
 
     // ---- per kind of tile: the record (or window row) loads, the query's
     // staging while they are in flight, then the dequantisation.  Each branch

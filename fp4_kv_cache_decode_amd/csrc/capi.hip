@@ -182,13 +182,17 @@ size_t csa2_workspace_bytes(int32_t op, int32_t B, int64_t max_ctx, int32_t n_bl
     return 0;
 }
 
-csa2_status csa2_quantize_kv(const csa2_cache* cache, const csa2_window* win, const float* k,
+csa2_status csa2_compress_kv(const csa2_cache* cache, const csa2_window* win, const float* k,
                              const float* v, const float* idx_k, const float* win_k,
                              const float* win_v, const int32_t* seq, const int64_t* pos,
-                             int64_t n, hipStream_t stream) {
+                             int64_t n, int32_t m, hipStream_t stream) {
     csa2_status st = check_cache(cache, true, idx_k != nullptr);
     if (st != CSA2_OK) return st;
-    if (!k || !v || !seq || !pos || n < 0) return CSA2_ERR_INVALID_ARG;
+    if (!seq || !pos || n < 0) return CSA2_ERR_INVALID_ARG;
+    if (m != 1 && m != 2) return CSA2_ERR_UNSUPPORTED;
+    if ((k == nullptr) != (v == nullptr)) return CSA2_ERR_INVALID_ARG;
+    if (!k && (idx_k || !win_k)) return CSA2_ERR_INVALID_ARG;   // window only
+    if (k && n % m != 0) return CSA2_ERR_INVALID_ARG;
     if ((win_k == nullptr) != (win_v == nullptr)) return CSA2_ERR_INVALID_ARG;
     if (win_k) {
         st = check_window(win, cache);
@@ -198,7 +202,15 @@ csa2_status csa2_quantize_kv(const csa2_cache* cache, const csa2_window* win, co
     if (n > ((int64_t)1 << 34)) return CSA2_ERR_UNSUPPORTED;
     if (n == 0) return CSA2_OK;
     return launched(csa2::launch_quantize(*cache, win, k, v, idx_k, win_k, win_v, seq, pos, n,
-                                          stream));
+                                          m, stream));
+}
+
+csa2_status csa2_quantize_kv(const csa2_cache* cache, const csa2_window* win, const float* k,
+                             const float* v, const float* idx_k, const float* win_k,
+                             const float* win_v, const int32_t* seq, const int64_t* pos,
+                             int64_t n, hipStream_t stream) {
+    if (!k || !v) return CSA2_ERR_INVALID_ARG;
+    return csa2_compress_kv(cache, win, k, v, idx_k, win_k, win_v, seq, pos, n, 1, stream);
 }
 
 csa2_status csa2_index_full(const csa2_cache* cache, const float* q_idx, const float* w,

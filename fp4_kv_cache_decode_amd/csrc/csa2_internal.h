@@ -24,11 +24,12 @@ inline PageMap page_map(const csa2_cache& c) {
     return m;
 }
 
-// Quantise-on-write of n rows into the cache (and window stores).
+// Quantise-on-write of n rows into the cache (and window stores); with m = 2
+// each pair of rows becomes one global entry from their fp32 mean (n even).
 hipError_t launch_quantize(const csa2_cache& c, const csa2_window* w, const float* k,
                            const float* v, const float* idx_k, const float* win_k,
                            const float* win_v, const int32_t* seq, const int64_t* pos,
-                           int64_t n, hipStream_t stream);
+                           int64_t n, int32_t m, hipStream_t stream);
 
 // Full-context scoring: block maxima M[b][j] for blocks j < ceil(ctx[b]/8).
 hipError_t launch_score_blocks(const csa2_cache& c, const float* q_idx, const float* w,

@@ -19,6 +19,14 @@
 // and pos of its rows first and then all of its row data, before it decides where
 // any row goes: a wait on a destination then never drains the row loads behind
 // it, and the row data is in flight while the destinations are checked.
+//
+// Compression M (M = 2 for the encoder's CSA2 layers, origotech.dev deep dive,
+// section "How the architecture shrinks the KV cache"; this library's reading of
+// the operator): part 0 then covers groups of M consecutive input rows, the
+// tokens at positions M*e .. M*e + M - 1 of one sequence, and writes entry e from
+// the rows' fp32 mean ((r0 + r1) * 0.5: one rounding of the sum, an exact
+// halving); the window parts still write every token.  M = 1 is plain
+// quantise-on-write and compiles to the same code as before the parameter.
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
@@ -44,6 +52,8 @@ struct QuantArgs {
     const int32_t* seq;
     const int64_t* pos;
     int64_t n;
+    int64_t n_main;          // M > 1: groups written to the global store (0: window only)
+    int64_t win_limit;       // M > 1: token positions the window accepts (m * cap)
     int64_t cap;
     PageMap pm;              // page table of a paged cache (table null otherwise)
     int32_t n_seq;
@@ -82,29 +92,62 @@ __device__ __forceinline__ bool row_target(const QuantArgs& a, int32_t s, int64_
     return true;
 }
 
-// Row g of the thread, clamped to the last row: loads need no branch (a branch
-// around a load makes the compiler wait for every load in flight at the join);
-// rows past n are loaded again from row n-1 and never stored.
-__device__ __forceinline__ int64_t load_row(const QuantArgs& a, int64_t row0, int g) {
+// Row (or group) g of the thread, clamped to the last of the n_items: loads need
+// no branch (a branch around a load makes the compiler wait for every load in
+// flight at the join); items past the end are loaded again from the last one
+// and never stored.
+__device__ __forceinline__ int64_t load_row(int64_t n_items, int64_t row0, int g) {
     const int64_t row = row0 + g * ROWS_GROUP;
-    return row < a.n ? row : a.n - 1;
+    return row < n_items ? row : n_items - 1;
 }
 
-// seq and pos of the thread's rows, loaded before anything else so that no later
-// wait for them also waits for the row data behind them.
-template <int QG>
-__device__ __forceinline__ void load_rows(const QuantArgs& a, int64_t row0, int32_t* sq,
-                                          int64_t* ps) {
+// seq and pos of the thread's rows (of the first row of each group of M),
+// loaded before anything else so that no later wait for them also waits for
+// the row data behind them.
+template <int QG, int M>
+__device__ __forceinline__ void load_rows(const QuantArgs& a, int64_t n_items, int64_t row0,
+                                          int32_t* sq, int64_t* ps) {
 #pragma unroll
     for (int g = 0; g < QG; ++g) {
-        const int64_t row = load_row(a, row0, g);
+        const int64_t row = load_row(n_items, row0, g) * M;
         sq[g] = a.seq[row];
         ps[g] = a.pos[row];
     }
 }
 
-template <int QG>
+// 16 floats of group e: the row itself (M = 1) or the fp32 mean of its M rows.
+template <int M>
+__device__ __forceinline__ void load_group16(const float* src, int64_t e, int dim, int off,
+                                             float4* x) {
+    load16(src + e * M * dim + off, x);
+    if (M == 2) {
+        float4 y[4];
+        load16(src + (e * M + 1) * dim + off, y);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            x[i].x = (x[i].x + y[i].x) * 0.5f;
+            x[i].y = (x[i].y + y[i].y) * 0.5f;
+            x[i].z = (x[i].z + y[i].z) * 0.5f;
+            x[i].w = (x[i].w + y[i].w) * 0.5f;
+        }
+    }
+}
+template <int M>
+__device__ __forceinline__ float4 load_group4(const float* src, int64_t e, int dim, int off) {
+    float4 x = *reinterpret_cast<const float4*>(src + e * M * dim + off);
+    if (M == 2) {
+        const float4 y = *reinterpret_cast<const float4*>(src + (e * M + 1) * dim + off);
+        x.x = (x.x + y.x) * 0.5f;
+        x.y = (x.y + y.y) * 0.5f;
+        x.z = (x.z + y.z) * 0.5f;
+        x.w = (x.w + y.w) * 0.5f;
+    }
+    return x;
+}
+
+template <int QG, int M>
 __global__ void __launch_bounds__(QTHREADS) quantize_kernel(QuantArgs a) {
+    static_assert(M == 1 || M == 2, "compression 1 or 2");
     const int part = blockIdx.y;
     const int t = threadIdx.x;
     const int u = t & 15;
@@ -113,22 +156,25 @@ __global__ void __launch_bounds__(QTHREADS) quantize_kernel(QuantArgs a) {
     int64_t ps[QG];
     float4 x[QG][4];
     if (part == 0) {
-        load_rows<QG>(a, row0, sq, ps);
+        // the grid covers the n tokens; part 0 has n_main = n / M groups (none
+        // for a window-only call)
+        const int64_t n_g = M > 1 ? a.n_main : a.n;
+        if (M > 1 && (int64_t)blockIdx.x * (ROWS_GROUP * QG) >= n_g) return;
+        load_rows<QG, M>(a, n_g, row0, sq, ps);
         float4 ik[QG];
 #pragma unroll
         for (int g = 0; g < QG; ++g)
-            load16((u < 8 ? a.k : a.v) + load_row(a, row0, g) * D + 16 * (u & 7), x[g]);
+            load_group16<M>(u < 8 ? a.k : a.v, load_row(n_g, row0, g), D, 16 * (u & 7), x[g]);
         if (a.idx_k) {
 #pragma unroll
             for (int g = 0; g < QG; ++g)
-                ik[g] = *reinterpret_cast<const float4*>(a.idx_k + load_row(a, row0, g) * IDX_DIM +
-                                                         4 * u);
+                ik[g] = load_group4<M>(a.idx_k, load_row(n_g, row0, g), IDX_DIM, 4 * u);
         }
 #pragma unroll
         for (int g = 0; g < QG; ++g) {
             const int64_t row = row0 + g * ROWS_GROUP;
             int64_t dst = 0;
-            const bool ok = row < a.n && row_target(a, sq[g], ps[g], dst);
+            const bool ok = row < n_g && ps[g] % M == 0 && row_target(a, sq[g], ps[g] / M, dst);
             uint32_t sc = 0, lo = 0, hi = 0;
             if (ok) {
                 float amax = 0.0f;
@@ -161,17 +207,19 @@ __global__ void __launch_bounds__(QTHREADS) quantize_kernel(QuantArgs a) {
     // window rows of layer l
     const int l = part - 1;
     const int64_t n = a.n;
-    load_rows<QG>(a, row0, sq, ps);
+    load_rows<QG, 1>(a, n, row0, sq, ps);
 #pragma unroll
     for (int g = 0; g < QG; ++g)
-        load16((u < 8 ? a.win_k : a.win_v) + ((int64_t)l * n + load_row(a, row0, g)) * D +
+        load16((u < 8 ? a.win_k : a.win_v) + ((int64_t)l * n + load_row(n, row0, g)) * D +
                    16 * (u & 7), x[g]);
 #pragma unroll
     for (int g = 0; g < QG; ++g) {
         const int64_t row = row0 + g * ROWS_GROUP;
         const int32_t s = sq[g];
         const int64_t p = ps[g];
-        if (row >= n || s < 0 || s >= a.n_seq || p < 0 || p >= a.cap) continue;
+        // token positions reach m * cap: the global store holds one entry per m
+        const int64_t lim = M > 1 ? a.win_limit : a.cap;
+        if (row >= n || s < 0 || s >= a.n_seq || p < 0 || p >= lim) continue;
         const int64_t slot = (((int64_t)l * a.n_seq + s) * a.w_cap + p % a.w_cap) * D + 16 * (u & 7);
         uint8_t* dstp = (u < 8 ? a.wk : a.wv) + slot;
         *reinterpret_cast<uint4*>(dstp) = fp8_group(x[g], u < 8 ? a.wk_scale : a.wv_scale);
@@ -183,7 +231,7 @@ __global__ void __launch_bounds__(QTHREADS) quantize_kernel(QuantArgs a) {
 hipError_t launch_quantize(const csa2_cache& c, const csa2_window* w, const float* k,
                            const float* v, const float* idx_k, const float* win_k,
                            const float* win_v, const int32_t* seq, const int64_t* pos,
-                           int64_t n, hipStream_t stream) {
+                           int64_t n, int32_t m, hipStream_t stream) {
     QuantArgs a{};
     a.kv = c.kv;
     a.idxk = c.idxk;
@@ -208,13 +256,19 @@ hipError_t launch_quantize(const csa2_cache& c, const csa2_window* w, const floa
         a.wv_scale = w->v_scale;
         parts = 1 + w->n_layers;
     }
+    // k and v null: window rows only (a compressed store gets its entries from
+    // complete groups, the window every token)
+    a.n_main = k ? n / m : 0;
+    a.win_limit = c.cap * m;
     const int64_t bulk_blocks = (n + ROWS_GROUP * QG_BULK - 1) / (ROWS_GROUP * QG_BULK);
-    if (bulk_blocks >= BULK_BLOCKS)
-        hipLaunchKernelGGL(quantize_kernel<QG_BULK>, dim3((unsigned)bulk_blocks, parts),
+    const dim3 small((unsigned)((n + ROWS_GROUP - 1) / ROWS_GROUP), parts);
+    if (m == 2 || !k)
+        hipLaunchKernelGGL((quantize_kernel<1, 2>), small, dim3(QTHREADS), 0, stream, a);
+    else if (bulk_blocks >= BULK_BLOCKS)
+        hipLaunchKernelGGL((quantize_kernel<QG_BULK, 1>), dim3((unsigned)bulk_blocks, parts),
                            dim3(QTHREADS), 0, stream, a);
     else
-        hipLaunchKernelGGL(quantize_kernel<1>, dim3((unsigned)((n + ROWS_GROUP - 1) / ROWS_GROUP), parts),
-                           dim3(QTHREADS), 0, stream, a);
+        hipLaunchKernelGGL((quantize_kernel<1, 1>), small, dim3(QTHREADS), 0, stream, a);
     return hipGetLastError();
 }
 

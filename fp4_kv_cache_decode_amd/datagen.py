@@ -89,12 +89,13 @@ def _rope_inplace(x: np.ndarray, pos: np.ndarray) -> None:
     x[:, 1:ROPE_DIMS:2] = (a * s + b * c).astype(np.float32)
 
 
-def kv_rows(seed: int, seq: int, p0: int, p1: int):
-    """Post-RoPE main K, main V [n,128] and indexer keys [n,64] for positions [p0,p1)."""
-    k = _normal_rows(seed, _K, 0, seq, p0, p1, D)
+def kv_rows(seed: int, seq: int, p0: int, p1: int, group: int = 0):
+    """Post-RoPE main K, main V [n,128] and indexer keys [n,64] for positions [p0,p1).
+    group: which layer group's main KV (each Full layer of the encoder has its own)."""
+    k = _normal_rows(seed, _K, group, seq, p0, p1, D)
     _rope_inplace(k, np.arange(p0, p1))
-    v = _normal_rows(seed, _V, 0, seq, p0, p1, D)
-    ik = _normal_rows(seed, _IDXK, 0, seq, p0, p1, DI)
+    v = _normal_rows(seed, _V, group, seq, p0, p1, D)
+    ik = _normal_rows(seed, _IDXK, group, seq, p0, p1, DI)
     return k, v, ik
 
 
@@ -141,15 +142,21 @@ def page_table(seed: int, n_seq: int, cap: int, page_tokens: int, n_used, spare:
 # ---------------------------------------------------------------------------
 
 DECODER_20 = ("F", "R", "R", "R") + ("I", "R", "R", "R") * 4
+# the encoder (same section): layers 1-2 sliding-window attention only ('S'),
+# then 18 CSA2 layers at compression m = 2 as 3 x [Full + 5 Reuse]
+ENCODER_20 = ("S", "S") + ("F", "R", "R", "R", "R", "R") * 3
 
 
 @dataclass(frozen=True)
 class Workload:
     """One synthetic workload: B queries over caches of N positions.
 
-    layers: per-layer CSA2 mode, 'F' (Full), 'I' (Reindex), 'R' (Reuse).
+    layers: per-layer CSA2 mode, 'F' (Full), 'I' (Reindex), 'R' (Reuse), or 'S'
+    (sliding window only).
     prefill: if set, the B queries are consecutive causal positions of one
     sequence starting at N (the chunk is written before the queries run).
+    m: global-KV compression (tokens per global entry); each Full layer then
+    keeps its own global store of cap // m entries.
     """
     name: str
     B: int
@@ -157,6 +164,7 @@ class Workload:
     layers: tuple
     prefill: bool = False
     w_cap: int = WINDOW
+    m: int = 1
     extra: dict = field(default_factory=dict)
 
     @property
@@ -190,6 +198,9 @@ WORKLOADS = {
     "decoder20_1m_b4": Workload("decoder20_1m_b4", B=4, N=1048576, layers=DECODER_20),
     "prefill_8k_over_128k": Workload("prefill_8k_over_128k", B=8192, N=131072,
                                      layers=("F",), prefill=True, w_cap=16384),
+    "encoder20_m2_chunk8k_over_128k": Workload("encoder20_m2_chunk8k_over_128k", B=8192,
+                                               N=131072, layers=ENCODER_20, prefill=True,
+                                               w_cap=16384, m=2),
 }
 
 

@@ -158,6 +158,38 @@ csa2_status csa2_quantize_kv(const csa2_cache* cache, const csa2_window* win,
                              const int64_t* pos, int64_t n, hipStream_t stream);
 
 /*
+ * csa2_compress_kv - quantise-on-write at global-KV compression m.
+ * Passage: the encoder's CSA2 layers run at compression m = 2, the decoder's at
+ * m = 1 ([P4] "How the architecture shrinks the KV cache").  The pages give the
+ * ratio, not the operator; this library's reading: global entry e of a
+ * sequence stands for its m tokens at positions m*e .. m*e + m - 1, and its K,
+ * V and indexer-key rows are those tokens' rows averaged in fp32 ((r0 + r1) *
+ * 0.5 for m = 2: one rounding of the sum, an exact halving), then quantised as
+ * csa2_quantize_kv quantises a token row.  The window keeps every token.  A
+ * query with N tokens of context then sees entries [0, N / m) (complete groups)
+ * and window rows [N - 128, N): pass ctx / m to the indexer calls and ctx to
+ * csa2_decode_attn.
+ *   m         1 or 2 (else CSA2_ERR_UNSUPPORTED); with k given, n must be a
+ *             multiple of m (else CSA2_ERR_INVALID_ARG).  m = 1 is exactly
+ *             csa2_quantize_kv.
+ *   k, v, idx_k  [n][128] / [n][64] fp32 token rows; rows i*m .. i*m + m - 1
+ *             form group i, written as entry pos[i*m] / m of sequence seq[i*m]
+ *             (record and indexer key; the cache's cap counts entries).  The
+ *             caller passes each group's tokens in position order, the first at
+ *             a multiple of m; a group whose first position is not a multiple
+ *             of m is skipped, and the other rows' seq and pos are not read.
+ *             k and v both NULL (idx_k NULL, win_k given): window rows only, n
+ *             any -- for tokens whose group is not complete yet.
+ *   win_k/v   as for csa2_quantize_kv, one row per token at slot pos[i] % w_cap;
+ *             token positions lie in [0, m * cap).
+ *   Other arguments, errors and races as for csa2_quantize_kv.
+ */
+csa2_status csa2_compress_kv(const csa2_cache* cache, const csa2_window* win,
+                             const float* k, const float* v, const float* idx_k,
+                             const float* win_k, const float* win_v, const int32_t* seq,
+                             const int64_t* pos, int64_t n, int32_t m, hipStream_t stream);
+
+/*
  * csa2_index_full - Full-mode indexer: score, block pool, top-k.
  * Passage: a Full layer computes its own indexer query and a fresh top-k; the
  * first Full layer selects 2,048 blocks of 8 positions (a 16,384-position pool)
@@ -233,6 +265,10 @@ csa2_status csa2_index_select_pool(const float* M, int64_t m_stride, const int64
  * valid main rows idx[b][j] >= 0 and the window rows of positions
  * [max(0, N-128), N); logits (q_h . k) * sm_scale; no sink, no bias.
  *   layer     window layer in [0, win->n_layers).
+ *   ctx       tokens of context N per query (the window rows are those of
+ *             positions [N-128, N)); a main entry is valid below min(N, cap).
+ *             For a store compressed m-fold (csa2_compress_kv) N is still the
+ *             token count and the entries are at most N / m.
  *   q         [B][16][128] fp32, |q| < 65504.
  *   idx       [B][topk] int32 positions (< ctx[b]) or -1.
  *   out       [B][16][128] fp32.  A query with no valid entry gets zeros.

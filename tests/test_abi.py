@@ -98,6 +98,23 @@ def test_quantize_error_paths(L):
     assert f(C.byref(c), None, FAKE, FAKE, None, None, None, FAKE, FAKE, 0, None) == 0
 
 
+def test_compress_error_paths(L):
+    from fp4_kv_cache_decode_amd import csa2 as K
+    c = _cache(K)
+    f = L.csa2_compress_kv
+    assert f(C.byref(c), None, FAKE, FAKE, None, None, None, FAKE, FAKE, 4, 3, None) == 2
+    assert f(C.byref(c), None, FAKE, FAKE, None, None, None, FAKE, FAKE, 4, 0, None) == 2
+    assert f(C.byref(c), None, FAKE, FAKE, None, None, None, FAKE, FAKE, 5, 2, None) == 1
+    assert f(C.byref(c), None, None, FAKE, None, None, None, FAKE, FAKE, 4, 2, None) == 1
+    assert f(C.byref(c), None, FAKE, FAKE, None, None, None, FAKE, FAKE, 0, 2, None) == 0
+    # window only: k and v both NULL, no indexer keys, window rows given
+    w = _win(K)
+    assert f(C.byref(c), C.byref(w), None, FAKE, None, FAKE, FAKE, FAKE, FAKE, 4, 2, None) == 1
+    assert f(C.byref(c), None, None, None, None, None, None, FAKE, FAKE, 4, 2, None) == 1
+    assert f(C.byref(c), C.byref(w), None, None, FAKE, FAKE, FAKE, FAKE, FAKE, 4, 2, None) == 1
+    assert f(C.byref(c), C.byref(w), None, None, None, FAKE, FAKE, FAKE, FAKE, 0, 2, None) == 0
+
+
 def test_index_error_paths(L):
     from fp4_kv_cache_decode_amd import csa2 as K
     c = _cache(K)

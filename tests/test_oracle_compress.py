@@ -160,14 +160,14 @@ def test_m2_layer_sees_n_over_two_entries_and_the_raw_window():
     k, v, ik, _, _ = _inputs(rng, N_tok, 1)
     wk = (rng.standard_normal((1, N_tok, 128))).astype(np.float32)
     wv = (rng.standard_normal((1, N_tok, 128))).astype(np.float32)
-    c = O.Cache(1, 512, 1, w_cap)
+    c = O.Cache(1, 256, 1, w_cap)
     seq = np.zeros(N_tok, np.int32)
     pos = np.arange(N_tok, dtype=np.int64)
     c.compress(k[:n], v[:n], ik[:n], wk[:, :n], wv[:, :n], seq[:n], pos[:n], 2)
     # the unpaired last token only reaches the window
-    c.compress(k[n:], v[n:], ik[n:], wk[:, n:], wv[:, n:], seq[n:], pos[n:], 1)
-    c.kv[0, n] = 0                 # undo its m = 1 main entry: it is not a pair
-    c.idxk[0, n] = 0
+    before = c.kv.copy(), c.idxk.copy()
+    c.compress(None, None, None, wk[:, n:], wv[:, n:], seq[n:], pos[n:], 2)
+    assert np.array_equal(c.kv, before[0]) and np.array_equal(c.idxk, before[1])
     n_c = N_tok // 2
     q_idx = rng.standard_normal((1, 4, 64)).astype(np.float32)
     w = rng.uniform(0, 1, (1, 4)).astype(np.float32)
