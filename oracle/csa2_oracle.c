@@ -208,7 +208,8 @@ void oracle_quantize_kv(uint8_t* kv, uint8_t* idxk, float idxk_scale, int64_t ca
  * group's entry is pos[i*m] / m of sequence seq[i*m], and a group whose first
  * position is not a multiple of m is skipped.  Window rows are written for
  * every token at its own position, as in oracle_quantize_kv.  m = 1 writes the
- * same bytes as oracle_quantize_kv. */
+ * same bytes as oracle_quantize_kv.  With k and v NULL only window rows are
+ * written (tokens whose group is not complete yet). */
 static void mean_rows(const float* x, int32_t m, int dim, float* out) {
     int c, j;
     for (c = 0; c < dim; ++c) {
@@ -225,8 +226,9 @@ void oracle_compress_kv(uint8_t* kv, uint8_t* idxk, float idxk_scale, int64_t ca
                         const float* win_k, const float* win_v, const int32_t* seq,
                         const int64_t* pos, int64_t n, int32_t m) {
     int64_t g, i;
+    const int64_t n_groups = (k && v) ? n / m : 0;
 #pragma omp parallel for schedule(static)
-    for (g = 0; g < n / m; ++g) {
+    for (g = 0; g < n_groups; ++g) {
         const int64_t i0 = g * m;
         float xk[OR_D], xv[OR_D], xi[OR_DI];
         int64_t row;

@@ -48,7 +48,9 @@ def lib():
             C.c_float, C.c_float, C.c_int32, C.c_int32, _f32p, _f32p, C.c_void_p,
             C.c_void_p, C.c_void_p, _i32p, _i64p, C.c_int64]
         L.oracle_quantize_kv.restype = None
-        L.oracle_compress_kv.argtypes = L.oracle_quantize_kv.argtypes + [C.c_int32]
+        L.oracle_compress_kv.argtypes = (L.oracle_quantize_kv.argtypes[:11] +
+                                         [C.c_void_p, C.c_void_p] +
+                                         L.oracle_quantize_kv.argtypes[13:] + [C.c_int32])
         L.oracle_compress_kv.restype = None
         L.oracle_index_score.argtypes = [_u8p, C.c_float, _f32p, _f32p]
         L.oracle_index_score.restype = C.c_double
@@ -149,10 +151,13 @@ class Cache:
     def compress(self, k, v, idx_k, win_k, win_v, seq, pos, m):
         """Write n tokens at compression m (1 or 2): rows i*m .. i*m+m-1 (token
         positions m*e .. m*e+m-1 of one sequence) become global entry e = pos[i*m] / m,
-        their fp32 mean quantised like a token row; window rows for every token."""
-        k, v = _c(k, np.float32), _c(v, np.float32)
-        n = k.shape[0]
-        assert m in (1, 2) and n % m == 0
+        their fp32 mean quantised like a token row; window rows for every token.
+        k = v = None (idx_k None): window rows only."""
+        n = win_k.shape[1] if k is None else k.shape[0]
+        assert m in (1, 2) and (k is None or n % m == 0)
+        assert (k is None) == (v is None) and (k is not None or idx_k is None)
+        k = None if k is None else _c(k, np.float32)
+        v = None if v is None else _c(v, np.float32)
         idx_k = None if idx_k is None else _c(idx_k, np.float32)
         win_k = None if win_k is None else _c(win_k, np.float32)
         win_v = None if win_v is None else _c(win_v, np.float32)
@@ -164,7 +169,8 @@ class Cache:
         lib().oracle_compress_kv(
             self.kv, _ptr(self.idxk), self.idxk_scale, self.cap, self.n_seq,
             _ptr(self.wk), _ptr(self.wv), self.wk_scale, self.wv_scale, self.w_cap,
-            self.n_layers, k, v, _ptr(idx_k), _ptr(win_k), _ptr(win_v), seq, pos, n, m)
+            self.n_layers, _ptr(k), _ptr(v), _ptr(idx_k), _ptr(win_k), _ptr(win_v), seq, pos,
+            n, m)
 
     # -- indexer
     def scores(self, seq: int, q_idx, w, N: int) -> np.ndarray:
