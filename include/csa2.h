@@ -344,7 +344,8 @@ csa2_status csa2_decode_attn_noalloc(const csa2_cache* cache, const csa2_window*
  * architecture shrinks the KV cache"; [P5] "CSA2 and the attention redesign").
  *   Arguments as in csa2_index_reindex and csa2_decode_attn_ex (block must be
  *   8; kvg_out may be NULL).  idx, out and kvg_out are bit-identical to those
- *   two calls.  B * (ceil(topk / 64) + 2) must not exceed 768 (the batches the
+ *   two calls.  One ctx serves both stages, so the store is uncompressed
+ *   (m = 1: Reindex layers are decoder layers).  B * (ceil(topk / 64) + 2) must not exceed 768 (the batches the
  *   separate attention call runs as 64-entry tiles; else CSA2_ERR_UNSUPPORTED).
  *   status    device int32: nothing is written when every barrier completes;
  *             a workgroup that polled a barrier max_polls times without seeing
