@@ -41,6 +41,14 @@ int main(void) {
     EXPECT(csa2_quantize_kv(&c, NULL, ff, ff, NULL, NULL, NULL, fi, fl, -1, NULL), CSA2_ERR_INVALID_ARG);
     EXPECT(csa2_quantize_kv(&c, NULL, ff, ff, NULL, NULL, NULL, fi, fl, 0, NULL), CSA2_OK);
     EXPECT(csa2_quantize_kv(&c, &w, ff, ff, ff, ff, ff, fi, fl, 0, NULL), CSA2_OK);
+    /* compression: m in {1, 2}, n a multiple of m, window-only calls */
+    EXPECT(csa2_compress_kv(&c, NULL, ff, ff, NULL, NULL, NULL, fi, fl, 4, 3, NULL), CSA2_ERR_UNSUPPORTED);
+    EXPECT(csa2_compress_kv(&c, NULL, ff, ff, NULL, NULL, NULL, fi, fl, 5, 2, NULL), CSA2_ERR_INVALID_ARG);
+    EXPECT(csa2_compress_kv(&c, NULL, NULL, ff, NULL, NULL, NULL, fi, fl, 4, 2, NULL), CSA2_ERR_INVALID_ARG);
+    EXPECT(csa2_compress_kv(&c, NULL, NULL, NULL, NULL, NULL, NULL, fi, fl, 4, 2, NULL), CSA2_ERR_INVALID_ARG);
+    EXPECT(csa2_compress_kv(&c, &w, NULL, NULL, ff, ff, ff, fi, fl, 4, 2, NULL), CSA2_ERR_INVALID_ARG);
+    EXPECT(csa2_compress_kv(&c, &w, NULL, NULL, NULL, ff, ff, fi, fl, 0, 2, NULL), CSA2_OK);
+    EXPECT(csa2_compress_kv(&c, NULL, ff, ff, ff, NULL, NULL, fi, fl, 0, 1, NULL), CSA2_OK);
     {
         csa2_cache bad = c;
         bad.idxk_scale = 0.0f;

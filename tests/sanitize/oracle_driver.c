@@ -18,6 +18,12 @@ void oracle_quantize_kv(uint8_t* kv, uint8_t* idxk, float idxk_scale, int64_t ca
                         float wv_scale, int32_t w_cap, int32_t n_layers, const float* k,
                         const float* v, const float* idx_k, const float* win_k,
                         const float* win_v, const int32_t* seq, const int64_t* pos, int64_t n);
+void oracle_compress_kv(uint8_t* kv, uint8_t* idxk, float idxk_scale, int64_t cap,
+                        int32_t n_seq, uint8_t* wk, uint8_t* wv, float wk_scale,
+                        float wv_scale, int32_t w_cap, int32_t n_layers, const float* k,
+                        const float* v, const float* idx_k, const float* win_k,
+                        const float* win_v, const int32_t* seq, const int64_t* pos, int64_t n,
+                        int32_t m);
 double oracle_index_score(const uint8_t* key, float scale, const float* q, const float* w);
 int32_t oracle_topk(const double* val, const int64_t* ids, int64_t n, int32_t k, int32_t* out,
                     double* kth);
@@ -102,6 +108,28 @@ int main(void) {
         oracle_quantize_kv(kv, NULL, 1.0f, CAP, S, wk, wv, 1.5f, 0.75f, WCAP, L, k, v, NULL,
                            wkf, wvf, ws, wp, nw);
         free(wkf); free(wvf); free(ws); free(wp);
+    }
+    {
+        /* compression 2 into a store of CAP / 2 entries per sequence: the first
+         * half of each sequence's tokens, a misaligned group, and window-only rows */
+        const int64_t nc = CAP;                 /* tokens of sequence 0 and 1, CAP / 2 each */
+        uint8_t* kv2 = xcalloc((size_t)S * (CAP / 2) * 144, 1);
+        uint8_t* ik2 = xcalloc((size_t)S * (CAP / 2) * DI, 1);
+        float* wkf = xcalloc((size_t)L * nc * D, sizeof(float));
+        float* wvf = xcalloc((size_t)L * nc * D, sizeof(float));
+        int32_t* cs = xcalloc((size_t)nc, sizeof(int32_t));
+        int64_t* cp = xcalloc((size_t)nc, sizeof(int64_t));
+        for (i = 0; i < L * nc * D; ++i) { wkf[i] = sym(4.0); wvf[i] = sym(4.0); }
+        for (i = 0; i < nc; ++i) { cs[i] = (int32_t)(i / (nc / 2)); cp[i] = i % (nc / 2); }
+        cp[2] = 3;                              /* group 1 starts at an odd position: skipped */
+        oracle_compress_kv(kv2, ik2, 0.5f, CAP / 2, S, wk, wv, 1.5f, 0.75f, WCAP, L, k, v, ik,
+                           wkf, wvf, cs, cp, nc, 2);
+        oracle_compress_kv(kv2, NULL, 1.0f, CAP / 2, S, wk, wv, 1.5f, 0.75f, WCAP, L, NULL, NULL,
+                           NULL, wkf, wvf, cs, cp, 7, 2);
+        oracle_compress_kv(kv2, ik2, 0.5f, CAP / 2, S, NULL, NULL, 1.0f, 1.0f, WCAP, L, k, v, ik,
+                           NULL, NULL, cs, cp, nc, 1);
+        for (i = 0; i < S * (CAP / 2) * 144; ++i) acc += kv2[i];
+        free(kv2); free(ik2); free(wkf); free(wvf); free(cs); free(cp);
     }
 
     /* indexer: scores, top-k, Full and Reindex with ragged contexts */
