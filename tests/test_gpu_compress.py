@@ -152,19 +152,31 @@ def _fill_group(K, oc, gc, seed, s, N, layers, group=0):
           np.arange(w0, N, dtype=np.int64), 2)
 
 
-def test_encoder_group_m2_against_oracle(K):
+@pytest.mark.parametrize("paged", [False, True], ids=["contiguous", "paged64"])
+def test_encoder_group_m2_against_oracle(K, paged):
     """One sliding-window layer and one [Full + 5 Reuse] group at m = 2 over
-    three sequences of 3,001, 4,096 and 515 tokens."""
+    three sequences of 3,001, 4,096 and 515 tokens (a paged store: 64-entry
+    pages over a shuffled pool)."""
     seed = 3
     Ns = np.array([3001, 4096, 515], np.int64)
     B, n_layers = Ns.size, 7                    # layer 0: window only; 1: Full; 2-6: Reuse
-    cap = int(Ns.max()) // 2 + 64
+    cap = int(Ns.max()) // 2 + 64               # 2,112 entries = 33 pages of 64
     oc = O.Cache(B, cap, n_layers, 256)
-    gc = K.Cache(B, cap, n_layers, 256)
+    if paged:
+        table, n_pages = shuffled_pages(7, B, cap, 64, Ns // 2)
+        gc = K.Cache(B, cap, n_layers, 256, page_tokens=64, n_pages=n_pages,
+                     page_table=torch.from_numpy(table))
+    else:
+        gc = K.Cache(B, cap, n_layers, 256)
     for s in range(B):
         _fill_group(K, oc, gc, seed, s, int(Ns[s]), range(n_layers))
     torch.cuda.synchronize()
-    assert np.array_equal(gc.kv.cpu().numpy(), oc.kv)
+    if paged:
+        gkv = unpage(gc.kv.cpu().numpy(), table, 64, cap)
+        for s in range(B):
+            assert np.array_equal(gkv[s, :Ns[s] // 2], oc.kv[s, :Ns[s] // 2])
+    else:
+        assert np.array_equal(gc.kv.cpu().numpy(), oc.kv)
     assert np.array_equal(gc.wk.cpu().numpy(), oc.wk)
 
     seq = np.arange(B, dtype=np.int32)
