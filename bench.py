@@ -712,13 +712,16 @@ def row_encoder(args):
     Full layer with its own store of 2-token entries (65,536 + 4,096 of them).
     A step writes the chunk (csa2_compress_kv: each group's entries and every
     layer's window rows), then runs every layer's indexer and attention for all
-    8,192 queries (query i: ctx_i = 131,073 + i tokens, ctx_i // 2 entries)."""
+    8,192 queries (query i: ctx_i = 131,073 + i tokens, ctx_i // 2 entries).  A
+    Full layer keeps its 512 best blocks: no Reindex layer follows it, and its
+    top-512 positions all lie in those blocks."""
     import torch
     import fp4_kv_cache_decode_amd.csa2 as K
     from fp4_kv_cache_decode_amd import datagen as G
     wl = G.WORKLOADS["encoder20_m2_chunk8k_over_128k"]
     B, N0, m = wl.B, wl.N, wl.m
     cap_c = wl.cap // m
+    nbk = wl.extra["pool_blocks"]          # blocks kept by a Full layer (TOPK: no Reindex pool)
     groups = [i for i, x in enumerate(wl.layers) if x == "F"]
     swa = [i for i, x in enumerate(wl.layers) if x == "S"]
     span = [list(range(f, f + 6)) for f in groups]          # a group's 6 layers
@@ -777,11 +780,11 @@ def row_encoder(args):
     # window-only layers: one absent main entry per query (the window carries them)
     none = torch.full((B, 1), -1, dtype=torch.int32, device="cuda")
     M = torch.empty((B, K.block_stride(cap_c)), dtype=torch.float32, device="cuda")
-    pool = torch.empty((B, G.N_BLOCKS), dtype=torch.int32, device="cuda")
+    pool = torch.empty((B, nbk), dtype=torch.int32, device="cuda")
     idx = torch.empty((B, G.TOPK), dtype=torch.int32, device="cuda")
     out = torch.empty((len(wl.layers), B, G.H, G.D), dtype=torch.float32, device="cuda")
-    ws_sel = K.alloc_workspace(K.OP_SELECT_POOL, B, cap_c)
-    ws_ri = K.alloc_workspace(K.OP_INDEX_REINDEX, B)
+    ws_sel = K.alloc_workspace(K.OP_SELECT_POOL, B, cap_c, n_blocks=nbk)
+    ws_ri = K.alloc_workspace(K.OP_INDEX_REINDEX, B, n_blocks=nbk)
     ws_at = K.alloc_workspace(K.OP_DECODE_ATTN, B)
     torch.cuda.synchronize()
     log(f"[bench] encoder inputs ready ({time.time() - t0:.1f}s)")
@@ -834,7 +837,8 @@ def row_encoder(args):
         for l in swa:
             ocs[0].decode_attn(wins[0].index(l), q_np[l][sample], nn, ss, sx)
         for gi, ls in enumerate(span):
-            _, oidx, _, _ = ocs[gi].index_full(iq[gi][0][sample], iq[gi][1][sample], ss, sxc)
+            _, oidx, _, _ = ocs[gi].index_full(iq[gi][0][sample], iq[gi][1][sample], ss, sxc,
+                                               n_blocks=nbk)
             for l in ls:
                 ocs[gi].decode_attn(wins[gi].index(l), q_np[l][sample], oidx, ss, sx)
         secs = time.perf_counter() - ts
@@ -845,7 +849,7 @@ def row_encoder(args):
                          f"the fp64 C oracle's indexers and all 20 layers' attention, "
                          f"{secs:.1f} s wall"}
     cfg = {"workload": wl.name, "queries": B, "prefix": N0, "compression": m,
-           "layers": "".join(wl.layers), "topk": G.TOPK, "pool_blocks": G.N_BLOCKS,
+           "layers": "".join(wl.layers), "topk": G.TOPK, "pool_blocks": nbk,
            "window": G.WINDOW, "key_evals": key_evals, "dtype": "fp32"}
     roof = {"bound": "alu", "achieved": tfs, "peak": PEAK_FP32_TFS, "unit": "TFLOP/s",
             "frac": tfs / PEAK_FP32_TFS,

@@ -198,9 +198,12 @@ WORKLOADS = {
     "decoder20_1m_b4": Workload("decoder20_1m_b4", B=4, N=1048576, layers=DECODER_20),
     "prefill_8k_over_128k": Workload("prefill_8k_over_128k", B=8192, N=131072,
                                      layers=("F",), prefill=True, w_cap=16384),
+    # the encoder's Full layers serve no Reindex layer, so they keep TOPK blocks
+    # (all their top-k positions lie in them), not the decoder's 2,048-block pool
     "encoder20_m2_chunk8k_over_128k": Workload("encoder20_m2_chunk8k_over_128k", B=8192,
                                                N=131072, layers=ENCODER_20, prefill=True,
-                                               w_cap=16384, m=2),
+                                               w_cap=16384, m=2,
+                                               extra={"pool_blocks": TOPK}),
 }
 
 

@@ -182,12 +182,16 @@ def test_encoder_group_m2_against_oracle(K, paged):
     seq = np.arange(B, dtype=np.int32)
     ctx, ctx_c = Ns, Ns // 2
     qi, wi = G.index_queries(seed, 1, B)
-    pool = torch.empty((B, G.N_BLOCKS), dtype=torch.int32, device="cuda")
+    nbk = G.WORKLOADS["encoder20_m2_chunk8k_over_128k"].extra["pool_blocks"]
+    pool = torch.empty((B, nbk), dtype=torch.int32, device="cuda")
     idx = torch.empty((B, G.TOPK), dtype=torch.int32, device="cuda")
-    ws = K.alloc_workspace(K.OP_INDEX_FULL, B, int(ctx_c.max()))
-    K.index_full(gc, dev(qi), dev(wi), dev(seq), dev(ctx_c), int(ctx_c.max()), pool, idx, ws)
+    ws = K.alloc_workspace(K.OP_INDEX_FULL, B, int(ctx_c.max()), n_blocks=nbk)
+    K.index_full(gc, dev(qi), dev(wi), dev(seq), dev(ctx_c), int(ctx_c.max()), pool, idx, ws,
+                 n_blocks=nbk)
     torch.cuda.synchronize()
-    opool, oidx, kb, kp = oc.index_full(qi, wi, seq, ctx_c)
+    opool, oidx, kb, kp = oc.index_full(qi, wi, seq, ctx_c, n_blocks=nbk)
+    # the encoder's 512 blocks hold the flat top-512: the decoder's 2,048-block pool agrees
+    assert np.array_equal(oc.index_full(qi, wi, seq, ctx_c)[1], oidx)
     gpool, gidx = pool.cpu().numpy(), idx.cpu().numpy()
     for b in range(B):
         sc = oc.scores(b, qi[b], wi[b], int(ctx_c[b]))
@@ -251,14 +255,18 @@ def test_encoder_chunk_8k_over_128k_sampled(K):
     seq, ctx = wl.seq(), wl.ctx()
     ctx_c = ctx // m
     qi, wi = G.index_queries(seed, 2, B)
-    pool = torch.empty((B, G.N_BLOCKS), dtype=torch.int32, device="cuda")
+    nbk = wl.extra["pool_blocks"]
+    pool = torch.empty((B, nbk), dtype=torch.int32, device="cuda")
     idx = torch.empty((B, G.TOPK), dtype=torch.int32, device="cuda")
-    ws = K.alloc_workspace(K.OP_INDEX_FULL, B, cap_c)
-    K.index_full(gc, dev(qi), dev(wi), dev(seq), dev(ctx_c), cap_c, pool, idx, ws)
+    ws = K.alloc_workspace(K.OP_INDEX_FULL, B, cap_c, n_blocks=nbk)
+    K.index_full(gc, dev(qi), dev(wi), dev(seq), dev(ctx_c), cap_c, pool, idx, ws, n_blocks=nbk)
     torch.cuda.synchronize()
     gpool, gidx = pool.cpu().numpy(), idx.cpu().numpy()
     sample = np.unique(np.r_[0, 1, 2, 3, 255, 256, 4095, 8190, 8191, np.arange(97, B, 1013)])
-    opool, oidx, kb, kp = oc.index_full(qi[sample], wi[sample], seq[sample], ctx_c[sample])
+    opool, oidx, kb, kp = oc.index_full(qi[sample], wi[sample], seq[sample], ctx_c[sample],
+                                        n_blocks=nbk)
+    assert np.array_equal(oc.index_full(qi[sample], wi[sample], seq[sample], ctx_c[sample])[1],
+                          oidx)
     n_exempt = 0
     for j, b in enumerate(sample):
         sc = oc.scores(0, qi[b], wi[b], int(ctx_c[b]))

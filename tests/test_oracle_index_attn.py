@@ -141,6 +141,19 @@ def test_hierarchical_equals_flat_topk(seed):
     assert set(sel // block) <= set(pool[0][pool[0] >= 0])
 
 
+@pytest.mark.parametrize("seed", range(6))
+def test_as_many_blocks_as_positions_still_hold_the_flat_topk(seed):
+    """The boundary n_blocks == topk: every top-k position lies in the top-k
+    blocks (ties included), so a Full layer that keeps only that many blocks
+    (no Reindex pool to serve) selects the flat top-k."""
+    N, topk = 3000 + 37 * seed, 64
+    c, q, w = _tie_heavy_cache(N, seed) if seed % 2 else (
+        _fill_cache(1, N, seed), *G.index_queries(seed, 0, 1))
+    _, idx, _, _ = c.index_full(q, w, [0], [N], n_blocks=topk, topk=topk)
+    sc = c.scores(0, q[0], w[0], N)
+    assert np.array_equal(idx[0], _brute_topk(list(sc), topk))
+
+
 def test_small_context_pool_is_every_block():
     c = _fill_cache(1, 1000, seed=4)
     q, w = G.index_queries(4, 0, 1)
