@@ -38,7 +38,8 @@ def test_row_counters_match_their_sources():
     import bench
     for prof, wl in (("quantize_bulk_decoder20_1m_b4.txt", "quantize_bulk_4x1m"),
                      ("attn_gather_b1024_n64k.txt", "gather_attention_b1024_n64k"),
-                     ("prefill_8k_over_128k_kernel_stats.txt", "prefill_8k_over_128k")):
+                     ("prefill_8k_over_128k_kernel_stats.txt", "prefill_8k_over_128k"),
+                     ("encoder_chunk8k_m2_kernel_stats.txt", "encoder20_m2_chunk8k_over_128k")):
         t = bench.row_counter_traffic(prof, wl)
         assert t is None or t > 0
         assert bench.row_counter_traffic(prof, "another_workload") is None
