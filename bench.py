@@ -603,12 +603,15 @@ def row_reindex_layer(args):
 def row_prefill(args):
     """The 8,192-token prefill chunk over a 131,072-token prefix: quantise the
     chunk (main KV, indexer keys, window rows), then the Full-layer indexer and
-    attention for all 8,192 causal queries (seq 0, ctx_i = 131,073 + i)."""
+    attention for all 8,192 causal queries (seq 0, ctx_i = 131,073 + i).  The
+    layer keeps its 512 best blocks (no Reindex layer follows it; --pool-blocks
+    2048 builds the decoder's pool instead): the top-512 lie in them either way."""
     import torch
     import fp4_kv_cache_decode_amd.csa2 as K
     from fp4_kv_cache_decode_amd import datagen as G
     wl = G.WORKLOADS["prefill_8k_over_128k"]
     B, N0, cap = wl.B, wl.N, wl.cap
+    nbk = args.pool_blocks or wl.extra["pool_blocks"]   # blocks the Full layer keeps
     t0 = time.time()
     dev = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
     c = K.Cache(1, cap, 1, wl.w_cap)
@@ -642,11 +645,11 @@ def row_prefill(args):
     q_np = G.attn_queries(args.seed, 0, B)
     seq, ctx, qi, wi, q = dev(seq_np), dev(ctx_np), dev(qi_np), dev(wi_np), dev(q_np)
     M = torch.empty((B, K.block_stride(cap)), dtype=torch.float32, device="cuda")
-    pool = torch.empty((B, G.N_BLOCKS), dtype=torch.int32, device="cuda")
+    pool = torch.empty((B, nbk), dtype=torch.int32, device="cuda")
     idx = torch.empty((B, G.TOPK), dtype=torch.int32, device="cuda")
     out = torch.empty((B, G.H, G.D), dtype=torch.float32, device="cuda")
-    ws_sel = K.alloc_workspace(K.OP_SELECT_POOL, B, cap)
-    ws_ri = K.alloc_workspace(K.OP_INDEX_REINDEX, B)
+    ws_sel = K.alloc_workspace(K.OP_SELECT_POOL, B, cap, n_blocks=nbk)
+    ws_ri = K.alloc_workspace(K.OP_INDEX_REINDEX, B, n_blocks=nbk)
     ws_at = K.alloc_workspace(K.OP_DECODE_ATTN, B)
     torch.cuda.synchronize()
     log(f"[bench] prefill inputs ready ({time.time() - t0:.1f}s)")
@@ -683,18 +686,19 @@ def row_prefill(args):
     cpu = None
     if oc is not None:
         # a strided sample of the chunk's queries through the oracle (index + attention)
-        sample = np.arange(0, B, 256)
+        sample = np.arange(0, B, 16)
         ts = time.perf_counter()
-        _, oidx, _, _ = oc.index_full(qi_np[sample], wi_np[sample], seq_np[sample], ctx_np[sample])
+        _, oidx, _, _ = oc.index_full(qi_np[sample], wi_np[sample], seq_np[sample], ctx_np[sample],
+                                      n_blocks=nbk)
         oc.decode_attn(0, q_np[sample], oidx, seq_np[sample], ctx_np[sample])
         secs = time.perf_counter() - ts
         threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
         cpu = {"value": sample.size / secs, "unit": "queries/s", "cores": threads,
                "kind": "oracle",
-               "sample": f"{sample.size} of the chunk's 8,192 queries (every 256th) through "
+               "sample": f"{sample.size} of the chunk's 8,192 queries (every 16th) through "
                          f"the fp64 C oracle's indexer and attention, {secs:.1f} s wall"}
     cfg = {"workload": wl.name, "queries": B, "prefix": N0, "topk": G.TOPK,
-           "pool_blocks": G.N_BLOCKS, "window": G.WINDOW, "key_evals": key_evals, "dtype": "fp32"}
+           "pool_blocks": nbk, "window": G.WINDOW, "key_evals": key_evals, "dtype": "fp32"}
     traffic = row_counter_traffic("prefill_8k_over_128k_kernel_stats.txt",
                                   "prefill_8k_over_128k")
     roof = {"bound": "alu", "achieved": tfs, "peak": PEAK_FP32_TFS, "unit": "TFLOP/s",
@@ -721,7 +725,7 @@ def row_encoder(args):
     wl = G.WORKLOADS["encoder20_m2_chunk8k_over_128k"]
     B, N0, m = wl.B, wl.N, wl.m
     cap_c = wl.cap // m
-    nbk = wl.extra["pool_blocks"]          # blocks kept by a Full layer (TOPK: no Reindex pool)
+    nbk = args.pool_blocks or wl.extra["pool_blocks"]   # blocks a Full layer keeps
     groups = [i for i, x in enumerate(wl.layers) if x == "F"]
     swa = [i for i, x in enumerate(wl.layers) if x == "S"]
     span = [list(range(f, f + 6)) for f in groups]          # a group's 6 layers
@@ -875,6 +879,9 @@ def main():
                          "pages scattered over a shuffled physical pool; 0 = contiguous")
     ap.add_argument("--eager", action="store_true",
                     help="launch every kernel from Python instead of replaying HIP graphs")
+    ap.add_argument("--pool-blocks", type=int, default=0,
+                    help="prefill and encoder rows: blocks a Full layer keeps (default: the "
+                         "workload's, 512; 2048 builds the decoder's Reindex pool)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration)")
     ap.add_argument("--row", default="decode",

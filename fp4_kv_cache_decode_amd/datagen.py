@@ -196,10 +196,12 @@ WORKLOADS = {
     "hier_256k_b8": Workload("hier_256k_b8", B=8, N=262144,
                              layers=("F", "I", "R", "R", "R")),
     "decoder20_1m_b4": Workload("decoder20_1m_b4", B=4, N=1048576, layers=DECODER_20),
+    # one Full layer and nothing after it: no Reindex layer needs the 2,048-block
+    # pool, so the layer keeps TOPK blocks (all its top-k positions lie in them)
     "prefill_8k_over_128k": Workload("prefill_8k_over_128k", B=8192, N=131072,
-                                     layers=("F",), prefill=True, w_cap=16384),
-    # the encoder's Full layers serve no Reindex layer, so they keep TOPK blocks
-    # (all their top-k positions lie in them), not the decoder's 2,048-block pool
+                                     layers=("F",), prefill=True, w_cap=16384,
+                                     extra={"pool_blocks": TOPK}),
+    # likewise the encoder's Full layers, which serve no Reindex layer
     "encoder20_m2_chunk8k_over_128k": Workload("encoder20_m2_chunk8k_over_128k", B=8192,
                                                N=131072, layers=ENCODER_20, prefill=True,
                                                w_cap=16384, m=2,
