@@ -26,7 +26,7 @@
 // tokens at positions M*e .. M*e + M - 1 of one sequence, and writes entry e from
 // the rows' fp32 mean ((r0 + r1) * 0.5: one rounding of the sum, an exact
 // halving); the window parts still write every token.  M = 1 is plain
-// quantise-on-write and compiles to the same code as before the parameter.
+// quantise-on-write: every step that depends on M folds away for it.
 #include "csa2_device.h"
 #include "csa2_internal.h"
 
