@@ -28,8 +28,10 @@
 // few instructions per value: a single-barrier block reduction, no atomics on
 // the chosen path, one coalesced store.
 //
-// Rows of up to 16,384 entries: one workgroup, one read of the row; up to
-// 32,768: the same with 32 values per thread.
+// Rows of up to 4,096 entries: the same core in a 256-thread workgroup (each
+// block-wide step is shorter, and about three rows share a CU); up to 16,384:
+// one 1,024-thread workgroup, one read of the row; up to 32,768: the same with
+// 32 values per thread.
 // Longer rows (up to 131,072): a segment kernel takes the exact top-q of each
 // 4,096-entry segment (q >= 4x a segment's expected share of the top-k) and
 // writes it densely in ascending index order; a merge kernel selects the top-k
@@ -52,6 +54,12 @@ using namespace topk_dev;
 __global__ void __launch_bounds__(BIG_T) topk_small_kernel(TopkArgs a) {
     __shared__ Shared<BIG_T> sh;
     topk_small_body(sh, a, blockIdx.x);
+}
+
+// Rows of up to SEG entries in a quarter-size workgroup.
+__global__ void __launch_bounds__(SEG_T) topk_quarter_kernel(TopkArgs a) {
+    __shared__ Shared<SEG_T> sh;
+    topk_quarter_body(sh, a, blockIdx.x);
 }
 
 // Rows of up to RUN2_MAX entries, 32 values per thread.
@@ -213,7 +221,7 @@ __global__ void __launch_bounds__(BIG_T) topk_merge_kernel(TopkArgs a) {
     }
     const int64_t n_pos = two_stage ? (int64_t)SMALL_MAX : n;
     const int g1_start = g1 * quota;
-    const bool done = select_run<VPT, true>(
+    const bool done = select_run<BIG_T, VPT, true>(
         sh, v, n_pos, (uint32_t)a.k, out,
         [&](int j) -> int32_t {
             const int32_t i = (int32_t)id[j];
@@ -255,6 +263,10 @@ hipError_t launch_topk(const float* vals, int64_t stride, const int64_t* ctx,
     a.k = k;
     a.out = out;
     const int64_t max_n = ctx ? (max_ctx + BLOCK - 1) / BLOCK : n_fixed;
+    if (max_n <= SEG) {
+        hipLaunchKernelGGL(topk_quarter_kernel, dim3(B), dim3(SEG_T), 0, stream, a);
+        return hipGetLastError();
+    }
     if (max_n <= SMALL_MAX || max_n > FAST_MAX_N) {
         hipLaunchKernelGGL(topk_small_kernel, dim3(B), dim3(BIG_T), 0, stream, a);
         return hipGetLastError();

@@ -246,7 +246,7 @@ __device__ void find_digit(Shared<NT>& sh, uint32_t kk, int nbins) {
 // ------------------------------------------------------------ select core
 
 template <int NT>
-__device__ bool resolve_candidates(Shared<NT>& sh, uint32_t kk, int words);
+__device__ __forceinline__ bool resolve_candidates(Shared<NT>& sh, uint32_t kk, int words);
 
 // Chooses the k best of the block's register-held values (v, id), -inf absent,
 // ties to the lower id.  Marks the choice in sh.sel_bits, bit (id - id_base),
@@ -323,7 +323,7 @@ __device__ bool select_core(Shared<NT>& sh, const float (&v)[VPT], const uint32_
 // their bits in sh.sel_bits.  Expects eq_bits[0, words) zero.  Returns false if
 // the candidate list overflowed.  Ends with a barrier.
 template <int NT>
-__device__ bool resolve_candidates(Shared<NT>& sh, uint32_t kk, int words) {
+__device__ __forceinline__ bool resolve_candidates(Shared<NT>& sh, uint32_t kk, int words) {
     const int t = threadIdx.x;
     const uint32_t m = sh.misc[2];
     if (m > (uint32_t)CAND_CAP) return false;
@@ -570,13 +570,14 @@ __device__ __forceinline__ void load_values(const float* row, int64_t base, int6
 // (nothing written) when the candidate list overflowed or a veto fired.
 // STATIC_J visits the chosen positions with compile-time j (for id_of / veto
 // that index register arrays, which a runtime j would move to scratch).
-template <int V, bool STATIC_J, typename IdOf, typename Veto>
-__device__ bool select_run(Shared<BIG_T>& sh, const float (&v)[V], int64_t n_pos, uint32_t k,
+template <int NT, int V, bool STATIC_J, typename IdOf, typename Veto>
+__device__ bool select_run(Shared<NT>& sh, const float (&v)[V], int64_t n_pos, uint32_t k,
                            int32_t* out, IdOf id_of, Veto veto) {
     static_assert(V == 16 || V == 32, "a thread's choice is one 32-bit mask word or half of one");
+    static_assert(NT == BIG_T || NT == SEG_T, "the block sizes Shared is laid out for");
     const int t = threadIdx.x;
     const int words = (int)((n_pos + 31) >> 5);
-    for (int i = t; i < NB; i += BIG_T) sh.hist[i] = 0;
+    for (int i = t; i < NB; i += NT) sh.hist[i] = 0;
     if (t < words) {
         sh.sel_bits[t] = 0;
         sh.eq_bits[t] = 0;
@@ -598,7 +599,7 @@ __device__ bool select_run(Shared<BIG_T>& sh, const float (&v)[V], int64_t n_pos
     }
     uint32_t n_valid, n_thr;
     float vmin, vmax, tmax_min;
-    block_stats<BIG_T>(cnt, lo, hi, sh, &n_valid, &vmin, &vmax, &tmax_min, &n_thr);
+    block_stats<NT>(cnt, lo, hi, sh, &n_valid, &vmin, &vmax, &tmax_min, &n_thr);
 
     uint32_t mask = 0;                   // bit j: position Vt + j chosen
     if (n_valid <= k) {
@@ -619,7 +620,7 @@ __device__ bool select_run(Shared<BIG_T>& sh, const float (&v)[V], int64_t n_pos
             if (bin[j] != 0xffffffffu) atomicAdd(&sh.hist[bin[j]], 1u);
         }
         __syncthreads();
-        find_digit<BIG_T>(sh, k, NB);
+        find_digit<NT>(sh, k, NB);
         const uint32_t d = sh.misc[0];
         const uint32_t kk = k - sh.misc[1];
         __syncthreads();
@@ -637,7 +638,7 @@ __device__ bool select_run(Shared<BIG_T>& sh, const float (&v)[V], int64_t n_pos
             }
         }
         __syncthreads();
-        if (!resolve_candidates<BIG_T>(sh, kk, words)) return false;
+        if (!resolve_candidates<NT>(sh, kk, words)) return false;
         const uint32_t bit0 = (uint32_t)(V * t);
         mask |= V == 32 ? sh.sel_bits[t] : (sh.sel_bits[bit0 >> 5] >> (bit0 & 31)) & 0xffffu;
     }
@@ -656,9 +657,13 @@ __device__ bool select_run(Shared<BIG_T>& sh, const float (&v)[V], int64_t n_pos
     }
     const uint32_t c = (uint32_t)__popc(mask);
     uint32_t total;
-    uint32_t pos = block_incl_scan<BIG_T>(c, sh, &total) - c;
+    uint32_t pos = block_incl_scan<NT>(c, sh, &total) - c;
     if (sh.misc[3]) return false;
-    int32_t* stage = reinterpret_cast<int32_t*>(sh.eq_bits);
+    // staging: eq_bits holds k <= 4096 entries at BIG_T; the smaller block's
+    // eq_bits is one word per 32 entries, so it stages in ckey (free again
+    // once the candidates are resolved)
+    int32_t* stage = NT == BIG_T ? reinterpret_cast<int32_t*>(sh.eq_bits)
+                                 : reinterpret_cast<int32_t*>(sh.ckey);
     if (STATIC_J) {
 #pragma unroll
         for (int j = 0; j < V; ++j) {
@@ -676,7 +681,7 @@ __device__ bool select_run(Shared<BIG_T>& sh, const float (&v)[V], int64_t n_pos
         }
     }
     __syncthreads();
-    for (int j = t; j < (int)k; j += BIG_T) out[j] = j < (int)total ? stage[j] : -1;
+    for (int j = t; j < (int)k; j += NT) out[j] = j < (int)total ? stage[j] : -1;
     return true;
 }
 
@@ -717,11 +722,37 @@ __device__ __forceinline__ void topk_small_body(Shared<BIG_T>& sh, const TopkArg
         pb[0] = 2 * t < a.n_blocks ? pool[2 * t] : 0;
         pb[1] = 2 * t + 1 < a.n_blocks ? pool[2 * t + 1] : 0;
     }
-    const bool done = select_run<VPT, false>(
+    const bool done = select_run<BIG_T, VPT, false>(
         sh, v, n, (uint32_t)a.k, out,
         [&](int j) -> int32_t { return pool ? pb[j >> 3] * BLOCK + (j & 7) : VPT * t + j; },
         [](int) { return false; });
     if (!done) topk_fallback(sh, row, n, a.k, pool, out);
+}
+
+// Rows of up to SEG entries (4,096) in a workgroup of SEG_T threads, 16 values
+// per thread: the steps of topk_small_body with a quarter of the waves, so each
+// block-wide step is shorter and about three such workgroups fit a CU (LDS
+// ~50 KB, against one of the 1,024-thread kind), which large batches of short
+// rows need.  With n <= CAND_CAP the candidate list cannot overflow and no veto
+// is used, so the selection always completes here.
+__device__ __forceinline__ void topk_quarter_body(Shared<SEG_T>& sh, const TopkArgs& a, int b) {
+    static_assert(SEG <= CAND_CAP, "a row's candidates always fit");
+    const int t = threadIdx.x;
+    const int64_t n = row_length(a, b);
+    const float* row = a.vals + (int64_t)b * a.stride;
+    int32_t* out = a.out + (int64_t)b * a.k;
+    const int32_t* pool = a.pool ? a.pool + (int64_t)b * a.n_blocks : nullptr;
+    float v[VPT];
+    load_run<VPT>(row, n, v);
+    int32_t pb[2] = {0, 0};
+    if (pool) {
+        pb[0] = 2 * t < a.n_blocks ? pool[2 * t] : 0;
+        pb[1] = 2 * t + 1 < a.n_blocks ? pool[2 * t + 1] : 0;
+    }
+    select_run<SEG_T, VPT, false>(
+        sh, v, n, (uint32_t)a.k, out,
+        [&](int j) -> int32_t { return pool ? pb[j >> 3] * BLOCK + (j & 7) : VPT * t + j; },
+        [](int) { return false; });
 }
 
 // Rows of up to RUN2_MAX entries in one workgroup, 32 values per thread (rows
@@ -744,7 +775,7 @@ __device__ __forceinline__ void topk_run32_body(Shared<BIG_T>& sh, const TopkArg
 #pragma unroll
         for (int i = 0; i < 4; ++i) pb[i] = 4 * t + i < a.n_blocks ? pool[4 * t + i] : 0;
     }
-    const bool done = select_run<2 * VPT, true>(
+    const bool done = select_run<BIG_T, 2 * VPT, true>(
         sh, v, n, (uint32_t)a.k, out,
         [&](int j) -> int32_t { return pool ? pb[j >> 3] * BLOCK + (j & 7) : 2 * VPT * t + j; },
         [](int) { return false; });
