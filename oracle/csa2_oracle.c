@@ -41,7 +41,10 @@
  *  - top-k ranks by value descending, ties to the lower index, output in
  *    ascending index order padded with -1;
  *  - attention: one softmax over the selected main rows and the window rows
- *    [max(0, N-128), N), logits q.k * sm_scale, no sink, no bias.
+ *    [max(0, N-128), N), logits q.k * sm_scale, no sink, no bias;
+ *  - global-KV compression m (the encoder's m = 2): an entry is the fp32 mean
+ *    of its m tokens' rows, quantised as a token row; the window keeps every
+ *    token (oracle_compress_kv).
  *
  * Arithmetic: fp64 everywhere except where a step is defined in fp32 (the
  * amax/6 division and x/scale before FP8 rounding).  Build with -O2
