@@ -1,8 +1,9 @@
 """Seeded randomized sweeps on the GPU.
 
 * Top-k selection against a brute-force stable sort: random row lengths from 1
-  to 140,000 (every select path: one workgroup at 16 or 32 values per thread,
-  segments + merge, and the exact fallback), k from 1 to 4,096, and value
+  to 140,000 (every select path: a 256-thread workgroup for rows of up to 4,096,
+  one 1,024-thread workgroup at 16 or 32 values per thread, segments + merge,
+  and the exact fallback), k from 1 to 4,096, and value
   distributions including ReLU-like, skewed, tie-heavy, signed-zero and mostly
   absent rows.
 * Block scores of large batches (four queries per key pass) against the same
@@ -52,6 +53,21 @@ def test_topk_random_sweep(K, seed):
         k = int(rng.choice([1, 8, 100, 512, 1000, 2048, 4096]))
         sizes = [int(rng.choice([rng.integers(1, 70), rng.integers(1, 20000),
                                  rng.integers(16000, 33000), rng.integers(33000, 140000)]))
+                 for _ in range(B)]
+        T.run(K, [_row(rng, n, kinds[int(rng.integers(len(kinds)))]) for n in sizes], k)
+
+
+@pytest.mark.parametrize("seed", [21, 22])
+def test_topk_short_rows_random_sweep(K, seed):
+    """Batches whose rows are all at most 4,096 entries (the quarter-size
+    workgroup), k from 1 to 4,096, every value distribution."""
+    rng = np.random.default_rng(seed)
+    kinds = ["normal", "few", "equal", "signed_zero", "absent", "narrow", "relu", "skew",
+             "zeros_then_big"]
+    for _ in range(30):
+        B = int(rng.integers(1, 9))
+        k = int(rng.choice([1, 8, 100, 512, 1000, 2048, 4096]))
+        sizes = [int(rng.choice([rng.integers(1, 70), rng.integers(1, 4097), 4096]))
                  for _ in range(B)]
         T.run(K, [_row(rng, n, kinds[int(rng.integers(len(kinds)))]) for n in sizes], k)
 
