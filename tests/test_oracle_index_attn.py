@@ -244,6 +244,23 @@ def test_single_entry_gives_its_value():
         assert np.array_equal(out[0, h], want)
 
 
+@pytest.mark.parametrize("idx_len", [1, 512])
+def test_no_main_entries_is_window_attention(idx_len):
+    """A window-only layer (every index -1): softmax attention over the 128
+    window rows of positions [N - 128, N) alone, dense numpy in fp64."""
+    N = 1000
+    c = _fill_cache(1, N, seed=21, n_layers=2, w_cap=160)
+    q = G.attn_queries(21, 1, 1)
+    sm = float(np.float32(1 / np.sqrt(128)))
+    out = c.decode_attn(1, q, np.full((1, idx_len), -1, np.int32), [0], [N], sm)
+    u = np.arange(N - 128, N)
+    Kw = E4M3[c.wk[1, 0, u % c.w_cap]] * c.wk_scale
+    Vw = E4M3[c.wv[1, 0, u % c.w_cap]] * c.wv_scale
+    z = q[0].astype(np.float64) @ Kw.T * sm
+    p = np.exp(z - z.max(1, keepdims=True))
+    np.testing.assert_allclose(out[0], (p / p.sum(1, keepdims=True)) @ Vw, rtol=2e-6, atol=2e-6)
+
+
 def test_reuse_layers_share_indices():
     """Reuse: same index list, different queries -> outputs differ only through q."""
     N = 2000
