@@ -200,6 +200,9 @@ csa2_status csa2_compress_kv(const csa2_cache* cache, const csa2_window* win,
  *   q_idx     [B][4][64] fp32, w [B][4] fp32.
  *   max_ctx   host bound with ctx[b] <= max_ctx <= cap for all b (sizes grids).
  *   n_blocks  pool size in blocks, 1..4096 (2048 in the pages); block must be 8.
+ *             The top-k positions always lie in the topk best blocks, so a Full
+ *             layer whose pool no Reindex layer reads may pass n_blocks = topk
+ *             and get the same idx for a quarter of the pool scoring.
  *   topk      1..2048 and <= n_blocks*8 (512 in the pages).
  *   pool      [B][n_blocks] int32 out, or NULL: the n_blocks largest block
  *             scores (ties to the lower block), ascending, -1 padded.
